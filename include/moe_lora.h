@@ -1,0 +1,214 @@
+/*
+ * moe_lora.h - C ABI of the MoE-LoRA expert layer for AMD MI355X (gfx950).
+ *
+ * The layer is the training forward and backward of one mixture-of-experts
+ * MLP block whose stacked expert weights carry LoRA adapters:
+ *
+ *   route     top-k experts per token from router logits, and combine weights
+ *   permute   (token, slot) pairs grouped by expert; rows gathered in that order
+ *   experts   per expert e, over its rows X:
+ *               h   = X W_gu[e]^T + s (X A_gu[e]^T) B_gu[e]^T     gate_up [E, 2I, H]
+ *               act = silu(h[:, :I]) * h[:, I:]                    SwiGLU
+ *               y   = act W_d[e]^T + s (act A_d[e]^T) B_d[e]^T     down    [E, H, I]
+ *   combine   Y[t] = sum_j w[t, j] y[pos(t, j)]
+ *
+ * and the backward producing dX, d logits and the LoRA gradients dA, dB with
+ * the base weights frozen. The adapter is applied in the "split" order, input
+ * times A first and then B, so W + s B A is never formed.
+ *
+ * Sources: Unsloth, "Fine-tune MoE models 12x faster" (unsloth.ai docs,
+ * faster-moe page): section "What is torch._grouped_mm?" for the per-expert
+ * loop, the gate/up chunk and the stacked gate_up_proj [E, 2I, H] parameter;
+ * section "Faster LoRA MoE training" for the split order (same outputs and
+ * gradients, products reordered by associativity); section "Implementation
+ * details" for the LoRA shapes (m, r), (r, n), the frozen router and the
+ * per-expert cost model. The SwiGLU form (gate e, e * sigmoid(e), times up)
+ * is the fused LoRA MLP definition in the aiflowlearn.net Unsloth tutorial,
+ * section on the LoRA fine-tuning principle.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers to row-major, contiguous memory that
+ *    the caller allocates and owns. The library allocates and frees nothing,
+ *    and never synchronises the stream: every call only enqueues kernels on
+ *    `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *  - Shapes: T tokens, H hidden, I intermediate, E experts, k experts per
+ *    token, r LoRA rank, N = T * k routed rows.
+ *  - dtype (moe_shape.dtype) is the element type of x, the weights, the LoRA
+ *    parameters, the saved activations, Y, dY, dX and the LoRA gradients:
+ *    MOE_F32 (float) or MOE_BF16 (bfloat16). Router logits, combine weights
+ *    and their gradients are always float32; indices are int32.
+ *  - Outputs are fully overwritten (gradients are not accumulated into).
+ *  - Arguments are checked before anything is enqueued. Errors:
+ *      MOE_ERR_INVALID_ARG   a NULL pointer that is not optional, T < 1,
+ *                            k < 1, k > E, E < 1, E > 1024, H < 1, I < 1,
+ *                            r < 1, N >= 2^31, unknown router or dtype
+ *      MOE_ERR_UNSUPPORTED   H or I not a multiple of 8, r > 64, k > 32
+ *      MOE_ERR_WORKSPACE     workspace smaller than moe_workspace_bytes says
+ *      MOE_ERR_HIP           a launch failed (moe_last_error() has the text)
+ *    Faults inside kernels surface at the caller's next synchronisation.
+ *  - Entry points keep no state between calls (the optional kernel timer
+ *    below aside), so calls on different streams may run concurrently if
+ *    their buffers do not overlap.
+ */
+#ifndef MOE_LORA_H
+#define MOE_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Router modes (how combine weights follow from the logits of the k chosen
+ * experts; the choice itself is always the k largest logits, ties to the
+ * lower expert index, ordered by logit descending):
+ *   MOE_SOFTMAX_TOPK         w_j = softmax(logits)[S_j]
+ *   MOE_SOFTMAX_TOPK_RENORM  w_j = softmax(logits)[S_j] / sum_j softmax(logits)[S_j]
+ *   MOE_TOPK_SOFTMAX         w   = softmax(logits[S])
+ *   MOE_SIGMOID_TOPK_RENORM  w_j = sigmoid(logits[S_j]) / sum_j sigmoid(logits[S_j])  */
+typedef enum {
+  MOE_SOFTMAX_TOPK = 0,
+  MOE_SOFTMAX_TOPK_RENORM = 1,
+  MOE_TOPK_SOFTMAX = 2,
+  MOE_SIGMOID_TOPK_RENORM = 3
+} moe_router;
+
+/* lora_scale is s above (alpha / r in the usual LoRA parameterisation). */
+typedef struct {
+  int32_t T, H, I, E, k, r;
+  int32_t dtype;      /* moe_dtype */
+  float lora_scale;
+} moe_shape;
+
+/* Frozen base weights and LoRA parameters, all of `dtype`:
+ *   w_gu [E, 2I, H]  (rows 0..I-1 gate, I..2I-1 up)   a_gu [E, r, H]   b_gu [E, 2I, r]
+ *   w_d  [E, H, I]                                     a_d  [E, r, I]   b_d  [E, H, r]  */
+typedef struct {
+  const void *w_gu, *a_gu, *b_gu, *w_d, *a_d, *b_d;
+} moe_weights;
+
+/* Activations the forward writes and the backward reads, all of `dtype`,
+ * rows in permuted (expert-grouped) order:
+ *   h     [N, 2I]  gate_up output before SwiGLU
+ *   act   [N, I]   SwiGLU output (input of down)
+ *   u_gu  [N, r]   s * X A_gu^T   (the scaled LoRA side product of gate_up)
+ *   u_d   [N, r]   s * act A_d^T  (the scaled LoRA side product of down)
+ *   y_exp [N, H]   per-row expert output before the combine weights  */
+typedef struct {
+  void *h, *act, *u_gu, *u_d, *y_exp;
+} moe_saved;
+
+/* LoRA gradients, shapes of the parameters, all of `dtype`. Experts that
+ * received no rows get zeros. */
+typedef struct {
+  void *da_gu, *db_gu, *da_d, *db_d;
+} moe_lora_grads;
+
+/* Bytes of device scratch each call needs (0 is possible). Host-only, no HIP
+ * call. Any pointer may be NULL to skip that figure. */
+moe_status moe_workspace_bytes(const moe_shape *shape, size_t *fwd_ws, size_t *bwd_ws,
+                               size_t *permute_ws);
+
+/* Top-k routing (faster-moe page, "What is torch._grouped_mm?": the expert
+ * mask the per-expert loop walks).
+ *   logits   [T, E] float32 in
+ *   topk_ids [T, k] int32 out: chosen experts, logit descending, ties to lower index
+ *   topk_w   [T, k] float32 out: combine weights per `router`  */
+moe_status moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t router,
+                     int32_t *topk_ids, float *topk_w, void *stream);
+
+/* Gradient of the routing weights with respect to the logits, the selection
+ * held fixed (the router is frozen, faster-moe page, "Implementation
+ * details", so this is the only router gradient).
+ *   d_topk_w [T, k] float32 in;  d_logits [T, E] float32 out (zeros where the
+ *   mode gives none)  */
+moe_status moe_route_bwd(const float *logits, const int32_t *topk_ids, const float *d_topk_w,
+                         int32_t T, int32_t E, int32_t k, int32_t router, float *d_logits,
+                         void *stream);
+
+/* Group the N (token, slot) pairs by expert, stably in pair order p = t*k + j
+ * (the per-expert token_idx of the faster-moe page's loop), and gather rows.
+ *   topk_ids    [T, k] int32 in, each in [0, E)
+ *   x           [T, H] dtype in (may be NULL when x_perm is NULL)
+ *   counts      [E] int32 out     rows per expert
+ *   offsets     [E+1] int32 out   exclusive prefix sum; expert e owns rows
+ *                                 offsets[e] .. offsets[e+1]-1
+ *   sorted_pair [N] int32 out     pair at each permuted row
+ *   inv_pos     [N] int32 out     permuted row of each pair
+ *   x_perm      [N, H] dtype out  x[sorted_pair[i] / k]; NULL skips the gather
+ *   ws          permute workspace (moe_workspace_bytes)  */
+moe_status moe_permute(const moe_shape *shape, const int32_t *topk_ids, const void *x,
+                       int32_t *counts, int32_t *offsets, int32_t *sorted_pair,
+                       int32_t *inv_pos, void *x_perm, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* Grouped expert forward with split LoRA and SwiGLU (faster-moe page, "Faster
+ * LoRA MoE training" and "Implementation details"): fills every field of
+ * `saved` for rows in permuted order. offsets is moe_permute's output.  */
+moe_status moe_grouped_lora_fwd(const moe_shape *shape, const void *x_perm,
+                                const int32_t *offsets, const moe_weights *weights,
+                                const moe_saved *saved, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/* Y[t] = sum_{j<k} w[t, j] * y_perm[inv_pos[t*k + j]], accumulated in float32
+ * in slot order. topk_w NULL means all weights 1 (the plain sum that brings
+ * dX_perm back to tokens).
+ *   y_perm [N, H] dtype in, inv_pos [N] in, topk_w [T, k] float32 in, y [T, H] out  */
+moe_status moe_unpermute_combine(const moe_shape *shape, const void *y_perm,
+                                 const int32_t *inv_pos, const float *topk_w, void *y,
+                                 void *stream);
+
+/* Backward of the combine:
+ *   dy_perm[inv_pos[t*k+j]] = w[t, j] * dy[t]          [N, H] dtype out
+ *   d_topk_w[t, j] = <dy[t], y_exp[inv_pos[t*k+j]]>    [T, k] float32 out  */
+moe_status moe_unpermute_combine_bwd(const moe_shape *shape, const void *dy,
+                                     const void *y_exp, const int32_t *inv_pos,
+                                     const float *topk_w, void *dy_perm, float *d_topk_w,
+                                     void *stream);
+
+/* Grouped expert backward, base weights frozen: from dy_perm (the combine
+ * backward's output) and the saved activations, writes dx_perm [N, H] and the
+ * four LoRA gradients.  */
+moe_status moe_grouped_lora_bwd(const moe_shape *shape, const void *dy_perm,
+                                const void *x_perm, const int32_t *offsets,
+                                const moe_weights *weights, const moe_saved *saved,
+                                void *dx_perm, const moe_lora_grads *grads, void *ws,
+                                size_t ws_bytes, void *stream);
+
+const char *moe_status_str(moe_status status);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Optional per-kernel timer (for measurement; off by default). While enabled,
+ * the library records a HIP event pair on the launch stream around each
+ * launch of the kernels listed in moe_kernel_id. moe_kernel_timer_read must be
+ * called after the caller has synchronised those streams; it returns the
+ * summed milliseconds and the number of launches since the last reset. Not
+ * thread-safe against concurrent launches; meant for a benchmark loop. */
+typedef enum {
+  MOE_K_ROUTE = 0, MOE_K_PERMUTE = 1, MOE_K_GATHER = 2, MOE_K_GATE_UP_FWD = 3,
+  MOE_K_DOWN_FWD = 4, MOE_K_COMBINE = 5, MOE_K_COMBINE_BWD = 6, MOE_K_ROUTE_BWD = 7,
+  MOE_K_DOWN_BWD = 8, MOE_K_GATE_UP_BWD = 9, MOE_K_LORA_SIDE = 10, MOE_K_LORA_WGRAD = 11,
+  MOE_K_UNPERMUTE = 12, MOE_K_COUNT = 13
+} moe_kernel_id;
+moe_status moe_kernel_timer_enable(int32_t on);
+moe_status moe_kernel_timer_reset(void);
+moe_status moe_kernel_timer_read(int32_t kernel_id, double *total_ms, int32_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LORA_H */

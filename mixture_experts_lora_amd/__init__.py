@@ -1,0 +1,252 @@
+"""MoE-LoRA expert layer on AMD MI355X (gfx950): Python binding of libmoe_lora.so.
+
+The functions below carry the names of the C ABI (include/moe_lora.h) and do
+argument marshalling only: they check that each torch tensor is a contiguous
+GPU tensor of the shape and dtype the kernels assume, then pass its address
+and torch's current HIP stream to the library. Every step of the layer runs in
+the HIP kernels; nothing here computes. PyTorch provides the device memory and
+the stream.
+
+Layer (per expert e over its rows X, split LoRA, SwiGLU):
+    h = X W_gu^T + s (X A_gu^T) B_gu^T,  act = silu(h[:, :I]) h[:, I:],
+    y = act W_d^T + s (act A_d^T) B_d^T,  Y[t] = sum_j w[t, j] y[pos(t, j)]
+following Unsloth's "Fine-tune MoE models 12x faster" (faster-moe page),
+sections "What is torch._grouped_mm?", "Faster LoRA MoE training" and
+"Implementation details".
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import MoeLoraGrads, MoeSaved, MoeShape, MoeWeights, ROUTER_IDS, check
+
+__all__ = [
+    "Shape", "moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
+    "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
+    "moe_grouped_lora_bwd", "kernel_timer", "ROUTER_IDS", "library_path",
+]
+
+_TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+_ABI_DTYPES = {"f32": _lib.MOE_F32, "bf16": _lib.MOE_BF16}
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+@dataclass(frozen=True)
+class Shape:
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    r: int
+    dtype: str = "bf16"       # "bf16" or "f32"
+    lora_scale: float = 1.0
+
+    @property
+    def N(self) -> int:
+        return self.T * self.k
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPES[self.dtype]
+
+    def c(self) -> MoeShape:
+        return MoeShape(self.T, self.H, self.I, self.E, self.k, self.r,
+                        _ABI_DTYPES[self.dtype], float(self.lora_scale))
+
+    @classmethod
+    def of(cls, cfg) -> "Shape":
+        return cls(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.r, cfg.dtype, cfg.lora_scale)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t, shape, dtype, name, optional=False):
+    """Address of a contiguous GPU tensor of exactly `shape` and `dtype`."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ws(t, need, name):
+    if need == 0:
+        return ctypes.c_void_p(t.data_ptr()) if t is not None else None, 0
+    if t is None or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor of >= {need} bytes")
+    nbytes = t.numel() * t.element_size()
+    return ctypes.c_void_p(t.data_ptr()), nbytes
+
+
+def moe_workspace_bytes(shape: Shape):
+    """(forward, backward, permute) workspace bytes for `shape`."""
+    f, b, p = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    check(_lib.load().moe_workspace_bytes(ctypes.byref(shape.c()), ctypes.byref(f),
+                                          ctypes.byref(b), ctypes.byref(p)),
+          "moe_workspace_bytes")
+    return f.value, b.value, p.value
+
+
+def moe_route(logits, k, router, topk_ids, topk_w, stream=None):
+    T, E = logits.shape
+    check(_lib.load().moe_route(
+        _ptr(logits, (T, E), torch.float32, "logits"), T, E, k, ROUTER_IDS[router],
+        _ptr(topk_ids, (T, k), torch.int32, "topk_ids"),
+        _ptr(topk_w, (T, k), torch.float32, "topk_w"), _stream(stream)), "moe_route")
+
+
+def moe_route_bwd(logits, topk_ids, d_topk_w, k, router, d_logits, stream=None):
+    T, E = logits.shape
+    check(_lib.load().moe_route_bwd(
+        _ptr(logits, (T, E), torch.float32, "logits"),
+        _ptr(topk_ids, (T, k), torch.int32, "topk_ids"),
+        _ptr(d_topk_w, (T, k), torch.float32, "d_topk_w"), T, E, k, ROUTER_IDS[router],
+        _ptr(d_logits, (T, E), torch.float32, "d_logits"), _stream(stream)), "moe_route_bwd")
+
+
+def moe_permute(shape: Shape, topk_ids, x, counts, offsets, sorted_pair, inv_pos, x_perm, ws,
+                stream=None):
+    _, _, need = moe_workspace_bytes(shape)
+    wsp, wsb = _ws(ws, need, "ws")
+    dt = shape.torch_dtype
+    check(_lib.load().moe_permute(
+        ctypes.byref(shape.c()),
+        _ptr(topk_ids, (shape.T, shape.k), torch.int32, "topk_ids"),
+        _ptr(x, (shape.T, shape.H), dt, "x", optional=x_perm is None),
+        _ptr(counts, (shape.E,), torch.int32, "counts"),
+        _ptr(offsets, (shape.E + 1,), torch.int32, "offsets"),
+        _ptr(sorted_pair, (shape.N,), torch.int32, "sorted_pair"),
+        _ptr(inv_pos, (shape.N,), torch.int32, "inv_pos"),
+        _ptr(x_perm, (shape.N, shape.H), dt, "x_perm", optional=True),
+        wsp, wsb, _stream(stream)), "moe_permute")
+
+
+def _weights(shape: Shape, w: dict) -> MoeWeights:
+    E, H, I, r, dt = shape.E, shape.H, shape.I, shape.r, shape.torch_dtype
+    return MoeWeights(
+        _ptr(w["w_gu"], (E, 2 * I, H), dt, "w_gu"), _ptr(w["a_gu"], (E, r, H), dt, "a_gu"),
+        _ptr(w["b_gu"], (E, 2 * I, r), dt, "b_gu"), _ptr(w["w_d"], (E, H, I), dt, "w_d"),
+        _ptr(w["a_d"], (E, r, I), dt, "a_d"), _ptr(w["b_d"], (E, H, r), dt, "b_d"))
+
+
+def _saved(shape: Shape, s: dict, need_y=True) -> MoeSaved:
+    N, H, I, r, dt = shape.N, shape.H, shape.I, shape.r, shape.torch_dtype
+    return MoeSaved(
+        _ptr(s["h"], (N, 2 * I), dt, "h"), _ptr(s["act"], (N, I), dt, "act"),
+        _ptr(s["u_gu"], (N, r), dt, "u_gu"), _ptr(s["u_d"], (N, r), dt, "u_d"),
+        _ptr(s.get("y_exp"), (N, H), dt, "y_exp", optional=not need_y))
+
+
+def moe_grouped_lora_fwd(shape: Shape, x_perm, offsets, weights: dict, saved: dict, ws,
+                         stream=None):
+    need, _, _ = moe_workspace_bytes(shape)
+    wsp, wsb = _ws(ws, need, "ws")
+    w = _weights(shape, weights)
+    s = _saved(shape, saved)
+    check(_lib.load().moe_grouped_lora_fwd(
+        ctypes.byref(shape.c()), _ptr(x_perm, (shape.N, shape.H), shape.torch_dtype, "x_perm"),
+        _ptr(offsets, (shape.E + 1,), torch.int32, "offsets"), ctypes.byref(w), ctypes.byref(s),
+        wsp, wsb, _stream(stream)), "moe_grouped_lora_fwd")
+
+
+def moe_unpermute_combine(shape: Shape, y_perm, inv_pos, topk_w, y, stream=None):
+    dt = shape.torch_dtype
+    check(_lib.load().moe_unpermute_combine(
+        ctypes.byref(shape.c()), _ptr(y_perm, (shape.N, shape.H), dt, "y_perm"),
+        _ptr(inv_pos, (shape.N,), torch.int32, "inv_pos"),
+        _ptr(topk_w, (shape.T, shape.k), torch.float32, "topk_w", optional=True),
+        _ptr(y, (shape.T, shape.H), dt, "y"), _stream(stream)), "moe_unpermute_combine")
+
+
+def moe_unpermute_combine_bwd(shape: Shape, dy, y_exp, inv_pos, topk_w, dy_perm, d_topk_w,
+                              stream=None):
+    dt = shape.torch_dtype
+    check(_lib.load().moe_unpermute_combine_bwd(
+        ctypes.byref(shape.c()), _ptr(dy, (shape.T, shape.H), dt, "dy"),
+        _ptr(y_exp, (shape.N, shape.H), dt, "y_exp"),
+        _ptr(inv_pos, (shape.N,), torch.int32, "inv_pos"),
+        _ptr(topk_w, (shape.T, shape.k), torch.float32, "topk_w"),
+        _ptr(dy_perm, (shape.N, shape.H), dt, "dy_perm"),
+        _ptr(d_topk_w, (shape.T, shape.k), torch.float32, "d_topk_w"), _stream(stream)),
+        "moe_unpermute_combine_bwd")
+
+
+def moe_grouped_lora_bwd(shape: Shape, dy_perm, x_perm, offsets, weights: dict, saved: dict,
+                         dx_perm, grads: dict, ws, stream=None):
+    _, need, _ = moe_workspace_bytes(shape)
+    wsp, wsb = _ws(ws, need, "ws")
+    E, H, I, r, dt = shape.E, shape.H, shape.I, shape.r, shape.torch_dtype
+    w = _weights(shape, weights)
+    s = _saved(shape, saved, need_y=False)
+    g = MoeLoraGrads(_ptr(grads["da_gu"], (E, r, H), dt, "da_gu"),
+                     _ptr(grads["db_gu"], (E, 2 * I, r), dt, "db_gu"),
+                     _ptr(grads["da_d"], (E, r, I), dt, "da_d"),
+                     _ptr(grads["db_d"], (E, H, r), dt, "db_d"))
+    check(_lib.load().moe_grouped_lora_bwd(
+        ctypes.byref(shape.c()), _ptr(dy_perm, (shape.N, H), dt, "dy_perm"),
+        _ptr(x_perm, (shape.N, H), dt, "x_perm"),
+        _ptr(offsets, (E + 1,), torch.int32, "offsets"), ctypes.byref(w), ctypes.byref(s),
+        _ptr(dx_perm, (shape.N, H), dt, "dx_perm"), ctypes.byref(g), wsp, wsb,
+        _stream(stream)), "moe_grouped_lora_bwd")
+
+
+class kernel_timer:
+    """Per-kernel HIP-event timer of the library (see moe_kernel_timer_* in the header).
+
+    with kernel_timer() as kt:
+        ...launches...
+    torch.cuda.synchronize(); kt.read("gate_up_fwd") -> (total_ms, launches)
+    """
+
+    def __enter__(self):
+        lib = _lib.load()
+        check(lib.moe_kernel_timer_reset(), "moe_kernel_timer_reset")
+        check(lib.moe_kernel_timer_enable(1), "moe_kernel_timer_enable")
+        return self
+
+    def __exit__(self, *exc):
+        check(_lib.load().moe_kernel_timer_enable(0), "moe_kernel_timer_enable")
+        return False
+
+    @staticmethod
+    def read(name: str):
+        ms, n = ctypes.c_double(), ctypes.c_int32()
+        check(_lib.load().moe_kernel_timer_read(_lib.KERNEL_IDS[name], ctypes.byref(ms),
+                                                ctypes.byref(n)), "moe_kernel_timer_read")
+        return ms.value, n.value
+
+    @staticmethod
+    def reset():
+        check(_lib.load().moe_kernel_timer_reset(), "moe_kernel_timer_reset")
+
+
+# Load at import: a missing library is an error, never a silent fallback.
+_lib.load()
+
+from .layer import MoELoRALayer, MoELoRAFunction  # noqa: E402
+
+__all__ += ["MoELoRALayer", "MoELoRAFunction"]

@@ -1,0 +1,366 @@
+// C ABI of the MoE-LoRA expert layer: argument checks, workspace carving and
+// launches on the caller's stream. Declarations and the contract of every
+// entry point are in include/moe_lora.h.
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const std::string& what) {
+  g_last_error = what;
+  return st;
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define CHECK_PTR(p)                                                                  \
+  do {                                                                                \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "null pointer: " #p);        \
+  } while (0)
+
+moe_status check_router(int32_t router) {
+  if (router < MOE_SOFTMAX_TOPK || router > MOE_SIGMOID_TOPK_RENORM)
+    return fail(MOE_ERR_INVALID_ARG, "unknown router mode " + std::to_string(router));
+  return MOE_OK;
+}
+
+moe_status check_routing_dims(int64_t T, int64_t E, int64_t k) {
+  if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1");
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "E must be in [1, 1024]");
+  if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "k must be in [1, E]");
+  if (k > 32) return fail(MOE_ERR_UNSUPPORTED, "k > 32 is not supported");
+  if (T * k >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARG, "T*k must be < 2^31");
+  return MOE_OK;
+}
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_ERR_INVALID_ARG, "null shape");
+  moe_status st = check_routing_dims(s->T, s->E, s->k);
+  if (st != MOE_OK) return st;
+  if (s->H < 1 || s->I < 1) return fail(MOE_ERR_INVALID_ARG, "H and I must be >= 1");
+  if (s->r < 1) return fail(MOE_ERR_INVALID_ARG, "r must be >= 1");
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype " + std::to_string(s->dtype));
+  if (s->H % 8 != 0 || s->I % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 8");
+  if (s->r > 64) return fail(MOE_ERR_UNSUPPORTED, "r > 64 is not supported");
+  const int64_t N = int64_t(s->T) * s->k;
+  if (N * (2 * int64_t(s->I)) >= (int64_t(1) << 40) || N * int64_t(s->H) >= (int64_t(1) << 40))
+    return fail(MOE_ERR_INVALID_ARG, "activation tensors too large");
+  return MOE_OK;
+}
+
+moe::ExpertDims dims_of(const moe_shape* s) {
+  moe::ExpertDims d;
+  d.N = int64_t(s->T) * s->k;
+  d.H = s->H;
+  d.I = s->I;
+  d.E = s->E;
+  d.r = s->r;
+  d.dtype = s->dtype;
+  d.scale = s->lora_scale;
+  return d;
+}
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------- kernel timer
+struct TimerRec {
+  int id;
+  hipEvent_t a, b;
+};
+
+struct TimerState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TimerRec> recs;
+  std::vector<hipEvent_t> pool;
+  std::vector<int> open;  // index into recs of the pending start, per id
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+TimerState& timer() {
+  static TimerState t;
+  return t;
+}
+
+moe::KernelTimer g_timer_handle;
+
+}  // namespace
+
+namespace moe {
+
+KernelTimer* active_timer() { return timer().on ? &g_timer_handle : nullptr; }
+
+void KernelTimer::record_start(int id, hipStream_t s) {
+  TimerState& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (t.open.size() < MOE_K_COUNT) t.open.assign(MOE_K_COUNT, -1);
+  hipEvent_t a = t.get(), b = t.get();
+  if (!a || !b) return;
+  hipEventRecord(a, s);
+  t.recs.push_back(TimerRec{id, a, b});
+  t.open[id] = static_cast<int>(t.recs.size()) - 1;
+}
+
+void KernelTimer::record_stop(int id, hipStream_t s) {
+  TimerState& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (t.open.size() < MOE_K_COUNT || t.open[id] < 0) return;
+  hipEventRecord(t.recs[t.open[id]].b, s);
+  t.open[id] = -1;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+const char* moe_status_str(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_workspace_bytes(const moe_shape* shape, size_t* fwd_ws, size_t* bwd_ws,
+                               size_t* permute_ws) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe::ExpertDims d = dims_of(shape);
+  if (fwd_ws) *fwd_ws = moe::experts_fwd_ws_bytes(d);
+  if (bwd_ws) *bwd_ws = moe::experts_bwd_ws_bytes(d);
+  if (permute_ws) *permute_ws = moe::permute_ws_bytes(d.N, d.E);
+  return MOE_OK;
+}
+
+moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t router,
+                     int32_t* topk_ids, float* topk_w, void* stream) {
+  moe_status st = check_routing_dims(T, E, k);
+  if (st != MOE_OK) return st;
+  if ((st = check_router(router)) != MOE_OK) return st;
+  CHECK_PTR(logits);
+  CHECK_PTR(topk_ids);
+  CHECK_PTR(topk_w);
+  moe::TimedScope ts(moe::active_timer(), MOE_K_ROUTE, as_stream(stream));
+  hipError_t e = moe::launch_route(logits, T, E, k, router, topk_ids, topk_w, as_stream(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route");
+}
+
+moe_status moe_route_bwd(const float* logits, const int32_t* topk_ids, const float* d_topk_w,
+                         int32_t T, int32_t E, int32_t k, int32_t router, float* d_logits,
+                         void* stream) {
+  moe_status st = check_routing_dims(T, E, k);
+  if (st != MOE_OK) return st;
+  if ((st = check_router(router)) != MOE_OK) return st;
+  CHECK_PTR(logits);
+  CHECK_PTR(topk_ids);
+  CHECK_PTR(d_topk_w);
+  CHECK_PTR(d_logits);
+  if (static_cast<const void*>(d_logits) == static_cast<const void*>(logits))
+    return fail(MOE_ERR_INVALID_ARG, "d_logits aliases logits");
+  moe::TimedScope ts(moe::active_timer(), MOE_K_ROUTE_BWD, as_stream(stream));
+  hipError_t e = moe::launch_route_bwd(logits, topk_ids, d_topk_w, T, E, k, router, d_logits,
+                                       as_stream(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_bwd");
+}
+
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, const void* x,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                       int32_t* inv_pos, void* x_perm, void* ws, size_t ws_bytes,
+                       void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(topk_ids);
+  CHECK_PTR(counts);
+  CHECK_PTR(offsets);
+  CHECK_PTR(sorted_pair);
+  CHECK_PTR(inv_pos);
+  if (x_perm) CHECK_PTR(x);
+  if (x_perm && x_perm == x) return fail(MOE_ERR_INVALID_ARG, "x_perm aliases x");
+  const moe::ExpertDims d = dims_of(shape);
+  const size_t need = moe::permute_ws_bytes(d.N, d.E);
+  if (need > 0) CHECK_PTR(ws);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "permute workspace needs " + std::to_string(need) + " bytes");
+  hipStream_t s = as_stream(stream);
+  moe::KernelTimer* tm = moe::active_timer();
+  hipError_t e = moe::launch_permute(topk_ids, d.N, d.E, counts, offsets, sorted_pair, inv_pos,
+                                     static_cast<int32_t*>(ws), s, tm);
+  if (e != hipSuccess) return hip_fail(e, "moe_permute");
+  if (x_perm) {
+    const int64_t row_bytes = int64_t(d.H) * (d.dtype == MOE_BF16 ? 2 : 4);
+    e = moe::launch_gather(x, sorted_pair, offsets, d.E, shape->k, d.N, row_bytes, x_perm, s, tm);
+    if (e != hipSuccess) return hip_fail(e, "moe_permute(gather)");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_grouped_lora_fwd(const moe_shape* shape, const void* x_perm,
+                                const int32_t* offsets, const moe_weights* weights,
+                                const moe_saved* saved, void* ws, size_t ws_bytes,
+                                void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(x_perm);
+  CHECK_PTR(offsets);
+  CHECK_PTR(weights);
+  CHECK_PTR(saved);
+  CHECK_PTR(weights->w_gu);
+  CHECK_PTR(weights->a_gu);
+  CHECK_PTR(weights->b_gu);
+  CHECK_PTR(weights->w_d);
+  CHECK_PTR(weights->a_d);
+  CHECK_PTR(weights->b_d);
+  CHECK_PTR(saved->h);
+  CHECK_PTR(saved->act);
+  CHECK_PTR(saved->u_gu);
+  CHECK_PTR(saved->u_d);
+  CHECK_PTR(saved->y_exp);
+  CHECK_PTR(ws);
+  const moe::ExpertDims d = dims_of(shape);
+  const size_t need = moe::experts_fwd_ws_bytes(d);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "forward workspace needs " + std::to_string(need) + " bytes");
+  if (saved->h == x_perm || saved->y_exp == x_perm || saved->act == x_perm)
+    return fail(MOE_ERR_INVALID_ARG, "a saved activation aliases x_perm");
+  hipError_t e = moe::launch_experts_fwd(d, x_perm, offsets, *weights, *saved, ws,
+                                         as_stream(stream), moe::active_timer());
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_lora_fwd");
+}
+
+moe_status moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
+                                 const int32_t* inv_pos, const float* topk_w, void* y,
+                                 void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(y_perm);
+  CHECK_PTR(inv_pos);
+  CHECK_PTR(y);
+  if (y == y_perm) return fail(MOE_ERR_INVALID_ARG, "y aliases y_perm");
+  hipError_t e = moe::launch_combine(shape->dtype, y_perm, inv_pos, topk_w, shape->T, shape->k,
+                                     shape->H, y, as_stream(stream), moe::active_timer());
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_unpermute_combine");
+}
+
+moe_status moe_unpermute_combine_bwd(const moe_shape* shape, const void* dy,
+                                     const void* y_exp, const int32_t* inv_pos,
+                                     const float* topk_w, void* dy_perm, float* d_topk_w,
+                                     void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(dy);
+  CHECK_PTR(y_exp);
+  CHECK_PTR(inv_pos);
+  CHECK_PTR(topk_w);
+  CHECK_PTR(dy_perm);
+  CHECK_PTR(d_topk_w);
+  if (dy_perm == dy || dy_perm == y_exp)
+    return fail(MOE_ERR_INVALID_ARG, "dy_perm aliases an input");
+  hipError_t e = moe::launch_combine_bwd(shape->dtype, dy, y_exp, inv_pos, topk_w, shape->T,
+                                         shape->k, shape->H, dy_perm, d_topk_w,
+                                         as_stream(stream), moe::active_timer());
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_unpermute_combine_bwd");
+}
+
+moe_status moe_grouped_lora_bwd(const moe_shape* shape, const void* dy_perm,
+                                const void* x_perm, const int32_t* offsets,
+                                const moe_weights* weights, const moe_saved* saved,
+                                void* dx_perm, const moe_lora_grads* grads, void* ws,
+                                size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(dy_perm);
+  CHECK_PTR(x_perm);
+  CHECK_PTR(offsets);
+  CHECK_PTR(weights);
+  CHECK_PTR(saved);
+  CHECK_PTR(grads);
+  CHECK_PTR(dx_perm);
+  CHECK_PTR(weights->w_gu);
+  CHECK_PTR(weights->a_gu);
+  CHECK_PTR(weights->b_gu);
+  CHECK_PTR(weights->w_d);
+  CHECK_PTR(weights->a_d);
+  CHECK_PTR(weights->b_d);
+  CHECK_PTR(saved->h);
+  CHECK_PTR(saved->act);
+  CHECK_PTR(saved->u_gu);
+  CHECK_PTR(saved->u_d);
+  CHECK_PTR(grads->da_gu);
+  CHECK_PTR(grads->db_gu);
+  CHECK_PTR(grads->da_d);
+  CHECK_PTR(grads->db_d);
+  CHECK_PTR(ws);
+  if (dx_perm == dy_perm || dx_perm == x_perm)
+    return fail(MOE_ERR_INVALID_ARG, "dx_perm aliases an input");
+  const moe::ExpertDims d = dims_of(shape);
+  const size_t need = moe::experts_bwd_ws_bytes(d);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "backward workspace needs " + std::to_string(need) + " bytes");
+  hipError_t e = moe::launch_experts_bwd(d, dy_perm, x_perm, offsets, *weights, *saved, dx_perm,
+                                         *grads, ws, as_stream(stream), moe::active_timer());
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_lora_bwd");
+}
+
+moe_status moe_kernel_timer_enable(int32_t on) {
+  TimerState& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.on = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_kernel_timer_reset(void) {
+  TimerState& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (auto& r : t.recs) {
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.recs.clear();
+  t.open.assign(MOE_K_COUNT, -1);
+  return MOE_OK;
+}
+
+moe_status moe_kernel_timer_read(int32_t kernel_id, double* total_ms, int32_t* launches) {
+  if (kernel_id < 0 || kernel_id >= MOE_K_COUNT)
+    return fail(MOE_ERR_INVALID_ARG, "unknown kernel id");
+  TimerState& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  double sum = 0.0;
+  int n = 0;
+  for (auto& r : t.recs) {
+    if (r.id != kernel_id) continue;
+    float ms = 0.f;
+    hipError_t e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "moe_kernel_timer_read");
+    sum += ms;
+    ++n;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = n;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,157 @@
+// Weighted combine of the k expert outputs of each token, and its backward.
+//
+//   combine      Y[t] = sum_{j<k} w[t, j] y_perm[inv_pos[t*k + j]]
+//                (w == NULL: plain sum, which brings dX_perm back to tokens)
+//   combine_bwd  G[inv_pos[t*k + j]] = w[t, j] dY[t]
+//                dw[t, j] = <dY[t], y_perm[inv_pos[t*k + j]]>
+//
+// Both are HBM-bound streams over rows; slots are summed in the fixed order
+// j = 0..k-1 in float32, and the dot products reduce in a fixed tree, so
+// results are identical run to run. The weighted sum over the selected
+// experts closes the MoE block whose per-expert loop the faster-moe page
+// (Unsloth, "Fine-tune MoE models 12x faster", section "What is
+// torch._grouped_mm?") shows.
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+template <typename T> struct Pack;  // 16 bytes of T
+template <> struct Pack<bf16_t> {
+  static constexpr int n = 8;
+  __device__ static void unpack(const uint4& r, float (&v)[8]) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static uint4 pack(const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct Pack<float> {
+  static constexpr int n = 4;
+  __device__ static void unpack(const uint4& r, float (&v)[4]) {
+    v[0] = __uint_as_float(r.x); v[1] = __uint_as_float(r.y);
+    v[2] = __uint_as_float(r.z); v[3] = __uint_as_float(r.w);
+  }
+  __device__ static uint4 pack(const float (&v)[4]) {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                      __float_as_uint(v[3]));
+  }
+};
+
+// One thread per (token, 16-byte column chunk).
+template <typename Elem>
+__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ yp,
+                                                      const int32_t* __restrict__ inv_pos,
+                                                      const float* __restrict__ w, int T, int k,
+                                                      int64_t cpr, uint4* __restrict__ y) {
+  constexpr int n = Pack<Elem>::n;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t t = g / cpr, c = g - t * cpr;
+  if (t >= T) return;
+  float acc[n];
+#pragma unroll
+  for (int i = 0; i < n; ++i) acc[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int pos = inv_pos[t * k + j];
+    if (pos < 0) continue;
+    const float wj = w ? w[t * k + j] : 1.0f;
+    float v[n];
+    Pack<Elem>::unpack(yp[static_cast<int64_t>(pos) * cpr + c], v);
+#pragma unroll
+    for (int i = 0; i < n; ++i) acc[i] += wj * v[i];
+  }
+  y[t * cpr + c] = Pack<Elem>::pack(acc);
+}
+
+// One block per token; threads stride over the row's 16-byte chunks.
+template <typename Elem>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dy,
+                                                          const uint4* __restrict__ yexp,
+                                                          const int32_t* __restrict__ inv_pos,
+                                                          const float* __restrict__ w, int k,
+                                                          int64_t cpr, uint4* __restrict__ g,
+                                                          float* __restrict__ dw) {
+  constexpr int n = Pack<Elem>::n;
+  __shared__ float red[256 / kWave];
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  for (int j = 0; j < k; ++j) {
+    const int pos = inv_pos[t * k + j];
+    const float wj = w[t * k + j];
+    float part = 0.f;
+    if (pos >= 0) {
+      for (int64_t c = threadIdx.x; c < cpr; c += blockDim.x) {
+        float d[n], y[n], o[n];
+        Pack<Elem>::unpack(dy[t * cpr + c], d);
+        Pack<Elem>::unpack(yexp[static_cast<int64_t>(pos) * cpr + c], y);
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+          part += d[i] * y[i];
+          o[i] = wj * d[i];
+        }
+        g[static_cast<int64_t>(pos) * cpr + c] = Pack<Elem>::pack(o);
+      }
+    }
+    part = wave_sum(part);
+    if (lane == 0) red[wave] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 256 / kWave; ++i) s += red[i];
+      dw[t * k + j] = s;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos, const float* w,
+                          int T, int k, int H, void* y, hipStream_t s, KernelTimer* tm) {
+  const int esz = dtype == MOE_BF16 ? 2 : 4;
+  const int64_t cpr = static_cast<int64_t>(H) * esz / 16;
+  const int64_t total = static_cast<int64_t>(T) * cpr;
+  dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  TimedScope scope(tm, w ? MOE_K_COMBINE : MOE_K_UNPERMUTE, s);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint4*>(y_perm), inv_pos, w, T, k, cpr,
+                       static_cast<uint4*>(y));
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const uint4*>(y_perm), inv_pos, w, T, k, cpr,
+                       static_cast<uint4*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_exp,
+                              const int32_t* inv_pos, const float* w, int T, int k, int H,
+                              void* g, float* dw, hipStream_t s, KernelTimer* tm) {
+  const int esz = dtype == MOE_BF16 ? 2 : 4;
+  const int64_t cpr = static_cast<int64_t>(H) * esz / 16;
+  TimedScope scope(tm, MOE_K_COMBINE_BWD, s);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(T), dim3(256), 0, s,
+                       static_cast<const uint4*>(dy), static_cast<const uint4*>(y_exp), inv_pos,
+                       w, k, cpr, static_cast<uint4*>(g), dw);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(T), dim3(256), 0, s,
+                       static_cast<const uint4*>(dy), static_cast<const uint4*>(y_exp), inv_pos,
+                       w, k, cpr, static_cast<uint4*>(g), dw);
+  return hipGetLastError();
+}
+
+}  // namespace moe

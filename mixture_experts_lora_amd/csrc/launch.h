@@ -1,0 +1,74 @@
+// Internal host-side interface between the C ABI (api.hip) and the kernel
+// files. Not installed; the public interface is include/moe_lora.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_lora.h"
+
+namespace moe {
+
+// Optional event timer around kernel launches (see moe_kernel_timer_* in the
+// public header). A null KernelTimer* disables it.
+class KernelTimer {
+ public:
+  void record_start(int id, hipStream_t s);
+  void record_stop(int id, hipStream_t s);
+};
+KernelTimer* active_timer();
+
+struct TimedScope {
+  KernelTimer* tm;
+  int id;
+  hipStream_t s;
+  TimedScope(KernelTimer* t, int i, hipStream_t st) : tm(t), id(i), s(st) {
+    if (tm) tm->record_start(id, s);
+  }
+  ~TimedScope() {
+    if (tm) tm->record_stop(id, s);
+  }
+};
+
+// ---- routing
+hipError_t launch_route(const float* logits, int T, int E, int k, int router, int32_t* ids,
+                        float* w, hipStream_t s);
+hipError_t launch_route_bwd(const float* logits, const int32_t* ids, const float* dw, int T,
+                            int E, int k, int router, float* dlogits, hipStream_t s);
+
+// ---- permutation
+size_t permute_ws_bytes(int64_t N, int E);
+hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_pair, int32_t* inv_pos,
+                          int32_t* table, hipStream_t s, KernelTimer* tm);
+hipError_t launch_gather(const void* x, const int32_t* sorted_pair, const int32_t* offsets,
+                         int E, int k, int64_t N, int64_t row_bytes, void* x_perm,
+                         hipStream_t s, KernelTimer* tm);
+
+// ---- combine
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos, const float* w,
+                          int T, int k, int H, void* y, hipStream_t s, KernelTimer* tm);
+hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_exp,
+                              const int32_t* inv_pos, const float* w, int T, int k, int H,
+                              void* g, float* dw, hipStream_t s, KernelTimer* tm);
+
+// ---- grouped expert GEMMs
+struct ExpertDims {
+  int64_t N;  // routed rows
+  int H, I, E, r, dtype;
+  float scale;
+};
+
+size_t experts_fwd_ws_bytes(const ExpertDims& d);
+size_t experts_bwd_ws_bytes(const ExpertDims& d);
+
+hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int32_t* offsets,
+                              const moe_weights& w, const moe_saved& sv, void* ws,
+                              hipStream_t s, KernelTimer* tm);
+hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_perm,
+                              const int32_t* offsets, const moe_weights& w,
+                              const moe_saved& sv, void* dx_perm, const moe_lora_grads& gr,
+                              void* ws, hipStream_t s, KernelTimer* tm);
+
+}  // namespace moe

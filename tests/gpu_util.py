@@ -1,0 +1,63 @@
+"""Helpers shared by the GPU parity tests: run the HIP layer, run the oracle on
+host copies of the very same inputs, and compare to the stated tolerances.
+
+Tolerances (per tensor, normwise): max |gpu - ref| <= tol * max |ref|, with
+tol = 1e-4 for float32 layers and 2e-2 for bfloat16 layers; routing weights
+and their gradients are float32 arithmetic on both sides for every layer and
+use 1e-4 (5e-4 where they consume bf16 expert outputs). Indices are compared
+bit for bit.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from workloads import make_inputs
+from workloads.synth import to_numpy
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+WEIGHTS = ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def close(name, got, ref, tol):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    assert err <= tol * scale, f"{name}: max abs err {err:.3e} > {tol} * max|ref| {scale:.3e}"
+    return err, scale
+
+
+class ExpertSlices:
+    """Indexable by expert: a float32 host copy of one expert's slice (cached)."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t, self.cache = t, {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = to_numpy(self.t[e])
+        return self.cache[e]
+
+
+def run_gpu(layer_cls, shape, cfg, inp):
+    layer = layer_cls(shape, cfg.router)
+    w = {n: inp[n] for n in WEIGHTS}
+    layer.step(inp["x"], inp["logits"], inp["dy"], w)
+    torch.cuda.synchronize()
+    return layer
+
+
+def gpu_inputs(cfg, seed):
+    return make_inputs(cfg, seed, device="cuda")

@@ -1,0 +1,138 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the header
+declares, sizes its workspaces, and rejects bad arguments before touching the
+GPU (each call here fails validation, so no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_lora.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mixture_experts_lora_amd import _lib
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_layer_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_lora_fwd", "moe_grouped_lora_bwd",
+              "moe_unpermute_combine"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(lib):
+    from mixture_experts_lora_amd import _lib
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(_lib.EXPORTS)
+
+
+def shape(T=64, H=128, I=64, E=8, k=2, r=16, dtype=1, s=1.0):
+    from mixture_experts_lora_amd._lib import MoeShape
+    return MoeShape(T, H, I, E, k, r, dtype, s)
+
+
+def ws(lib, sh):
+    f, b, p = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    st = lib.moe_workspace_bytes(ctypes.byref(sh), ctypes.byref(f), ctypes.byref(b), ctypes.byref(p))
+    return st, f.value, b.value, p.value
+
+
+def test_workspace_never_holds_a_merged_delta(lib):
+    from workloads import CONFIGS
+    for cfg in CONFIGS.values():
+        sh = shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.r, 1 if cfg.dtype == "bf16" else 0)
+        st, f, b, p = ws(lib, sh)
+        assert st == 0
+        esz = 2 if cfg.dtype == "bf16" else 4
+        delta = cfg.E * 2 * cfg.I * cfg.H * esz   # one materialised W + B A for gate_up
+        # forward scratch is a tile list only; backward holds dH [N, 2I] and two [N, r]
+        assert f < 1 << 20
+        assert b <= cfg.N * (2 * cfg.I + 2 * cfg.r) * esz + (1 << 20)
+        if cfg.T * cfg.k < cfg.E * cfg.H:            # the regime the pages' memory model favours
+            assert b < delta
+        assert p > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), 1), (dict(k=0), 1), (dict(k=9), 1), (dict(E=0), 1), (dict(E=2000, k=2), 1),
+    (dict(H=100), 2), (dict(I=12), 2), (dict(r=65), 2), (dict(r=0), 1), (dict(dtype=7), 1),
+    (dict(k=40, E=64), 2),
+])
+def test_shape_validation(lib, kw, status):
+    st, *_ = ws(lib, shape(**kw))
+    assert st == status
+    assert lib.moe_last_error()
+
+
+def test_null_pointers_rejected(lib):
+    P = ctypes.c_void_p
+    fake = P(0x10000)
+    sh = shape()
+    assert lib.moe_route(None, 64, 8, 2, 0, fake, fake, None) == 1
+    assert lib.moe_route(fake, 64, 8, 2, 9, fake, fake, None) == 1        # unknown router
+    assert lib.moe_route(fake, 64, 8, 9, 0, fake, fake, None) == 1        # k > E
+    assert lib.moe_route_bwd(fake, fake, fake, 64, 8, 2, 0, None, None) == 1
+    assert lib.moe_permute(ctypes.byref(sh), None, fake, fake, fake, fake, fake, fake, fake,
+                           1 << 30, None) == 1
+    assert lib.moe_unpermute_combine(ctypes.byref(sh), fake, fake, None, None, None) == 1
+    assert lib.moe_unpermute_combine_bwd(ctypes.byref(sh), fake, fake, fake, None, fake, fake,
+                                         None) == 1
+    from mixture_experts_lora_amd._lib import MoeLoraGrads, MoeSaved, MoeWeights
+    w = MoeWeights(*(0x10000,) * 6)
+    sv = MoeSaved(0x10000, 0x10000, 0x10000, 0x10000, None)
+    assert lib.moe_grouped_lora_fwd(ctypes.byref(sh), fake, fake, ctypes.byref(w), ctypes.byref(sv),
+                                    fake, 1 << 30, None) == 1           # y_exp missing
+    g = MoeLoraGrads(0x10000, None, 0x10000, 0x10000)
+    assert lib.moe_grouped_lora_bwd(ctypes.byref(sh), fake, fake, fake, ctypes.byref(w),
+                                    ctypes.byref(sv), P(0x20000), ctypes.byref(g), fake, 1 << 30,
+                                    None) == 1
+
+
+def test_short_workspace_rejected(lib):
+    P = ctypes.c_void_p
+    fake = P(0x10000)
+    sh = shape()
+    st, f, b, p = ws(lib, sh)
+    from mixture_experts_lora_amd._lib import MoeLoraGrads, MoeSaved, MoeWeights
+    w = MoeWeights(*(0x10000,) * 6)
+    sv = MoeSaved(*(0x30000 + i * 0x1000 for i in range(5)))
+    g = MoeLoraGrads(*(0x50000 + i * 0x1000 for i in range(4)))
+    assert lib.moe_permute(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, P(0x20000), fake,
+                           p - 1, None) == 3
+    assert lib.moe_grouped_lora_fwd(ctypes.byref(sh), fake, fake, ctypes.byref(w), ctypes.byref(sv),
+                                    fake, f - 1, None) == 3
+    assert lib.moe_grouped_lora_bwd(ctypes.byref(sh), fake, P(0x60000), fake, ctypes.byref(w),
+                                    ctypes.byref(sv), P(0x70000), ctypes.byref(g), fake, b - 1,
+                                    None) == 3
+
+
+def test_aliasing_rejected(lib):
+    P = ctypes.c_void_p
+    fake = P(0x10000)
+    sh = shape()
+    assert lib.moe_unpermute_combine(ctypes.byref(sh), fake, P(0x20000), None, fake, None) == 1
+    assert lib.moe_route_bwd(fake, P(0x20000), P(0x30000), 64, 8, 2, 0, fake, None) == 1
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert lib.moe_status_str(st)
+
+
+def test_python_binding_checks_shapes_on_host():
+    import torch
+    import mixture_experts_lora_amd as mel
+    with pytest.raises(ValueError):
+        mel.moe_route(torch.zeros(4, 8), 2, "topk_softmax", torch.zeros(4, 2, dtype=torch.int32),
+                      torch.zeros(4, 2))          # CPU tensors are refused before any call

@@ -1,0 +1,84 @@
+"""GPU parity at the full layer sizes, in the launch configuration the bench times.
+
+At these sizes the oracle cannot redo the whole layer in seconds, so:
+  - routing ids and the permutation are checked bit for bit over all tokens;
+  - Y, dX, d logits and the routing weights are checked on sampled tokens
+    (the layer is per token, so the oracle runs on just those tokens);
+  - the saved activations and the LoRA gradients are checked for sampled
+    experts (the oracle runs that expert's full row group);
+  - every zero-token expert must get exactly zero LoRA gradients.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS
+from workloads.synth import to_numpy
+
+from gpu_util import TOL, WEIGHTS, ExpertSlices, close, gpu_inputs, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+SEED = 3407
+
+
+@pytest.mark.parametrize("name", ["gpt-oss-20b", "qwen3-30b-a3b", "deepseek-v3",
+                                  "gpt-oss-20b-long"])
+def test_full_size_layer(name):
+    import mixture_experts_lora_amd as mel
+    cfg = CONFIGS[name]
+    say(f"[fullsize] {name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} r={cfg.r}")
+    inp = gpu_inputs(cfg, SEED)
+    layer = run_gpu(mel.MoELoRALayer, mel.Shape.of(cfg), cfg, inp)
+    say("  gpu layer done")
+    tol = TOL[cfg.dtype]
+    logits = to_numpy(inp["logits"])
+    ids, w = oracle.route(logits, cfg.k, cfg.router)
+    counts, offsets, sp, inv = oracle.permute(ids, cfg.E)
+    np.testing.assert_array_equal(to_numpy(layer.topk_ids), ids)
+    np.testing.assert_array_equal(to_numpy(layer.counts), counts)
+    np.testing.assert_array_equal(to_numpy(layer.offsets), offsets)
+    np.testing.assert_array_equal(to_numpy(layer.sorted_pair), sp)
+    np.testing.assert_array_equal(to_numpy(layer.inv_pos), inv)
+    close("topk_w", to_numpy(layer.topk_w), w, 1e-5)
+    say(f"  routing exact; experts with no rows: {int((counts == 0).sum())}, "
+        f"max rows {int(counts.max())}")
+
+    wts = {n: ExpertSlices(inp[n]) for n in WEIGHTS}
+    x, dy = inp["x"], inp["dy"]
+    rng = np.random.default_rng(0)
+    nsamp = 4 if cfg.H * cfg.I > 8_000_000 else 6
+    S = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, nsamp - 2, replace=False)]))
+    xs, dys = to_numpy(x[S]), to_numpy(dy[S])
+    Ys, gs, _ = oracle.layer_forward_backward(xs, logits[S], dys, wts, cfg.k, cfg.router,
+                                              cfg.lora_scale)
+    close("Y[sample]", to_numpy(layer.y[S]), Ys, tol)
+    close("dX[sample]", to_numpy(layer.dx[S]), gs["dx"], tol)
+    close("d_topk_w[sample]", to_numpy(layer.d_topk_w[S]), gs["dw"], 5e-3)
+    close("d_logits[sample]", to_numpy(layer.d_logits[S]), gs["dlogits"], 5e-3)
+    say(f"  sampled tokens {S.tolist()} ok")
+
+    nz = np.where(counts > 0)[0]
+    experts = sorted({int(nz[np.argmax(counts[nz])]), int(nz[len(nz) // 2])})
+    wn = to_numpy(layer.topk_w)
+    for e in experts:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        pairs = sp[lo:hi]
+        toks = pairs // cfg.k
+        X_e = to_numpy(x[torch.from_numpy(toks).cuda()])
+        G_e = wn.reshape(-1)[pairs][:, None] * to_numpy(dy[torch.from_numpy(toks).cuda()])
+        we = {n: wts[n][e] for n in WEIGHTS}
+        f = oracle.expert_forward(X_e, **we, s=cfg.lora_scale)
+        b = oracle.expert_backward(X_e, G_e, f, **we, s=cfg.lora_scale)
+        close(f"h[e={e}]", to_numpy(layer.saved["h"][lo:hi]), f["h"], tol)
+        close(f"act[e={e}]", to_numpy(layer.saved["act"][lo:hi]), f["a"], tol)
+        close(f"y_exp[e={e}]", to_numpy(layer.saved["y_exp"][lo:hi]), f["y"], tol)
+        close(f"dx_perm[e={e}]", to_numpy(layer.dx_perm[lo:hi]), b["dx"], tol)
+        for n in ("da_gu", "db_gu", "da_d", "db_d"):
+            close(f"{n}[e={e}]", to_numpy(layer.grads[n][e]), b[n], tol)
+        say(f"  expert {e} ({hi - lo} rows) ok")
+    dead = np.where(counts == 0)[0]
+    for n in ("da_gu", "db_gu", "da_d", "db_d"):
+        if dead.size:
+            assert float(layer.grads[n][torch.from_numpy(dead).cuda()].abs().max()) == 0.0
