@@ -110,103 +110,6 @@ __device__ __forceinline__ T load_elem(const View<T>& v, int n, int k) {
   return v.kcontig ? v.base[g * v.ld + k] : v.base[static_cast<int64_t>(k) * v.ld + g];
 }
 
-// ----------------------------------------------------------------- tile staging (bf16)
-template <int ROWS, int BK>
-struct Regs {
-  static constexpr int CPR = BK / 8;               // 16-byte chunks per row (k contiguous)
-  static constexpr int CH = ROWS * CPR;            // chunks per tile
-  static constexpr int PER_K = (CH + 255) / 256;   // chunks per thread, k-contiguous
-  static constexpr int NBLK = ROWS * BK / 32;      // 4(k) x 8(mn) blocks, transposed
-  static constexpr int PER_B = (NBLK + 255) / 256;
-  static constexpr int NR = PER_K > 4 * PER_B ? PER_K : 4 * PER_B;
-  uint4 r[NR];
-};
-
-// Global -> registers (vector modes only; the scalar mode loads in commit()).
-template <int ROWS, int BK>
-__device__ __forceinline__ void fetch(const View<bf16_t>& v, int k0, Regs<ROWS, BK>& R) {
-  typedef Regs<ROWS, BK> RG;
-  const int tid = threadIdx.x;
-  if (!v.vec) return;
-  if (v.kcontig) {
-#pragma unroll
-    for (int i = 0; i < RG::PER_K; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / RG::CPR, kc = c % RG::CPR;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (c < RG::CH) {
-        bool ok;
-        const int64_t g = map_mn(v, row, ok);
-        const int k = k0 + kc * 8;
-        if (ok && k < v.klim) val = *reinterpret_cast<const uint4*>(v.base + g * v.ld + k);
-      }
-      R.r[i] = val;
-    }
-  } else {
-    constexpr int MNC = ROWS / 8;
-#pragma unroll
-    for (int i = 0; i < RG::PER_B; ++i) {
-      const int b = tid + 256 * i;
-      const int mnc = b % MNC, kq = b / MNC;
-      const bool ok = b < RG::NBLK && mnc * 8 < v.mn_lim;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = k0 + kq * 4 + q;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (ok && k < v.klim)
-          val = *reinterpret_cast<const uint4*>(v.base + static_cast<int64_t>(k) * v.ld + mnc * 8);
-        R.r[4 * i + q] = val;
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ uint32_t half_of(const uint4& r, int n) {
-  const uint32_t w = (n >> 1) == 0 ? r.x : (n >> 1) == 1 ? r.y : (n >> 1) == 2 ? r.z : r.w;
-  return (n & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
-// Registers (or global, scalar mode) -> LDS tile [ROWS][LDK], k contiguous.
-template <int ROWS, int BK, int LDK>
-__device__ __forceinline__ void commit(const View<bf16_t>& v, int k0, const Regs<ROWS, BK>& R,
-                                       bf16_t* lds) {
-  typedef Regs<ROWS, BK> RG;
-  const int tid = threadIdx.x;
-  if (!v.vec) {
-    for (int e = tid; e < ROWS * BK; e += 256) {
-      const int row = e / BK, kk = e % BK;
-      lds[row * LDK + kk] = load_elem(v, row, k0 + kk);
-    }
-    return;
-  }
-  if (v.kcontig) {
-#pragma unroll
-    for (int i = 0; i < RG::PER_K; ++i) {
-      const int c = tid + 256 * i;
-      if (c < RG::CH) {
-        const int row = c / RG::CPR, kc = c % RG::CPR;
-        *reinterpret_cast<uint4*>(lds + row * LDK + kc * 8) = R.r[i];
-      }
-    }
-  } else {
-    constexpr int MNC = ROWS / 8;
-#pragma unroll
-    for (int i = 0; i < RG::PER_B; ++i) {
-      const int b = tid + 256 * i;
-      if (b < RG::NBLK) {
-        const int mnc = b % MNC, kq = b / MNC;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          uint2 w;
-          w.x = half_of(R.r[4 * i + 0], n) | (half_of(R.r[4 * i + 1], n) << 16);
-          w.y = half_of(R.r[4 * i + 2], n) | (half_of(R.r[4 * i + 3], n) << 16);
-          *reinterpret_cast<uint2*>(lds + (mnc * 8 + n) * LDK + kq * 4) = w;
-        }
-      }
-    }
-  }
-}
-
 // ----------------------------------------------------------------- epilogue helpers
 // Four consecutive columns [col, col+4) of one row; ragged column tails and
 // unaligned rows fall back to element stores.
@@ -272,13 +175,186 @@ __device__ __forceinline__ void epi_swiglu(const GemmArgs& p, int64_t row0, int 
 }
 
 // ----------------------------------------------------------------- bf16 MFMA kernel
-template <int BM, int BN, int WM, int WN, int MODE, int EPI, bool PAIRED>
+// LDS tiles are kBK = 64 deep in k, unpadded, with a 16-byte-chunk XOR swizzle:
+//   k-contiguous tile [R][64]: row r keeps k-chunk c at position c ^ (r & 7)
+//   n-contiguous tile [64][R]: k-row k keeps n-chunk c at position c ^ nswz<R>(k)
+// Fragment reads are bank-conflict free: ds_read_b128 for the first layout,
+// ds_read_b64_tr_b16 (CDNA4 LDS transpose read) for the second, and both give
+// the same MFMA fragment: lane l holds 8 consecutive k (block l/32) of the
+// row or column l%32. Tiles are filled by buffer->LDS DMA (no register
+// staging): each wave instruction writes 1 KB of LDS, lane l at +16 l, from a
+// per-lane byte offset that encodes the swizzle; lanes outside the operand
+// get an out-of-range offset and the hardware writes zeros. Three LDS stages
+// keep two tiles in flight while the third is multiplied.
+constexpr int kBK = 64;
+constexpr int kStages = 3;
+constexpr uint32_t kOOB = 0x80000000u;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+template <int R>
+__device__ __forceinline__ int nswz(int k) {
+  return R >= 64 ? ((k & 3) << 1) : 0;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Own LDS traffic finished, then a workgroup barrier.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ int clamp_records(int64_t bytes) {
+  return bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes));
+}
+
+// DMA plan of one operand tile: resource, per-instruction lane offsets, k limit.
+template <int NI>
+struct Plan {
+  const void* base;  // buffer resource: base address and size in bytes
+  int nrec;
+  uint32_t vo[NI];
+  int vec;
+  int klim;
+  int64_t ld;
+  View<bf16_t> view;  // element view for the slow (non-DMA) fill
+};
+
+// k-contiguous operand of ROWS rows: element (row, k) at base[map(row)*ld + k].
+template <int ROWS>
+__device__ __forceinline__ void plan_kc(Plan<ROWS / 32>& P, const View<bf16_t>& v,
+                                        int64_t bytes, int vec, int wave, int lane) {
+  P.view = v;
+  P.vec = vec;
+  P.klim = v.klim;
+  P.ld = v.ld;
+  P.base = v.base;
+  P.nrec = clamp_records(bytes);
+  const int c = (lane & 7) ^ ((lane >> 3) & 7);  // k-chunk this lane fetches
+#pragma unroll
+  for (int i = 0; i < ROWS / 32; ++i) {
+    const int row = 8 * (wave * (ROWS / 32) + i) + (lane >> 3);
+    bool ok;
+    const int64_t g = map_mn(v, row, ok);
+    P.vo[i] = ok ? static_cast<uint32_t>((g * v.ld + c * 8) * 2) : kOOB;
+  }
+}
+
+// n-contiguous operand of ROWS columns: element (mn, k) at base[k*ld + mn].
+template <int ROWS>
+__device__ __forceinline__ void plan_nc(Plan<ROWS / 32>& P, const View<bf16_t>& v,
+                                        int64_t bytes, int vec, int wave, int lane) {
+  P.view = v;
+  P.vec = vec;
+  P.klim = v.klim;
+  P.ld = v.ld;
+  P.base = v.base;
+  P.nrec = clamp_records(bytes);
+  constexpr int CPR = ROWS / 8;        // 16-byte chunks per k-row
+  constexpr int KPI = 64 / CPR;        // k-rows per 1 KB instruction
+#pragma unroll
+  for (int i = 0; i < ROWS / 32; ++i) {
+    const int kr = (wave * (ROWS / 32) + i) * KPI + lane / CPR;
+    const int cn = (lane % CPR) ^ nswz<ROWS>(kr);
+    P.vo[i] = cn * 8 < v.mn_lim ? static_cast<uint32_t>((kr * v.ld + cn * 8) * 2) : kOOB;
+  }
+}
+
+// Issue one tile: DMA when possible, else an element-wise fill.
+template <int ROWS, bool KC>
+__device__ __forceinline__ void fill(const Plan<ROWS / 32>& P, int k0, char* lds, int wave,
+                                     int lane) {
+  if (P.vec) {
+    uint32_t soff;
+    bool tail = false;
+    if (KC) {
+      soff = static_cast<uint32_t>(k0) * 2;
+      tail = k0 + kBK > P.klim;
+    } else {
+      soff = static_cast<uint32_t>(k0 * P.ld * 2);
+    }
+    const int kc = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
+    const bool kok = !tail || (k0 + kc < P.klim);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(P.base), 0, P.nrec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < ROWS / 32; ++i) {
+      const uint32_t vo = kok ? P.vo[i] : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void*)(lds + (wave * (ROWS / 32) + i) * 1024), 16, vo, soff, 0, 0);
+    }
+  } else {
+    bf16_t* t = reinterpret_cast<bf16_t*>(lds);
+    for (int e = threadIdx.x; e < ROWS * kBK; e += 256) {
+      int byte;
+      bf16_t val;
+      if (KC) {
+        const int row = e / kBK, k = e % kBK;
+        byte = row * 128 + ((((k >> 3) ^ (row & 7))) << 4) + (k & 7) * 2;
+        val = load_elem(P.view, row, k0 + k);
+      } else {
+        const int k = e / ROWS, mn = e % ROWS;
+        byte = k * ROWS * 2 + (((mn >> 3) ^ nswz<ROWS>(k)) << 4) + (mn & 7) * 2;
+        val = load_elem(P.view, mn, k0 + k);
+      }
+      t[byte >> 1] = val;
+    }
+  }
+}
+
+// Per-lane LDS byte offsets of the MFMA fragments.
+template <int ROWS, bool KC, int NFR>
+struct FragAddr {
+  int off[KC ? 4 : NFR];  // KC: per k-step (same for all fragments); NC: per fragment
+};
+
+template <int ROWS, bool KC, int NFR>
+__device__ __forceinline__ void frag_addr(FragAddr<ROWS, KC, NFR>& F, const int (&fr_base)[NFR],
+                                          int lane) {
+  if (KC) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      F.off[ks] = (lane & 31) * 128 + ((((2 * ks + h) ^ (lane & 7))) << 4);
+  } else {
+    const int G = lane >> 4, li = lane & 15;
+    const int kl = (G >> 1) * 8 + (li >> 2);  // k row of this lane within a k-step (call 0)
+#pragma unroll
+    for (int f = 0; f < (KC ? 0 : NFR); ++f) {
+      const int n = fr_base[f] + (G & 1) * 16 + (li & 3) * 4;
+      F.off[KC ? 0 : f] = kl * ROWS * 2 + ((((n >> 3) ^ nswz<ROWS>(kl))) << 4) + (n & 7) * 2;
+    }
+  }
+}
+
+template <int ROWS, bool KC, int NFR>
+__device__ __forceinline__ bf16x8 read_frag(const char* tile, const FragAddr<ROWS, KC, NFR>& F,
+                                            int f, int fr_base_f, int ks) {
+  if (KC) {
+    return *reinterpret_cast<const bf16x8*>(tile + fr_base_f * 128 + F.off[ks]);
+  } else {
+    const char* p = tile + F.off[KC ? 0 : f] + ks * 16 * ROWS * 2;
+    v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+    v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(p + 4 * ROWS * 2));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    v8s r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, r);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int MODE, int EPI, bool PAIRED, bool A_KC, bool B_KC>
 __global__ __launch_bounds__(256) void gemm_bf16(GemmArgs p) {
-  constexpr int BK = 64, LDK = BK + 8;
   constexpr int WAVES_N = BN / WN, MF = WM / 32, NF = WN / 32;
+  constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2, ST = A_BYTES + B_BYTES;
+  constexpr int NIA = BM / 32, NIB = BN / 32;  // DMA instructions per wave per stage
   static_assert((BM / WM) * (BN / WN) == 4, "four waves per block");
   static_assert(!PAIRED || (NF % 2 == 0), "paired tiles need gate and up fragments");
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * LDK];
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * ST];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -289,9 +365,16 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmArgs p) {
     const int mtot = *p.ntiles;
     const int total = mtot * p.ntn;
     if (static_cast<int>(blockIdx.x) >= total) return;
+    // XCD-contiguous ranges, then groups of 8 M tiles swept across all N tiles,
+    // so the tiles an XCD runs together share A rows and weight columns in L2.
     const int L = xcd_remap(blockIdx.x, total);
-    const int mt = L % mtot;
-    n_tile = L / mtot;
+    constexpr int GM = 8;
+    const int mg = L / (GM * p.ntn);
+    const int gbase = mg * GM;
+    const int gsz = min(GM, mtot - gbase);
+    const int rem = L - gbase * p.ntn;
+    n_tile = rem / gsz;
+    const int mt = gbase + rem % gsz;
     const int4 t = p.tiles[mt];
     e = t.x;
     row0 = t.y;
@@ -311,17 +394,27 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmArgs p) {
   }
   const int n0 = PAIRED ? 0 : n_tile * BN;
 
-  auto make_views = [&](int seg, View<bf16_t>& va, View<bf16_t>& vb) {
+  // ---- DMA plans for the main segment (0) and the LoRA segment (1)
+  Plan<NIA> pa[2];
+  Plan<NIB> pb[2];
+  const int nseg = MODE == GROUP_M ? 2 : 1;
+#pragma unroll
+  for (int seg = 0; seg < 2; ++seg) {
+    if (seg >= nseg) break;
     const Opnd& A = p.a[seg];
     const Opnd& B = p.b[seg];
-    va.ld = A.ld; va.kcontig = A.kcontig; va.vec = A.vec; va.paired = 0;
-    vb.ld = B.ld; vb.kcontig = B.kcontig; vb.vec = B.vec; vb.paired = 0;
+    View<bf16_t> va{}, vb{};
+    va.ld = A.ld; va.kcontig = A.kcontig; va.vec = A.vec;
+    vb.ld = B.ld; vb.kcontig = B.kcontig; vb.vec = B.vec;
+    int64_t abytes, bbytes;
     if (MODE == GROUP_M) {
+      const int K = p.K[seg];
       va.base = static_cast<const bf16_t*>(A.ptr) + row0 * A.ld;
-      va.klim = p.K[seg];
+      va.klim = K;
       va.mn_lim = rows;
+      abytes = static_cast<int64_t>(rows) * A.ld * 2;
       const bf16_t* wb = static_cast<const bf16_t*>(B.ptr) + static_cast<int64_t>(e) * B.estride;
-      vb.klim = p.K[seg];
+      vb.klim = K;
       if (PAIRED) {
         vb.base = wb;
         vb.paired = 1;
@@ -329,23 +422,65 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmArgs p) {
         vb.pbase = n_tile * (BN / 2);
         vb.I = p.I;
         vb.mn_lim = BN;
-      } else {
-        vb.base = B.kcontig ? wb + static_cast<int64_t>(n0) * B.ld : wb + n0;
+        bbytes = static_cast<int64_t>(2) * p.I * B.ld * 2;
+      } else if (B_KC) {
+        vb.base = wb + static_cast<int64_t>(n0) * B.ld;
         vb.mn_lim = p.N - n0;
+        bbytes = static_cast<int64_t>(p.N - n0) * B.ld * 2;
+      } else {
+        vb.base = wb + n0;
+        vb.mn_lim = p.N - n0;
+        bbytes = static_cast<int64_t>(K) * B.ld * 2 - static_cast<int64_t>(n0) * 2;
       }
     } else {
       va.base = static_cast<const bf16_t*>(A.ptr) + row0 * A.ld + m0;
       va.klim = krows;
       va.mn_lim = p.M - m0;
+      abytes = static_cast<int64_t>(krows) * A.ld * 2 - static_cast<int64_t>(m0) * 2;
       vb.base = static_cast<const bf16_t*>(B.ptr) + row0 * B.ld + n0;
       vb.klim = krows;
       vb.mn_lim = p.N - n0;
+      bbytes = static_cast<int64_t>(krows) * B.ld * 2 - static_cast<int64_t>(n0) * 2;
+    }
+    if (A_KC) plan_kc<BM>(pa[seg], va, abytes, A.vec, wave, lane);
+    else plan_nc<BM>(pa[seg], va, abytes, A.vec, wave, lane);
+    if (B_KC) plan_kc<BN>(pb[seg], vb, bbytes, B.vec, wave, lane);
+    else plan_nc<BN>(pb[seg], vb, bbytes, B.vec, wave, lane);
+  }
+
+  const int nk0 = MODE == GROUP_M ? (p.K[0] + kBK - 1) / kBK : (krows + kBK - 1) / kBK;
+  const int nk1 = MODE == GROUP_M ? (p.K[1] + kBK - 1) / kBK : 0;
+  const int nk = nk0 + nk1;
+
+  auto issue = [&](int j) {
+    char* sa = smem + (j % kStages) * ST;
+    char* sb = sa + A_BYTES;
+    if (j < nk0) {
+      fill<BM, A_KC>(pa[0], j * kBK, sa, wave, lane);
+      fill<BN, B_KC>(pb[0], j * kBK, sb, wave, lane);
+    } else {
+      fill<BM, A_KC>(pa[1], (j - nk0) * kBK, sa, wave, lane);
+      fill<BN, B_KC>(pb[1], (j - nk0) * kBK, sb, wave, lane);
     }
   };
+  // DMA-only stage: the number of loads it leaves outstanding is known.
+  auto dma_stage = [&](int j) { return j < nk0 ? (pa[0].vec && pb[0].vec) : (pa[1].vec && pb[1].vec); };
 
-  const int nk0 = MODE == GROUP_M ? (p.K[0] + BK - 1) / BK : (krows + BK - 1) / BK;
-  const int nk1 = MODE == GROUP_M ? (p.K[1] + BK - 1) / BK : 0;
-  const int nk = nk0 + nk1;
+  // fragment row bases (in tile rows) and lane offsets
+  int fa_base[MF], fb_base[NF];
+#pragma unroll
+  for (int mi = 0; mi < MF; ++mi) fa_base[mi] = wm * WM + mi * 32;
+#pragma unroll
+  for (int ni = 0; ni < NF; ++ni) {
+    if (PAIRED)
+      fb_base[ni] = (ni < NF / 2) ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NF / 2) * 32;
+    else
+      fb_base[ni] = wn * WN + ni * 32;
+  }
+  FragAddr<BM, A_KC, MF> FA;
+  FragAddr<BN, B_KC, NF> FB;
+  frag_addr<BM, A_KC, MF>(FA, fa_base, lane);
+  frag_addr<BN, B_KC, NF>(FB, fb_base, lane);
 
   f32x16 acc[MF][NF];
 #pragma unroll
@@ -355,75 +490,30 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  Regs<BM, BK> ra;
-  Regs<BN, BK> rb;
-  View<bf16_t> va, vb;
-  int seg = 0, k0 = 0;
-  if (nk > 0) {
-    seg = nk0 > 0 ? 0 : 1;
-    k0 = 0;
-    make_views(seg, va, vb);
-    fetch<BM, BK>(va, k0, ra);
-    fetch<BN, BK>(vb, k0, rb);
-    commit<BM, BK, LDK>(va, k0, ra, smem);
-    commit<BN, BK, LDK>(vb, k0, rb, smem + BM * LDK);
-  }
-  __syncthreads();
-
+  if (nk > 0) issue(0);
+  if (nk > 1) issue(1);
   for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    const int kvalid = (seg == 0 ? (MODE == GROUP_M ? p.K[0] : krows) : p.K[1]) - k0;
-    View<bf16_t> na, nb;
-    int nseg = seg, nk0v = k0;
-    const bool has_next = it + 1 < nk;
-    if (has_next) {
-      if (it + 1 < nk0) {
-        nseg = 0;
-        nk0v = (it + 1) * BK;
-      } else {
-        nseg = 1;
-        nk0v = (it + 1 - nk0) * BK;
-      }
-      make_views(nseg, na, nb);
-      fetch<BM, BK>(na, nk0v, ra);
-      fetch<BN, BK>(nb, nk0v, rb);
+    if (it + 1 < nk && dma_stage(it + 1))
+      wait_vmcnt<NIA + NIB>();
+    else
+      wait_vmcnt<0>();
+    barrier_lds();
+    if (it + 2 < nk) issue(it + 2);
+    const char* sa = smem + (it % kStages) * ST;
+    const char* sb = sa + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      bf16x8 af[MF], bf[NF];
+#pragma unroll
+      for (int mi = 0; mi < MF; ++mi) af[mi] = read_frag<BM, A_KC, MF>(sa, FA, mi, fa_base[mi], ks);
+#pragma unroll
+      for (int ni = 0; ni < NF; ++ni) bf[ni] = read_frag<BN, B_KC, NF>(sb, FB, ni, fb_base[ni], ks);
+#pragma unroll
+      for (int mi = 0; mi < MF; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NF; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ni], af[mi], acc[mi][ni], 0, 0, 0);
     }
-
-    const bf16_t* sA = smem + cur * (BM + BN) * LDK;
-    const bf16_t* sB = sA + BM * LDK;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks * 16 < kvalid) {
-        bf16x8 af[MF], bf[NF];
-        const int kof = ks * 16 + (lane >> 5) * 8;
-#pragma unroll
-        for (int mi = 0; mi < MF; ++mi)
-          af[mi] = *reinterpret_cast<const bf16x8*>(sA + (wm * WM + mi * 32 + (lane & 31)) * LDK + kof);
-#pragma unroll
-        for (int ni = 0; ni < NF; ++ni) {
-          int nr;
-          if (PAIRED)
-            nr = (ni < NF / 2) ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NF / 2) * 32;
-          else
-            nr = wn * WN + ni * 32;
-          bf[ni] = *reinterpret_cast<const bf16x8*>(sB + (nr + (lane & 31)) * LDK + kof);
-        }
-#pragma unroll
-        for (int mi = 0; mi < MF; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NF; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ni], af[mi], acc[mi][ni], 0, 0, 0);
-      }
-    }
-
-    if (has_next) {
-      bf16_t* dA = smem + (cur ^ 1) * (BM + BN) * LDK;
-      commit<BM, BK, LDK>(na, nk0v, ra, dA);
-      commit<BN, BK, LDK>(nb, nk0v, rb, dA + BM * LDK);
-      seg = nseg;
-      k0 = nk0v;
-    }
-    __syncthreads();
   }
 
   // Lane holds, for MFMA tile (mi, ni), row m = wm*WM + mi*32 + lane%32 and the
@@ -687,9 +777,18 @@ hipError_t side_product(const ExpertDims& d, const int32_t* offsets, const WsLay
   a.scale = d.scale;
   if (d.dtype == MOE_BF16) {
     a.ntn = 1;
+    if (l_kcontig) {
+      if (d.r <= 32)
+        return launch(gemm_bf16<128, 32, 32, 32, GROUP_M, EPI_STORE, false, true, true>,
+                      gm_grid(d, 1), a, s);
+      return launch(gemm_bf16<128, 64, 32, 64, GROUP_M, EPI_STORE, false, true, true>,
+                    gm_grid(d, 1), a, s);
+    }
     if (d.r <= 32)
-      return launch(gemm_bf16<128, 32, 32, 32, GROUP_M, EPI_STORE, false>, gm_grid(d, 1), a, s);
-    return launch(gemm_bf16<128, 64, 32, 64, GROUP_M, EPI_STORE, false>, gm_grid(d, 1), a, s);
+      return launch(gemm_bf16<128, 32, 32, 32, GROUP_M, EPI_STORE, false, true, false>,
+                    gm_grid(d, 1), a, s);
+    return launch(gemm_bf16<128, 64, 32, 64, GROUP_M, EPI_STORE, false, true, false>,
+                  gm_grid(d, 1), a, s);
   }
   a.ntn = ceil_div(d.r, 64);
   return launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, a.ntn), a, s);
@@ -716,19 +815,19 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
       a.ntn = 1;
       if (Q <= 32) {
         a.ntm = ceil_div(P, 256);
-        return launch(gemm_bf16<256, 32, 64, 32, GROUP_K, EPI_STORE, false>, d.E * a.ntm, a, s);
+        return launch(gemm_bf16<256, 32, 64, 32, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm, a, s);
       }
       a.ntm = ceil_div(P, 256);
-      return launch(gemm_bf16<256, 64, 64, 64, GROUP_K, EPI_STORE, false>, d.E * a.ntm, a, s);
+      return launch(gemm_bf16<256, 64, 64, 64, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm, a, s);
     }
     // [r, big] (or both small)
     a.ntn = ceil_div(Q, 256);
     if (P <= 32) {
       a.ntm = 1;
-      return launch(gemm_bf16<32, 256, 32, 64, GROUP_K, EPI_STORE, false>, d.E * a.ntn, a, s);
+      return launch(gemm_bf16<32, 256, 32, 64, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntn, a, s);
     }
     a.ntm = ceil_div(P, 64);
-    return launch(gemm_bf16<64, 256, 64, 64, GROUP_K, EPI_STORE, false>, d.E * a.ntm * a.ntn, a,
+    return launch(gemm_bf16<64, 256, 64, 64, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm * a.ntn, a,
                   s);
   }
   a.ntm = ceil_div(P, 64);
@@ -786,7 +885,7 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
     TimedScope ts(tm, MOE_K_GATE_UP_FWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(I, 128);
-      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_SWIGLU, true>, gm_grid(d, a.ntn),
+      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_SWIGLU, true, true, true>, gm_grid(d, a.ntn),
                      a, s));
     } else {
       a.ntn = ceil_div(I, 64);
@@ -812,7 +911,7 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
     TimedScope ts(tm, MOE_K_DOWN_FWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(H, 256);
-      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_STORE, false>, gm_grid(d, a.ntn),
+      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_STORE, false, true, true>, gm_grid(d, a.ntn),
                      a, s));
     } else {
       a.ntn = ceil_div(H, 64);
@@ -860,7 +959,7 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     TimedScope ts(tm, MOE_K_DOWN_BWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(I, 256);
-      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_SWIGLU_BWD, false>,
+      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_SWIGLU_BWD, false, true, false>,
                      gm_grid(d, a.ntn), a, s));
     } else {
       a.ntn = ceil_div(I, 64);
@@ -891,7 +990,7 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     TimedScope ts(tm, MOE_K_GATE_UP_BWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(H, 256);
-      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_STORE, false>, gm_grid(d, a.ntn),
+      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_STORE, false, true, false>, gm_grid(d, a.ntn),
                      a, s));
     } else {
       a.ntn = ceil_div(H, 64);
