@@ -104,7 +104,9 @@ def main():
     ap.add_argument("--config", default=None)
     ap.add_argument("--seed", type=int, default=3407)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="only copy MIB mebibytes device-to-device once (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer is benchmarked on a single MI355X "
@@ -112,6 +114,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calib_copy:
+        n = args.calib_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "read_bytes": n, "write_bytes": n}))
+        return
     import mixture_experts_lora_amd as mel
     from workloads import BENCH_CONFIG, get_config, make_inputs
 

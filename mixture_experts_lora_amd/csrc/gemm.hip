@@ -33,6 +33,8 @@
 // weight tile is the MFMA A operand so that each lane ends up holding four
 // consecutive output columns of one row (8-byte stores). float32 layers use a
 // plain FMA kernel with the same tiling logic.
+#include <stdlib.h>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -175,27 +177,33 @@ __device__ __forceinline__ void epi_swiglu(const GemmArgs& p, int64_t row0, int 
 }
 
 // ----------------------------------------------------------------- bf16 MFMA kernel
-// LDS tiles are kBK = 64 deep in k, unpadded, with a 16-byte-chunk XOR swizzle:
-//   k-contiguous tile [R][64]: row r keeps k-chunk c at position c ^ (r & 7)
-//   n-contiguous tile [64][R]: k-row k keeps n-chunk c at position c ^ nswz<R>(k)
-// Fragment reads are bank-conflict free: ds_read_b128 for the first layout,
-// ds_read_b64_tr_b16 (CDNA4 LDS transpose read) for the second, and both give
-// the same MFMA fragment: lane l holds 8 consecutive k (block l/32) of the
-// row or column l%32. Tiles are filled by buffer->LDS DMA (no register
-// staging): each wave instruction writes 1 KB of LDS, lane l at +16 l, from a
-// per-lane byte offset that encodes the swizzle; lanes outside the operand
-// get an out-of-range offset and the hardware writes zeros. Three LDS stages
-// keep two tiles in flight while the third is multiplied.
-constexpr int kBK = 64;
-constexpr int kStages = 3;
+// LDS tiles are BK (32 or 64) deep in k, unpadded, with 16-byte-chunk XOR swizzles:
+//   k-contiguous tile [R][BK]: row r keeps k-chunk c at position c ^ kswz<BK>(r)
+//   n-contiguous tile [BK][R]: k-row k keeps n-chunk c at position c ^ nswz<R>(k)
+// chosen so that every 256-byte group of a fragment read (16 lanes of
+// ds_read_b128, 32 lanes of ds_read_b64_tr_b16) touches each LDS bank once.
+// Both layouts yield the same MFMA fragment: lane l holds 8 consecutive k
+// (block l/32) of the row or column l%32 (the transpose read, CDNA4's
+// ds_read_b64_tr_b16, gathers them from the k-major tile). Tiles are filled by
+// buffer->LDS DMA with no register staging: each wave instruction writes 1 KB
+// of LDS, lane l at +16 l, from a per-lane byte offset that encodes the
+// swizzle; lanes outside the operand get an out-of-range offset and the
+// hardware writes zeros. NST LDS stages keep NST-1 tiles in flight while one
+// is multiplied.
 constexpr uint32_t kOOB = 0x80000000u;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+template <int BK>
+__device__ __forceinline__ int kswz(int row) {
+  return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
 
 template <int R>
 __device__ __forceinline__ int nswz(int k) {
-  return R >= 64 ? ((k & 3) << 1) : 0;
+  return R >= 128 ? ((k & 3) << 2) : (R == 64 ? (((k >> 1) & 1) << 2) : 0);
 }
 
 template <int N>
@@ -208,93 +216,131 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (V#) over [base, base + nrec bytes): raw, stride 0.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, int nrec) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = static_cast<uint32_t>(b);
+  r[1] = static_cast<uint32_t>(b >> 32) & 0xffffu;
+  r[2] = static_cast<uint32_t>(nrec);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// 16 bytes per lane, global -> LDS: lane l's bytes land at lds + 16 l. The
+// instruction is issued from inline asm so that the compiler does not treat
+// it as an LDS store it must wait for before every later LDS read (it would
+// insert s_waitcnt vmcnt(0) and drain all tiles in flight); completion is
+// tracked by the explicit vmcnt waits of the pipeline instead. The asm has no
+// outputs, so no register is ever written by a load still in flight.
+__device__ __forceinline__ void dma16(const char* lds, const u32x4& rs, uint32_t vo,
+                                      uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(lds))));
+  // resource and offset are wave-uniform; make that explicit for the SGPR operands
+  u32x4 srs;
+  srs[0] = __builtin_amdgcn_readfirstlane(rs[0]);
+  srs[1] = __builtin_amdgcn_readfirstlane(rs[1]);
+  srs[2] = __builtin_amdgcn_readfirstlane(rs[2]);
+  srs[3] = __builtin_amdgcn_readfirstlane(rs[3]);
+  const uint32_t ssoff = __builtin_amdgcn_readfirstlane(soff);
+  // s_nop 4: the resource/offset SGPRs may have just been written by VALU
+  // (v_readfirstlane), which a VMEM read may only follow after 5 wait states,
+  // and M0 needs 1 wait state before an LDS DMA; the compiler's hazard
+  // recognizer does not look inside inline asm, so the asm provides both.
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(vo),
+               "s"(srs), "s"(ssoff)
+               : "memory");
+}
+
 __device__ __forceinline__ int clamp_records(int64_t bytes) {
   return bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes));
 }
 
-// DMA plan of one operand tile: resource, per-instruction lane offsets, k limit.
-template <int NI>
+// DMA geometry of one operand tile of ROWS rows (or columns) x BK.
+template <int ROWS, int BK, bool KC>
+struct Geo {
+  static constexpr int TI = ROWS * BK * 2 / 1024;  // 1 KB instructions per tile
+  static constexpr int NIW = (TI + 3) / 4;         // per wave (upper bound)
+  static constexpr int MINW = TI / 4;              // issued by every wave
+  static constexpr int CPR = KC ? BK / 8 : ROWS / 8;        // chunks per LDS row
+  static constexpr int RPI = KC ? 512 / BK : 512 / ROWS;    // LDS rows per instruction
+};
+
+// DMA plan of one operand tile: buffer (base, bytes), per-instruction lane offsets.
+template <int ROWS, int BK, bool KC>
 struct Plan {
-  const void* base;  // buffer resource: base address and size in bytes
+  const void* base;
   int nrec;
-  uint32_t vo[NI];
+  uint32_t vo[Geo<ROWS, BK, KC>::NIW];
   int vec;
   int klim;
   int64_t ld;
   View<bf16_t> view;  // element view for the slow (non-DMA) fill
 };
 
-// k-contiguous operand of ROWS rows: element (row, k) at base[map(row)*ld + k].
-template <int ROWS>
-__device__ __forceinline__ void plan_kc(Plan<ROWS / 32>& P, const View<bf16_t>& v,
-                                        int64_t bytes, int vec, int wave, int lane) {
+template <int ROWS, int BK, bool KC>
+__device__ __forceinline__ void make_plan(Plan<ROWS, BK, KC>& P, const View<bf16_t>& v,
+                                          int64_t bytes, int vec, int wave, int lane) {
+  typedef Geo<ROWS, BK, KC> G;
   P.view = v;
   P.vec = vec;
   P.klim = v.klim;
   P.ld = v.ld;
   P.base = v.base;
   P.nrec = clamp_records(bytes);
-  const int c = (lane & 7) ^ ((lane >> 3) & 7);  // k-chunk this lane fetches
 #pragma unroll
-  for (int i = 0; i < ROWS / 32; ++i) {
-    const int row = 8 * (wave * (ROWS / 32) + i) + (lane >> 3);
-    bool ok;
-    const int64_t g = map_mn(v, row, ok);
-    P.vo[i] = ok ? static_cast<uint32_t>((g * v.ld + c * 8) * 2) : kOOB;
-  }
-}
-
-// n-contiguous operand of ROWS columns: element (mn, k) at base[k*ld + mn].
-template <int ROWS>
-__device__ __forceinline__ void plan_nc(Plan<ROWS / 32>& P, const View<bf16_t>& v,
-                                        int64_t bytes, int vec, int wave, int lane) {
-  P.view = v;
-  P.vec = vec;
-  P.klim = v.klim;
-  P.ld = v.ld;
-  P.base = v.base;
-  P.nrec = clamp_records(bytes);
-  constexpr int CPR = ROWS / 8;        // 16-byte chunks per k-row
-  constexpr int KPI = 64 / CPR;        // k-rows per 1 KB instruction
-#pragma unroll
-  for (int i = 0; i < ROWS / 32; ++i) {
-    const int kr = (wave * (ROWS / 32) + i) * KPI + lane / CPR;
-    const int cn = (lane % CPR) ^ nswz<ROWS>(kr);
-    P.vo[i] = cn * 8 < v.mn_lim ? static_cast<uint32_t>((kr * v.ld + cn * 8) * 2) : kOOB;
+  for (int i = 0; i < G::NIW; ++i) {
+    const int j = wave + 4 * i;  // instruction index within the tile
+    const int r = G::RPI * j + lane / G::CPR;
+    const int p = lane % G::CPR;
+    uint32_t vo = kOOB;
+    if (KC) {
+      const int c = p ^ kswz<BK>(r);
+      bool ok;
+      const int64_t g = map_mn(v, r, ok);
+      if (ok && r < ROWS) vo = static_cast<uint32_t>((g * v.ld + c * 8) * 2);
+    } else {
+      const int cn = p ^ nswz<ROWS>(r);
+      if (cn * 8 < v.mn_lim && r < BK) vo = static_cast<uint32_t>((r * v.ld + cn * 8) * 2);
+    }
+    P.vo[i] = vo;
   }
 }
 
 // Issue one tile: DMA when possible, else an element-wise fill.
-template <int ROWS, bool KC>
-__device__ __forceinline__ void fill(const Plan<ROWS / 32>& P, int k0, char* lds, int wave,
+template <int ROWS, int BK, bool KC>
+__device__ __forceinline__ void fill(const Plan<ROWS, BK, KC>& P, int k0, char* lds, int wave,
                                      int lane) {
+  typedef Geo<ROWS, BK, KC> G;
   if (P.vec) {
-    uint32_t soff;
-    bool tail = false;
-    if (KC) {
-      soff = static_cast<uint32_t>(k0) * 2;
-      tail = k0 + kBK > P.klim;
-    } else {
-      soff = static_cast<uint32_t>(k0 * P.ld * 2);
-    }
-    const int kc = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
-    const bool kok = !tail || (k0 + kc < P.klim);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(P.base), 0, P.nrec, 0x00020000);
+    const uint32_t soff = KC ? static_cast<uint32_t>(k0) * 2
+                             : static_cast<uint32_t>(static_cast<int64_t>(k0) * P.ld * 2);
+    const bool tail = KC && (k0 + BK > P.klim);  // n-contiguous tails hit the buffer bound
+    const u32x4 rs = buffer_rsrc(P.base, P.nrec);
 #pragma unroll
-    for (int i = 0; i < ROWS / 32; ++i) {
-      const uint32_t vo = kok ? P.vo[i] : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void*)(lds + (wave * (ROWS / 32) + i) * 1024), 16, vo, soff, 0, 0);
+    for (int i = 0; i < G::NIW; ++i) {
+      const int j = wave + 4 * i;
+      if (G::TI % 4 == 0 || j < G::TI) {
+        uint32_t vo = P.vo[i];
+        if (tail) {
+          const int r = G::RPI * j + lane / G::CPR;
+          const int c = (lane % G::CPR) ^ kswz<BK>(r);
+          if (k0 + c * 8 >= P.klim) vo = kOOB;
+        }
+        dma16(lds + j * 1024, rs, vo, soff);
+      }
     }
   } else {
     bf16_t* t = reinterpret_cast<bf16_t*>(lds);
-    for (int e = threadIdx.x; e < ROWS * kBK; e += 256) {
+    for (int e = threadIdx.x; e < ROWS * BK; e += 256) {
       int byte;
       bf16_t val;
       if (KC) {
-        const int row = e / kBK, k = e % kBK;
-        byte = row * 128 + ((((k >> 3) ^ (row & 7))) << 4) + (k & 7) * 2;
+        const int row = e / BK, k = e % BK;
+        byte = row * BK * 2 + (((k >> 3) ^ kswz<BK>(row)) << 4) + (k & 7) * 2;
         val = load_elem(P.view, row, k0 + k);
       } else {
         const int k = e / ROWS, mn = e % ROWS;
@@ -306,23 +352,41 @@ __device__ __forceinline__ void fill(const Plan<ROWS / 32>& P, int k0, char* lds
   }
 }
 
+// One DMA instruction (index i of this wave's share) of a tile; DMA plans only.
+template <int ROWS, int BK, bool KC>
+__device__ __forceinline__ void fill_one(const Plan<ROWS, BK, KC>& P, int k0, char* lds,
+                                         int wave, int lane, int i) {
+  typedef Geo<ROWS, BK, KC> G;
+  const int j = wave + 4 * i;
+  if (G::TI % 4 != 0 && j >= G::TI) return;
+  const uint32_t soff = KC ? static_cast<uint32_t>(k0) * 2
+                           : static_cast<uint32_t>(static_cast<int64_t>(k0) * P.ld * 2);
+  uint32_t vo = P.vo[i];
+  if (KC && k0 + BK > P.klim) {  // k tail of a k-contiguous operand: mask by lane
+    const int r = G::RPI * j + lane / G::CPR;
+    const int c = (lane % G::CPR) ^ kswz<BK>(r);
+    if (k0 + c * 8 >= P.klim) vo = kOOB;
+  }
+  dma16(lds + j * 1024, buffer_rsrc(P.base, P.nrec), vo, soff);
+}
+
 // Per-lane LDS byte offsets of the MFMA fragments.
-template <int ROWS, bool KC, int NFR>
+template <int ROWS, int BK, bool KC, int NFR>
 struct FragAddr {
-  int off[KC ? 4 : NFR];  // KC: per k-step (same for all fragments); NC: per fragment
+  int off[KC ? BK / 16 : NFR];  // KC: per k-step (shared by all fragments); NC: per fragment
 };
 
-template <int ROWS, bool KC, int NFR>
-__device__ __forceinline__ void frag_addr(FragAddr<ROWS, KC, NFR>& F, const int (&fr_base)[NFR],
-                                          int lane) {
+template <int ROWS, int BK, bool KC, int NFR>
+__device__ __forceinline__ void frag_addr(FragAddr<ROWS, BK, KC, NFR>& F,
+                                          const int (&fr_base)[NFR], int lane) {
   if (KC) {
-    const int h = lane >> 5;
+    const int h = lane >> 5, r = lane & 31;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      F.off[ks] = (lane & 31) * 128 + ((((2 * ks + h) ^ (lane & 7))) << 4);
+    for (int ks = 0; ks < BK / 16; ++ks)
+      F.off[ks] = r * BK * 2 + ((((2 * ks + h) ^ kswz<BK>(r))) << 4);
   } else {
     const int G = lane >> 4, li = lane & 15;
-    const int kl = (G >> 1) * 8 + (li >> 2);  // k row of this lane within a k-step (call 0)
+    const int kl = (G >> 1) * 8 + (li >> 2);  // k row of this lane in a k-step (first read)
 #pragma unroll
     for (int f = 0; f < (KC ? 0 : NFR); ++f) {
       const int n = fr_base[f] + (G & 1) * 16 + (li & 3) * 4;
@@ -331,30 +395,34 @@ __device__ __forceinline__ void frag_addr(FragAddr<ROWS, KC, NFR>& F, const int 
   }
 }
 
-template <int ROWS, bool KC, int NFR>
-__device__ __forceinline__ bf16x8 read_frag(const char* tile, const FragAddr<ROWS, KC, NFR>& F,
-                                            int f, int fr_base_f, int ks) {
+template <int ROWS, int BK, bool KC, int NFR>
+__device__ __forceinline__ bf16x8 read_frag(const char* tile,
+                                            const FragAddr<ROWS, BK, KC, NFR>& F, int f,
+                                            int fr_base_f, int ks) {
   if (KC) {
-    return *reinterpret_cast<const bf16x8*>(tile + fr_base_f * 128 + F.off[ks]);
+    return *reinterpret_cast<const bf16x8*>(tile + fr_base_f * BK * 2 + F.off[ks]);
   } else {
     const char* p = tile + F.off[KC ? 0 : f] + ks * 16 * ROWS * 2;
     v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
     v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4s*)(p + 4 * ROWS * 2));
-    typedef short v8s __attribute__((ext_vector_type(8)));
     v8s r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, r);
   }
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, int EPI, bool PAIRED, bool A_KC, bool B_KC>
-__global__ __launch_bounds__(256) void gemm_bf16(GemmArgs p) {
+template <int BM, int BN, int WM, int WN, int BK, int NST, int MINB, int MODE, int EPI,
+          bool PAIRED, bool A_KC, bool B_KC>
+__global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
   constexpr int WAVES_N = BN / WN, MF = WM / 32, NF = WN / 32;
-  constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2, ST = A_BYTES + B_BYTES;
-  constexpr int NIA = BM / 32, NIB = BN / 32;  // DMA instructions per wave per stage
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, ST = A_BYTES + B_BYTES;
+  typedef Geo<BM, BK, A_KC> GA;
+  typedef Geo<BN, BK, B_KC> GB;
   static_assert((BM / WM) * (BN / WN) == 4, "four waves per block");
   static_assert(!PAIRED || (NF % 2 == 0), "paired tiles need gate and up fragments");
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * ST];
+  static_assert(GA::TI >= 1 && GB::TI >= 1, "tile smaller than one DMA instruction");
+  static_assert(NST >= 3 && NST <= 6 && (NST - 2) * (GA::MINW + GB::MINW) <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[NST * ST];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -394,13 +462,13 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmArgs p) {
   }
   const int n0 = PAIRED ? 0 : n_tile * BN;
 
-  // ---- DMA plans for the main segment (0) and the LoRA segment (1)
-  Plan<NIA> pa[2];
-  Plan<NIB> pb[2];
-  const int nseg = MODE == GROUP_M ? 2 : 1;
-#pragma unroll
-  for (int seg = 0; seg < 2; ++seg) {
-    if (seg >= nseg) break;
+  // ---- DMA plans for the main segment (0) and the LoRA segment (1). Kept in
+  // plain variables, never indexed by a runtime value, so they stay in
+  // registers: a scratch access would bring an s_waitcnt vmcnt(0) that also
+  // drains every tile in flight.
+  Plan<BM, BK, A_KC> pa0, pa1;
+  Plan<BN, BK, B_KC> pb0, pb1;
+  auto build = [&](int seg, Plan<BM, BK, A_KC>& PA, Plan<BN, BK, B_KC>& PB) {
     const Opnd& A = p.a[seg];
     const Opnd& B = p.b[seg];
     View<bf16_t> va{}, vb{};
@@ -442,45 +510,51 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmArgs p) {
       vb.mn_lim = p.N - n0;
       bbytes = static_cast<int64_t>(krows) * B.ld * 2 - static_cast<int64_t>(n0) * 2;
     }
-    if (A_KC) plan_kc<BM>(pa[seg], va, abytes, A.vec, wave, lane);
-    else plan_nc<BM>(pa[seg], va, abytes, A.vec, wave, lane);
-    if (B_KC) plan_kc<BN>(pb[seg], vb, bbytes, B.vec, wave, lane);
-    else plan_nc<BN>(pb[seg], vb, bbytes, B.vec, wave, lane);
+    make_plan<BM, BK, A_KC>(PA, va, abytes, A.vec, wave, lane);
+    make_plan<BN, BK, B_KC>(PB, vb, bbytes, B.vec, wave, lane);
+  };
+  build(0, pa0, pb0);
+  if (MODE == GROUP_M) {
+    build(1, pa1, pb1);
+  } else {
+    pa1 = pa0;
+    pb1 = pb0;
   }
 
-  const int nk0 = MODE == GROUP_M ? (p.K[0] + kBK - 1) / kBK : (krows + kBK - 1) / kBK;
-  const int nk1 = MODE == GROUP_M ? (p.K[1] + kBK - 1) / kBK : 0;
+  const int nk0 = MODE == GROUP_M ? (p.K[0] + BK - 1) / BK : (krows + BK - 1) / BK;
+  const int nk1 = MODE == GROUP_M ? (p.K[1] + BK - 1) / BK : 0;
   const int nk = nk0 + nk1;
+  const bool dma0 = pa0.vec && pb0.vec, dma1 = pa1.vec && pb1.vec;
 
-  auto issue = [&](int j) {
-    char* sa = smem + (j % kStages) * ST;
+  auto issue = [&](int j) {  // a whole stage at once (prologue, element-wise fills)
+    char* sa = smem + (j % NST) * ST;
     char* sb = sa + A_BYTES;
     if (j < nk0) {
-      fill<BM, A_KC>(pa[0], j * kBK, sa, wave, lane);
-      fill<BN, B_KC>(pb[0], j * kBK, sb, wave, lane);
+      fill<BM, BK, A_KC>(pa0, j * BK, sa, wave, lane);
+      fill<BN, BK, B_KC>(pb0, j * BK, sb, wave, lane);
     } else {
-      fill<BM, A_KC>(pa[1], (j - nk0) * kBK, sa, wave, lane);
-      fill<BN, B_KC>(pb[1], (j - nk0) * kBK, sb, wave, lane);
+      fill<BM, BK, A_KC>(pa1, (j - nk0) * BK, sa, wave, lane);
+      fill<BN, BK, B_KC>(pb1, (j - nk0) * BK, sb, wave, lane);
     }
   };
-  // DMA-only stage: the number of loads it leaves outstanding is known.
-  auto dma_stage = [&](int j) { return j < nk0 ? (pa[0].vec && pb[0].vec) : (pa[1].vec && pb[1].vec); };
+  // A stage filled only by DMA leaves at least MINW loads per operand outstanding.
+  auto dma_stage = [&](int j) { return j < nk0 ? dma0 : dma1; };
 
-  // fragment row bases (in tile rows) and lane offsets
   int fa_base[MF], fb_base[NF];
 #pragma unroll
   for (int mi = 0; mi < MF; ++mi) fa_base[mi] = wm * WM + mi * 32;
 #pragma unroll
   for (int ni = 0; ni < NF; ++ni) {
     if (PAIRED)
-      fb_base[ni] = (ni < NF / 2) ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NF / 2) * 32;
+      fb_base[ni] = (ni < NF / 2) ? wn * (WN / 2) + ni * 32
+                                  : BN / 2 + wn * (WN / 2) + (ni - NF / 2) * 32;
     else
       fb_base[ni] = wn * WN + ni * 32;
   }
-  FragAddr<BM, A_KC, MF> FA;
-  FragAddr<BN, B_KC, NF> FB;
-  frag_addr<BM, A_KC, MF>(FA, fa_base, lane);
-  frag_addr<BN, B_KC, NF>(FB, fb_base, lane);
+  FragAddr<BM, BK, A_KC, MF> FA;
+  FragAddr<BN, BK, B_KC, NF> FB;
+  frag_addr<BM, BK, A_KC, MF>(FA, fa_base, lane);
+  frag_addr<BN, BK, B_KC, NF>(FB, fb_base, lane);
 
   f32x16 acc[MF][NF];
 #pragma unroll
@@ -490,29 +564,66 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  if (nk > 0) issue(0);
-  if (nk > 1) issue(1);
-  for (int it = 0; it < nk; ++it) {
-    if (it + 1 < nk && dma_stage(it + 1))
-      wait_vmcnt<NIA + NIB>();
-    else
-      wait_vmcnt<0>();
-    barrier_lds();
-    if (it + 2 < nk) issue(it + 2);
-    const char* sa = smem + (it % kStages) * ST;
-    const char* sb = sa + A_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nk) issue(s);
+  for (int it = 0; it < nk; ++it) {
+    // stage `it` must have landed; the DMA-only stages after it may stay in flight
+    {
+      int ahead = min(NST - 2, nk - 1 - it);
+      for (int s = 1; s <= ahead; ++s)
+        if (!dma_stage(it + s)) ahead = 0;
+      constexpr int PER = GA::MINW + GB::MINW;
+      switch (ahead) {
+        case 1: wait_vmcnt<PER>(); break;
+        case 2: wait_vmcnt<2 * PER>(); break;
+        case 3: wait_vmcnt<3 * PER>(); break;
+        case 4: wait_vmcnt<4 * PER>(); break;
+        default: wait_vmcnt<0>(); break;
+      }
+    }
+    barrier_lds();
+    // Stage it+NST-1 is refilled while stage `it` is multiplied: its DMA
+    // instructions are spread over the k-steps so that load issue overlaps the
+    // MFMAs instead of stalling in-order issue in one burst.
+    const int jn = it + NST - 1;
+    const bool refill = jn < nk;
+    const bool refill_dma = refill && dma_stage(jn);
+    if (refill && !refill_dma) issue(jn);  // element-wise fill (rare shapes)
+    const bool segn1 = jn >= nk0;
+    const int k0n = (segn1 ? jn - nk0 : jn) * BK;
+    const Plan<BM, BK, A_KC> PA = segn1 ? pa1 : pa0;
+    const Plan<BN, BK, B_KC> PB = segn1 ? pb1 : pb0;
+    char* san = smem + (jn % NST) * ST;
+    char* sbn = san + A_BYTES;
+    const char* sa = smem + (it % NST) * ST;
+    const char* sb = sa + A_BYTES;
+    constexpr int KS = BK / 16;
+    constexpr int NT = GA::NIW + GB::NIW;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (refill_dma) {
+#pragma unroll
+        for (int t = ks * NT / KS; t < (ks + 1) * NT / KS; ++t) {
+          if (t < GA::NIW)
+            fill_one<BM, BK, A_KC>(PA, k0n, san, wave, lane, t);
+          else
+            fill_one<BN, BK, B_KC>(PB, k0n, sbn, wave, lane, t - GA::NIW);
+        }
+      }
       bf16x8 af[MF], bf[NF];
 #pragma unroll
-      for (int mi = 0; mi < MF; ++mi) af[mi] = read_frag<BM, A_KC, MF>(sa, FA, mi, fa_base[mi], ks);
+      for (int mi = 0; mi < MF; ++mi)
+        af[mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks);
 #pragma unroll
-      for (int ni = 0; ni < NF; ++ni) bf[ni] = read_frag<BN, B_KC, NF>(sb, FB, ni, fb_base[ni], ks);
+      for (int ni = 0; ni < NF; ++ni)
+        bf[ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], ks);
 #pragma unroll
       for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NF; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ni], af[mi], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ni], af[mi], acc[mi][ni], 0, 0, 0);
     }
   }
 
@@ -743,6 +854,35 @@ hipError_t launch(K kern, int grid, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Tile variants of the four expert GEMMs (128 x 256 tiles, four waves), chosen
+// by measurement on MI355X (variant 1 is the default; MOE_LORA_GEMM_VARIANT
+// overrides it for tuning runs):
+//   0: BK 64, 3 LDS stages (144 KB), one block per CU
+//   1: BK 32, 3 LDS stages (72 KB), two blocks per CU
+//   2: BK 32, 4 LDS stages (96 KB), one block per CU
+//   3: BK 32, 6 LDS stages (144 KB), one block per CU
+int big_variant() {
+  static int v = [] {
+    const char* e = getenv("MOE_LORA_GEMM_VARIANT");
+    return e ? atoi(e) : 1;
+  }();
+  return v;
+}
+
+template <int MODE, int EPI, bool PAIRED, bool A_KC, bool B_KC>
+hipError_t launch_big(int grid, const GemmArgs& a, hipStream_t s) {
+  switch (big_variant()) {
+    case 0:
+      return launch(gemm_bf16<128, 256, 64, 128, 64, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
+    case 2:
+      return launch(gemm_bf16<128, 256, 64, 128, 32, 4, 1, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
+    case 3:
+      return launch(gemm_bf16<128, 256, 64, 128, 32, 6, 1, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
+    default:
+      return launch(gemm_bf16<128, 256, 64, 128, 32, 3, 2, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
+  }
+}
+
 // M-tile grid bound for GROUP_M launches (excess blocks exit at once).
 inline int gm_grid(const ExpertDims& d, int ntn) {
   return static_cast<int>(tile_cap(d.N, d.E, tile_rows(d.dtype)) * ntn);
@@ -779,15 +919,15 @@ hipError_t side_product(const ExpertDims& d, const int32_t* offsets, const WsLay
     a.ntn = 1;
     if (l_kcontig) {
       if (d.r <= 32)
-        return launch(gemm_bf16<128, 32, 32, 32, GROUP_M, EPI_STORE, false, true, true>,
+        return launch(gemm_bf16<128, 32, 32, 32, 64, 3, 2, GROUP_M, EPI_STORE, false, true, true>,
                       gm_grid(d, 1), a, s);
-      return launch(gemm_bf16<128, 64, 32, 64, GROUP_M, EPI_STORE, false, true, true>,
+      return launch(gemm_bf16<128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE, false, true, true>,
                     gm_grid(d, 1), a, s);
     }
     if (d.r <= 32)
-      return launch(gemm_bf16<128, 32, 32, 32, GROUP_M, EPI_STORE, false, true, false>,
+      return launch(gemm_bf16<128, 32, 32, 32, 64, 3, 2, GROUP_M, EPI_STORE, false, true, false>,
                     gm_grid(d, 1), a, s);
-    return launch(gemm_bf16<128, 64, 32, 64, GROUP_M, EPI_STORE, false, true, false>,
+    return launch(gemm_bf16<128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE, false, true, false>,
                   gm_grid(d, 1), a, s);
   }
   a.ntn = ceil_div(d.r, 64);
@@ -815,19 +955,19 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
       a.ntn = 1;
       if (Q <= 32) {
         a.ntm = ceil_div(P, 256);
-        return launch(gemm_bf16<256, 32, 64, 32, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm, a, s);
+        return launch(gemm_bf16<256, 32, 64, 32, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm, a, s);
       }
       a.ntm = ceil_div(P, 256);
-      return launch(gemm_bf16<256, 64, 64, 64, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm, a, s);
+      return launch(gemm_bf16<256, 64, 64, 64, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm, a, s);
     }
     // [r, big] (or both small)
     a.ntn = ceil_div(Q, 256);
     if (P <= 32) {
       a.ntm = 1;
-      return launch(gemm_bf16<32, 256, 32, 64, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntn, a, s);
+      return launch(gemm_bf16<32, 256, 32, 64, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntn, a, s);
     }
     a.ntm = ceil_div(P, 64);
-    return launch(gemm_bf16<64, 256, 64, 64, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm * a.ntn, a,
+    return launch(gemm_bf16<64, 256, 64, 64, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm * a.ntn, a,
                   s);
   }
   a.ntm = ceil_div(P, 64);
@@ -885,8 +1025,8 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
     TimedScope ts(tm, MOE_K_GATE_UP_FWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(I, 128);
-      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_SWIGLU, true, true, true>, gm_grid(d, a.ntn),
-                     a, s));
+      MOE_TRY((launch_big<GROUP_M, EPI_SWIGLU, true, true, true>( gm_grid(d, a.ntn),
+                     a, s)));
     } else {
       a.ntn = ceil_div(I, 64);
       MOE_TRY(launch(gemm_f32<GROUP_M, EPI_SWIGLU, true>, gm_grid(d, a.ntn), a, s));
@@ -911,8 +1051,8 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
     TimedScope ts(tm, MOE_K_DOWN_FWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(H, 256);
-      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_STORE, false, true, true>, gm_grid(d, a.ntn),
-                     a, s));
+      MOE_TRY((launch_big<GROUP_M, EPI_STORE, false, true, true>( gm_grid(d, a.ntn),
+                     a, s)));
     } else {
       a.ntn = ceil_div(H, 64);
       MOE_TRY(launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, a.ntn), a, s));
@@ -959,8 +1099,8 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     TimedScope ts(tm, MOE_K_DOWN_BWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(I, 256);
-      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_SWIGLU_BWD, false, true, false>,
-                     gm_grid(d, a.ntn), a, s));
+      MOE_TRY((launch_big<GROUP_M, EPI_SWIGLU_BWD, false, true, false>(
+                     gm_grid(d, a.ntn), a, s)));
     } else {
       a.ntn = ceil_div(I, 64);
       MOE_TRY(launch(gemm_f32<GROUP_M, EPI_SWIGLU_BWD, false>, gm_grid(d, a.ntn), a, s));
@@ -990,8 +1130,8 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     TimedScope ts(tm, MOE_K_GATE_UP_BWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(H, 256);
-      MOE_TRY(launch(gemm_bf16<128, 256, 64, 128, GROUP_M, EPI_STORE, false, true, false>, gm_grid(d, a.ntn),
-                     a, s));
+      MOE_TRY((launch_big<GROUP_M, EPI_STORE, false, true, false>( gm_grid(d, a.ntn),
+                     a, s)));
     } else {
       a.ntn = ceil_div(H, 64);
       MOE_TRY(launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, a.ntn), a, s));
