@@ -244,8 +244,13 @@ class kernel_timer:
         check(_lib.load().moe_kernel_timer_reset(), "moe_kernel_timer_reset")
 
 
-# Load at import: a missing library is an error, never a silent fallback.
-_lib.load()
+# Load at import when the library is built; if it is not (for instance while
+# `python -m mixture_experts_lora_amd.build` runs), every entry point raises
+# on first use: there is no fallback implementation.
+try:
+    _lib.load()
+except RuntimeError:
+    pass
 
 from .layer import MoELoRALayer, MoELoRAFunction  # noqa: E402
 

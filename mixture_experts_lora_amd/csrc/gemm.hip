@@ -274,6 +274,7 @@ template <int ROWS, int BK, bool KC>
 struct Plan {
   const void* base;
   int nrec;
+  u32x4 rs;  // buffer resource over [base, base + nrec)
   uint32_t vo[Geo<ROWS, BK, KC>::NIW];
   int vec;
   int klim;
@@ -291,6 +292,7 @@ __device__ __forceinline__ void make_plan(Plan<ROWS, BK, KC>& P, const View<bf16
   P.ld = v.ld;
   P.base = v.base;
   P.nrec = clamp_records(bytes);
+  P.rs = buffer_rsrc(v.base, P.nrec);
 #pragma unroll
   for (int i = 0; i < G::NIW; ++i) {
     const int j = wave + 4 * i;  // instruction index within the tile
@@ -319,7 +321,7 @@ __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC>& P, int k0, char* 
     const uint32_t soff = KC ? static_cast<uint32_t>(k0) * 2
                              : static_cast<uint32_t>(static_cast<int64_t>(k0) * P.ld * 2);
     const bool tail = KC && (k0 + BK > P.klim);  // n-contiguous tails hit the buffer bound
-    const u32x4 rs = buffer_rsrc(P.base, P.nrec);
+    const u32x4 rs = P.rs;
 #pragma unroll
     for (int i = 0; i < G::NIW; ++i) {
       const int j = wave + 4 * i;
@@ -367,7 +369,7 @@ __device__ __forceinline__ void fill_one(const Plan<ROWS, BK, KC>& P, int k0, ch
     const int c = (lane % G::CPR) ^ kswz<BK>(r);
     if (k0 + c * 8 >= P.klim) vo = kOOB;
   }
-  dma16(lds + j * 1024, buffer_rsrc(P.base, P.nrec), vo, soff);
+  dma16(lds + j * 1024, P.rs, vo, soff);
 }
 
 // Per-lane LDS byte offsets of the MFMA fragments.
@@ -424,7 +426,10 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
   static_assert(NST >= 3 && NST <= 6 && (NST - 2) * (GA::MINW + GB::MINW) <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[NST * ST];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a wave-uniform (scalar) value, so that everything derived
+  // from it (DMA destinations, resources) stays in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
   int e, n_tile, rows, m0 = 0, krows = 0;
@@ -600,8 +605,24 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
     const char* sb = sa + A_BYTES;
     constexpr int KS = BK / 16;
     constexpr int NT = GA::NIW + GB::NIW;
+    // Fragments are double-buffered in registers: the LDS reads of k-step
+    // ks+1 are in flight while the MFMAs of k-step ks run.
+    bf16x8 af[2][MF], bf[2][NF];
+#pragma unroll
+    for (int mi = 0; mi < MF; ++mi) af[0][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], 0);
+#pragma unroll
+    for (int ni = 0; ni < NF; ++ni) bf[0][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int mi = 0; mi < MF; ++mi)
+          af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
+#pragma unroll
+        for (int ni = 0; ni < NF; ++ni)
+          bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], ks + 1);
+      }
       if (refill_dma) {
 #pragma unroll
         for (int t = ks * NT / KS; t < (ks + 1) * NT / KS; ++t) {
@@ -611,19 +632,12 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
             fill_one<BN, BK, B_KC>(PB, k0n, sbn, wave, lane, t - GA::NIW);
         }
       }
-      bf16x8 af[MF], bf[NF];
-#pragma unroll
-      for (int mi = 0; mi < MF; ++mi)
-        af[mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks);
-#pragma unroll
-      for (int ni = 0; ni < NF; ++ni)
-        bf[ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], ks);
 #pragma unroll
       for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NF; ++ni)
-          acc[mi][ni] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ni], af[mi], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][ni], af[cur][mi],
+                                                                acc[mi][ni], 0, 0, 0);
     }
   }
 

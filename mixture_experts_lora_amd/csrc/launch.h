@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/moe_lora.h"
+#include "moe_lora.h"  // include/ is on the compiler include path
 
 namespace moe {
 
