@@ -413,6 +413,66 @@ __device__ __forceinline__ bf16x8 read_frag(const char* tile,
   }
 }
 
+// ---- epilogue staging helpers
+// A wave's float32 slab is 32 rows x WN columns; row r keeps 16-byte chunk c
+// at c ^ sswz(r), so that 16 lanes writing one chunk column of 16 rows, or
+// reading 16 row segments, hit distinct LDS banks.
+template <int WN>
+__device__ __forceinline__ int slab_off(int r, int c) {
+  const int sw = WN >= 64 ? (r & 15) : ((r >> 1) & 7);
+  return r * WN * 4 + ((c ^ sw) << 4);
+}
+
+// Eight floats: chunks c and c+1 of row r.
+template <int WN>
+__device__ __forceinline__ void read8(const char* slab, int r, int c, float (&v)[8]) {
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(slab + slab_off<WN>(r, c));
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(slab + slab_off<WN>(r, c + 1));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = lo[j];
+    v[4 + j] = hi[j];
+  }
+}
+
+// Columns 8s..8s+7 of row r. Lanes of the upper half of a row read their odd
+// chunk first, so that 16 lanes of either read touch 16 distinct 16-byte bank groups.
+template <int WN>
+__device__ __forceinline__ void read8_interleaved(const char* slab, int r, int s, float (&v)[8]) {
+  const int odd = s >= WN / 16 ? 1 : 0;
+  const f32x4 x = *reinterpret_cast<const f32x4*>(slab + slab_off<WN>(r, 2 * s + odd));
+  const f32x4 y = *reinterpret_cast<const f32x4*>(slab + slab_off<WN>(r, 2 * s + (odd ^ 1)));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = odd ? y[j] : x[j];
+    v[4 + j] = odd ? x[j] : y[j];
+  }
+}
+
+// Eight consecutive bf16 as one 16-byte global access (16-byte aligned).
+__device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
+  const uint4 r = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(w[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = static_cast<uint32_t>(f32_to_bf16(v[2 * j])) |
+           (static_cast<uint32_t>(f32_to_bf16(v[2 * j + 1])) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// LDS writes of this wave are complete (and not reordered by the compiler)
+// before its lanes read what other lanes wrote.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 template <int BM, int BN, int WM, int WN, int BK, int NST, int MINB, int MODE, int EPI,
           bool PAIRED, bool A_KC, bool B_KC>
 __global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
@@ -641,40 +701,96 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
     }
   }
 
-  // Lane holds, for MFMA tile (mi, ni), row m = wm*WM + mi*32 + lane%32 and the
-  // columns 8*(v/4) + 4*(lane/32) + v%4 of the tile's 32 weight rows.
-  const int m_lane = wm * WM + (lane & 31);
-  const int c_lane = 4 * (lane >> 5);
-  if (PAIRED) {
+  // ---- Epilogue, staged through LDS. After the final wait no DMA is in
+  // flight, so once every wave is past its last fragment read the whole ring
+  // is free. Each wave then stages one 32-row slab of its accumulators at a
+  // time as float32 and writes the outputs back as whole 16-byte row segments
+  // (8 consecutive bf16), which keeps global stores, and the h loads of the
+  // SwiGLU backward, coalesced along rows.
+  // Accumulator layout: lane holds, for MFMA tile (mi, ni), row lane%32 of the
+  // 32-row slab mi and the columns 8*(v/4) + 4*(lane/32) + v%4 of fragment ni.
+  __syncthreads();
+  constexpr int SLAB = 32 * WN * 4;
+  static_assert(4 * SLAB <= NST * ST, "epilogue slab does not fit in the LDS ring");
+  char* slab = smem + wave * SLAB;
+  const int srow = lane & 31, shalf = lane >> 5;
+  const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0 && (p.ld_out & 7) == 0 &&
+                       (p.out_estride & 7) == 0;
 #pragma unroll
-    for (int mi = 0; mi < MF; ++mi)
+  for (int mi = 0; mi < MF; ++mi) {
+    if (mi) wave_lds_sync();  // previous slab fully read
 #pragma unroll
-      for (int ni = 0; ni < NF / 2; ++ni)
+    for (int ni = 0; ni < NF; ++ni)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float g[4], u[4];
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            g[j] = acc[mi][ni][4 * q + j];
-            u[j] = acc[mi][ni + NF / 2][4 * q + j];
+        for (int j = 0; j < 4; ++j) v[j] = acc[mi][ni][4 * q + j];
+        *reinterpret_cast<f32x4*>(slab + slab_off<WN>(srow, ni * 8 + 2 * q + shalf)) = v;
+      }
+    wave_lds_sync();
+    const int mbase = wm * WM + mi * 32;  // first tile row of this slab
+    if (PAIRED) {
+      // slab columns [0, WN/2) are gate features, [WN/2, WN) the matching up features
+      constexpr int SEGS = WN / 16, RPP = 64 / SEGS;
+#pragma unroll
+      for (int pass = 0; pass < 32 / RPP; ++pass) {
+        const int r = pass * RPP + lane / SEGS, s = lane % SEGS;
+        const int m_local = mbase + r;
+        const int f = n_tile * (BN / 2) + wn * (WN / 2) + 8 * s;
+        float g[8], u[8], a[8];
+        read8<WN>(slab, r, 2 * s, g);
+        read8<WN>(slab, r, WN / 8 + 2 * s, u);
+        if (m_local < rows && f < p.I) {  // I is a multiple of 8
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a[j] = swiglu(g[j], u[j]);
+          const int64_t row = row0 + m_local;
+          bf16_t* hr = static_cast<bf16_t*>(p.out) + row * p.ld_out;
+          store8(hr + f, g);
+          store8(hr + p.I + f, u);
+          store8(static_cast<bf16_t*>(p.out2) + row * p.ld_out2 + f, a);
+        }
+      }
+    } else {
+      constexpr int SEGS = WN / 8, RPP = 64 / SEGS;
+#pragma unroll
+      for (int pass = 0; pass < 32 / RPP; ++pass) {
+        const int r = pass * RPP + lane / SEGS, s = lane % SEGS;
+        const int m_local = mbase + r;
+        const int col = n0 + wn * WN + 8 * s;
+        float v[8];
+        read8_interleaved<WN>(slab, r, s, v);
+        if (m_local >= rows) continue;
+        if (MODE == GROUP_M && EPI == EPI_SWIGLU_BWD) {
+          if (col >= p.N) continue;  // N = I, a multiple of 8
+          const int64_t row = row0 + m_local;
+          const bf16_t* hr = static_cast<const bf16_t*>(p.aux) + row * p.ld_aux;
+          float g[8], u[8], dg[8], du[8];
+          load8(hr + col, g);
+          load8(hr + p.I + col, u);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) swiglu_bwd(g[j], u[j], v[j], dg[j], du[j]);
+          bf16_t* dr = static_cast<bf16_t*>(p.out) + row * p.ld_out;
+          store8(dr + col, dg);
+          store8(dr + p.I + col, du);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] *= p.scale;
+          // GROUP_M: an expert's row; GROUP_K: feature row m0 + m_local of expert e's gradient
+          bf16_t* rp = MODE == GROUP_M
+                           ? static_cast<bf16_t*>(p.out) + (row0 + m_local) * p.ld_out
+                           : static_cast<bf16_t*>(p.out) + static_cast<int64_t>(e) * p.out_estride +
+                                 static_cast<int64_t>(m0 + m_local) * p.ld_out;
+          if (out_vec && col + 8 <= p.N) {
+            store8(rp + col, v);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (col + j < p.N) rp[col + j] = f32_to_bf16(v[j]);
           }
-          const int f = n_tile * (BN / 2) + wn * (WN / 2) + ni * 32 + 8 * q + c_lane;
-          epi_swiglu<bf16_t>(p, row0, m_lane + mi * 32, rows, f, g, u);
         }
-  } else {
-    const int64_t rbase = MODE == GROUP_M ? row0 : static_cast<int64_t>(m0);
-#pragma unroll
-    for (int mi = 0; mi < MF; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NF; ++ni)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float v[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = acc[mi][ni][4 * q + j];
-          const int col = n0 + wn * WN + ni * 32 + 8 * q + c_lane;
-          epi_store<bf16_t, MODE, EPI>(p, e, rbase, m_lane + mi * 32, rows, col, v);
-        }
+      }
+    }
   }
 }
 
