@@ -16,6 +16,8 @@ roofline = the dominant GEMM kernel's algorithmic FLOPs per launch over its
            by the library's kernel timer, against the dense bf16 MFMA peak.
 cpu_baseline = the CPU oracle (NumPy float32 per-expert loop) on a bounded
            sample of the same workload, on the host's cores.
+hbm      = the memory-bound kernels' algorithmic bytes per launch over their
+           mean launch time, against the 8 TB/s HBM3E peak.
 """
 from __future__ import annotations
 
@@ -49,6 +51,21 @@ def kernel_flops(name, cfg):
     }[name]
 
 
+def kernel_bytes(name, cfg):
+    """Algorithmic HBM bytes of one launch of a memory-bound kernel (each tensor once)."""
+    T, H, E, k, N = cfg.T, cfg.H, cfg.E, cfg.k, cfg.N
+    es = 2 if cfg.dtype == "bf16" else 4
+    return {
+        "route": T * E * 4 + T * k * 8,                        # logits in; ids, weights out
+        "permute": N * 4 * 3 + (2 * E + 1) * 4,                # ids in; sorted_pair, inv_pos, counts
+        "gather": T * H * es + N * H * es + N * 4,            # x in, X_perm out, sorted_pair
+        "combine": N * H * es + T * H * es + N * 8,           # Yexp in, Y out, inv_pos + weights
+        "combine_bwd": T * H * es + 2 * N * H * es + N * 12,  # dY, Yexp in; G out; idx, w, dw
+        "route_bwd": 2 * T * E * 4 + T * k * 8,                # logits in, dlogits out; ids, dw
+        "unpermute": N * H * es + T * H * es + N * 4,         # dX_perm in, dX out, inv_pos
+    }.get(name)
+
+
 def source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_lora_amd", "csrc")
@@ -69,6 +86,62 @@ def traffic_for(kernel, workload):
     return d.get("hbm_bytes_per_launch")
 
 
+def classify_gemm(kernel_name):
+    """Map a profiler kernel name of the bf16 grouped GEMM to the step it runs."""
+    import re
+    m = re.search(r"gemm_bf16<([^>]*)>", kernel_name)
+    if not m:
+        return None
+    a = [x.strip() for x in m.group(1).split(",")]
+    bm, bn, mode, epi, b_kc = int(a[0]), int(a[1]), int(a[7]), int(a[8]), a[11] == "true"
+    if mode != 0 or bn < 128:
+        return None  # LoRA side products and weight gradients
+    if epi == 1:
+        return "gate_up_fwd"
+    if epi == 2:
+        return "down_bwd"
+    return "down_fwd" if b_kc else "gate_up_bwd"
+
+
+def write_traffic(d, workload):
+    """profiles/traffic_<kernel>_<workload>.json from rocprofv3 --pmc runs under d:
+    d/fetch and d/write (FETCH_SIZE, WRITE_SIZE of a bench run), d/calib_fetch and
+    d/calib_write (the same counters over one device copy of --calib-copy MiB)."""
+    import csv
+    from collections import defaultdict
+
+    def per_dispatch(sub, counter, pick):
+        tot, ids = defaultdict(float), defaultdict(set)
+        with open(os.path.join(d, sub, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                k = pick(r["Kernel_Name"])
+                if k and r["Counter_Name"] == counter:
+                    tot[k] += float(r["Counter_Value"])
+                    ids[k].add(r["Dispatch_Id"])
+        return {k: (tot[k] / len(ids[k]), len(ids[k])) for k in tot}
+
+    copy = lambda n: "copyBuffer" if "copyBuffer" in n else None  # noqa: E731
+    calib = json.load(open(os.path.join(d, "calib.json")))
+    cf = calib["read_bytes"] / (per_dispatch("calib_fetch", "FETCH_SIZE", copy)["copyBuffer"][0] * 1024)
+    cw = calib["write_bytes"] / (per_dispatch("calib_write", "WRITE_SIZE", copy)["copyBuffer"][0] * 1024)
+    fetch = per_dispatch("fetch", "FETCH_SIZE", classify_gemm)
+    write = per_dispatch("write", "WRITE_SIZE", classify_gemm)
+    if calib.get("source_hash") != source_hash():
+        raise SystemExit("counter runs were taken on other kernel sources than these")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for k in sorted(fetch):
+        rec = {"kernel": k, "workload": workload, "source_hash": source_hash(),
+               "fetch_kib_per_dispatch": round(fetch[k][0], 1),
+               "write_kib_per_dispatch": round(write[k][0], 1), "dispatches": fetch[k][1],
+               "calib_fetch_factor": round(cf, 4), "calib_write_factor": round(cw, 4),
+               "hbm_read_bytes_per_launch": int(fetch[k][0] * 1024 * cf),
+               "hbm_write_bytes_per_launch": int(write[k][0] * 1024 * cw)}
+        rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+        with open(os.path.join(ROOT, "profiles", f"traffic_{k}_{workload}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+
+
 def cpu_baseline(cfg, inp, sample_tokens):
     import numpy as np
     import oracle
@@ -83,6 +156,9 @@ def cpu_baseline(cfg, inp, sample_tokens):
     S = slice(0, Ts)
     h = {n: to_numpy(inp[n]) for n in ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")}
     x, lg, dy = to_numpy(inp["x"][S]), to_numpy(inp["logits"][S]), to_numpy(inp["dy"][S])
+    w = min(256, Ts)  # warm-up on a few tokens (BLAS threads, page faults)
+    oracle.layer_forward_backward(x[:w], lg[:w], dy[:w], h, cfg.k, cfg.router, cfg.lora_scale,
+                                  np.float32)
     t0 = time.perf_counter()
     oracle.layer_forward_backward(x, lg, dy, h, cfg.k, cfg.router, cfg.lora_scale, np.float32)
     dt = time.perf_counter() - t0
@@ -107,7 +183,13 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB mebibytes device-to-device once (HBM counter calibration)")
+    ap.add_argument("--write-traffic", metavar="DIR", default=None,
+                    help="only write profiles/traffic_*.json from rocprofv3 counter runs in DIR")
     args = ap.parse_args()
+    if args.write_traffic:
+        from workloads import BENCH_CONFIG
+        write_traffic(args.write_traffic, args.config or BENCH_CONFIG)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer is benchmarked on a single MI355X "
               "(run with --gpus 1).", file=sys.stderr)
@@ -121,7 +203,8 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"calib_copy_bytes": n, "read_bytes": n, "write_bytes": n}))
+        print(json.dumps({"calib_copy_bytes": n, "read_bytes": n, "write_bytes": n,
+                          "source_hash": source_hash()}))
         return
     import mixture_experts_lora_amd as mel
     from workloads import BENCH_CONFIG, get_config, make_inputs
@@ -138,15 +221,29 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: K steps, kernel timer live (HIP events on the launch stream)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     with mel.kernel_timer() as kt:
         torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
+        ev[0].record()
+        for i in range(args.steps):
             layer.step(inp["x"], inp["logits"], inp["dy"], weights)
-        stop.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+
+    # forward-only and backward-only, after the timed region
+    def timed(fn, n=5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+    fwd_ms = timed(lambda: layer.forward(inp["x"], inp["logits"], weights))
+    bwd_ms = timed(lambda: layer.backward(inp["dy"], inp["logits"], weights))
     kms = {}
     for name in mel._lib.KERNEL_IDS:
         tot, n = kt.read(name)
@@ -166,9 +263,18 @@ def main():
                 "peak": peak, "unit": "TFLOP/s", "frac": round(dom_tf / peak, 4),
                 "traffic": traffic_for(dom, cfg.name),
                 "flops_per_launch": kernel_flops(dom, cfg), "ms_per_launch": dom_ms}
+    hbm = {}
+    for name, kv in kms.items():
+        nb = kernel_bytes(name, cfg)
+        if nb:
+            gbs = nb / (kv["ms_per_launch"] / 1e3) / 1e9
+            hbm[name] = {"bytes_per_launch": nb, "GB/s": round(gbs, 1),
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)}
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_median": round(step_ms[len(step_ms) // 2], 4), "ms_min": round(step_ms[0], 4),
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
         "config": {"workload": f"{cfg.name}-shaped MoE-LoRA expert layer fwd+bwd",
@@ -179,6 +285,7 @@ def main():
         "flops_per_step": F,
         "peak_hbm_bytes": int(peak_bytes),
         "roofline": roofline,
+        "hbm": hbm,
         "kernels": kms,
     }
     if not args.no_cpu:
