@@ -171,6 +171,21 @@ def test_gather_then_unpermute_is_identity_for_k1():
     assert (back == x).all()
 
 
+def test_gather_rows_are_the_routed_tokens():
+    # Distinct token rows identify tokens: expert e's rows are exactly the
+    # tokens that chose e, in token order, and every token appears k times.
+    rng = np.random.default_rng(5)
+    T, E, k, H = 40, 6, 3, 4
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = rng.normal(size=(T, H))
+    _, off, sp, _ = oracle.permute(ids, E)
+    xp = oracle.gather_rows(x, sp, k)
+    tok = [int(np.flatnonzero((x == row).all(axis=1))[0]) for row in xp]
+    for e in range(E):
+        assert tok[off[e]:off[e + 1]] == [t for t in range(T) if e in ids[t]]
+    assert np.bincount(tok, minlength=T).tolist() == [k] * T
+
+
 def test_combine_one_hot_selects_expert_output():
     rng = np.random.default_rng(6)
     T, k, H = 20, 3, 4
