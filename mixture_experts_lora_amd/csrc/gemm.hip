@@ -259,33 +259,34 @@ __device__ __forceinline__ int clamp_records(int64_t bytes) {
   return bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes));
 }
 
-// DMA geometry of one operand tile of ROWS rows (or columns) x BK.
-template <int ROWS, int BK, bool KC>
+// Fill geometry of one operand tile of ROWS rows (or columns) x BK, filled
+// by NW waves in 1 KB wave instructions (16 bytes per lane).
+template <int ROWS, int BK, bool KC, int NW>
 struct Geo {
   static constexpr int TI = ROWS * BK * 2 / 1024;  // 1 KB instructions per tile
-  static constexpr int NIW = (TI + 3) / 4;         // per wave (upper bound)
-  static constexpr int MINW = TI / 4;              // issued by every wave
+  static constexpr int NIW = (TI + NW - 1) / NW;   // per wave (upper bound)
+  static constexpr int MINW = TI / NW;             // issued by every wave
   static constexpr int CPR = KC ? BK / 8 : ROWS / 8;        // chunks per LDS row
   static constexpr int RPI = KC ? 512 / BK : 512 / ROWS;    // LDS rows per instruction
 };
 
 // DMA plan of one operand tile: buffer (base, bytes), per-instruction lane offsets.
-template <int ROWS, int BK, bool KC>
+template <int ROWS, int BK, bool KC, int NW>
 struct Plan {
   const void* base;
   int nrec;
   u32x4 rs;  // buffer resource over [base, base + nrec)
-  uint32_t vo[Geo<ROWS, BK, KC>::NIW];
+  uint32_t vo[Geo<ROWS, BK, KC, NW>::NIW];
   int vec;
   int klim;
   int64_t ld;
   View<bf16_t> view;  // element view for the slow (non-DMA) fill
 };
 
-template <int ROWS, int BK, bool KC>
-__device__ __forceinline__ void make_plan(Plan<ROWS, BK, KC>& P, const View<bf16_t>& v,
+template <int ROWS, int BK, bool KC, int NW>
+__device__ __forceinline__ void make_plan(Plan<ROWS, BK, KC, NW>& P, const View<bf16_t>& v,
                                           int64_t bytes, int vec, int wave, int lane) {
-  typedef Geo<ROWS, BK, KC> G;
+  typedef Geo<ROWS, BK, KC, NW> G;
   P.view = v;
   P.vec = vec;
   P.klim = v.klim;
@@ -295,7 +296,7 @@ __device__ __forceinline__ void make_plan(Plan<ROWS, BK, KC>& P, const View<bf16
   P.rs = buffer_rsrc(v.base, P.nrec);
 #pragma unroll
   for (int i = 0; i < G::NIW; ++i) {
-    const int j = wave + 4 * i;  // instruction index within the tile
+    const int j = wave + NW * i;  // instruction index within the tile
     const int r = G::RPI * j + lane / G::CPR;
     const int p = lane % G::CPR;
     uint32_t vo = kOOB;
@@ -313,10 +314,10 @@ __device__ __forceinline__ void make_plan(Plan<ROWS, BK, KC>& P, const View<bf16
 }
 
 // Issue one tile: DMA when possible, else an element-wise fill.
-template <int ROWS, int BK, bool KC>
-__device__ __forceinline__ void fill(const Plan<ROWS, BK, KC>& P, int k0, char* lds, int wave,
+template <int ROWS, int BK, bool KC, int NW>
+__device__ __forceinline__ void fill(const Plan<ROWS, BK, KC, NW>& P, int k0, char* lds, int wave,
                                      int lane) {
-  typedef Geo<ROWS, BK, KC> G;
+  typedef Geo<ROWS, BK, KC, NW> G;
   if (P.vec) {
     const uint32_t soff = KC ? static_cast<uint32_t>(k0) * 2
                              : static_cast<uint32_t>(static_cast<int64_t>(k0) * P.ld * 2);
@@ -324,8 +325,8 @@ __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC>& P, int k0, char* 
     const u32x4 rs = P.rs;
 #pragma unroll
     for (int i = 0; i < G::NIW; ++i) {
-      const int j = wave + 4 * i;
-      if (G::TI % 4 == 0 || j < G::TI) {
+      const int j = wave + NW * i;
+      if (G::TI % NW == 0 || j < G::TI) {
         uint32_t vo = P.vo[i];
         if (tail) {
           const int r = G::RPI * j + lane / G::CPR;
@@ -337,7 +338,7 @@ __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC>& P, int k0, char* 
     }
   } else {
     bf16_t* t = reinterpret_cast<bf16_t*>(lds);
-    for (int e = threadIdx.x; e < ROWS * BK; e += 256) {
+    for (int e = threadIdx.x; e < ROWS * BK; e += 64 * NW) {
       int byte;
       bf16_t val;
       if (KC) {
@@ -355,12 +356,12 @@ __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC>& P, int k0, char* 
 }
 
 // One DMA instruction (index i of this wave's share) of a tile; DMA plans only.
-template <int ROWS, int BK, bool KC>
-__device__ __forceinline__ void fill_one(const Plan<ROWS, BK, KC>& P, int k0, char* lds,
+template <int ROWS, int BK, bool KC, int NW>
+__device__ __forceinline__ void fill_one(const Plan<ROWS, BK, KC, NW>& P, int k0, char* lds,
                                          int wave, int lane, int i) {
-  typedef Geo<ROWS, BK, KC> G;
-  const int j = wave + 4 * i;
-  if (G::TI % 4 != 0 && j >= G::TI) return;
+  typedef Geo<ROWS, BK, KC, NW> G;
+  const int j = wave + NW * i;
+  if (G::TI % NW != 0 && j >= G::TI) return;
   const uint32_t soff = KC ? static_cast<uint32_t>(k0) * 2
                            : static_cast<uint32_t>(static_cast<int64_t>(k0) * P.ld * 2);
   uint32_t vo = P.vo[i];
@@ -371,6 +372,12 @@ __device__ __forceinline__ void fill_one(const Plan<ROWS, BK, KC>& P, int k0, ch
   }
   dma16(lds + j * 1024, P.rs, vo, soff);
 }
+
+// A fill geometry tagged with its operand's k-contiguity (for generic lambdas).
+template <typename G, bool KC>
+struct GeoK : G {
+  static constexpr bool KCV = KC;
+};
 
 // Per-lane LDS byte offsets of the MFMA fragments.
 template <int ROWS, int BK, bool KC, int NFR>
@@ -474,16 +481,18 @@ __device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int BM, int BN, int WM, int WN, int BK, int NST, int MINB, int MODE, int EPI,
-          bool PAIRED, bool A_KC, bool B_KC>
-__global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
+          bool PAIRED, bool A_KC, bool B_KC, bool VST = false>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(GemmArgs p) {
   constexpr int WAVES_N = BN / WN, MF = WM / 32, NF = WN / 32;
+  constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, ST = A_BYTES + B_BYTES;
-  typedef Geo<BM, BK, A_KC> GA;
-  typedef Geo<BN, BK, B_KC> GB;
-  static_assert((BM / WM) * (BN / WN) == 4, "four waves per block");
+  typedef Geo<BM, BK, A_KC, NW> GA;
+  typedef Geo<BN, BK, B_KC, NW> GB;
+  static_assert(NW == 4 || NW == 8, "four or eight waves per block");
   static_assert(!PAIRED || (NF % 2 == 0), "paired tiles need gate and up fragments");
   static_assert(GA::TI >= 1 && GB::TI >= 1, "tile smaller than one DMA instruction");
-  static_assert(NST >= 3 && NST <= 6 && (NST - 2) * (GA::MINW + GB::MINW) <= 63, "vmcnt range");
+  static_assert(VST || (NST >= 3 && NST <= 6 && (NST - 2) * (GA::MINW + GB::MINW) <= 63),
+                "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[NST * ST];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -531,9 +540,9 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
   // plain variables, never indexed by a runtime value, so they stay in
   // registers: a scratch access would bring an s_waitcnt vmcnt(0) that also
   // drains every tile in flight.
-  Plan<BM, BK, A_KC> pa0, pa1;
-  Plan<BN, BK, B_KC> pb0, pb1;
-  auto build = [&](int seg, Plan<BM, BK, A_KC>& PA, Plan<BN, BK, B_KC>& PB) {
+  Plan<BM, BK, A_KC, NW> pa0, pa1;
+  Plan<BN, BK, B_KC, NW> pb0, pb1;
+  auto build = [&](int seg, Plan<BM, BK, A_KC, NW>& PA, Plan<BN, BK, B_KC, NW>& PB) {
     const Opnd& A = p.a[seg];
     const Opnd& B = p.b[seg];
     View<bf16_t> va{}, vb{};
@@ -575,8 +584,8 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
       vb.mn_lim = p.N - n0;
       bbytes = static_cast<int64_t>(krows) * B.ld * 2 - static_cast<int64_t>(n0) * 2;
     }
-    make_plan<BM, BK, A_KC>(PA, va, abytes, A.vec, wave, lane);
-    make_plan<BN, BK, B_KC>(PB, vb, bbytes, B.vec, wave, lane);
+    make_plan<BM, BK, A_KC, NW>(PA, va, abytes, A.vec, wave, lane);
+    make_plan<BN, BK, B_KC, NW>(PB, vb, bbytes, B.vec, wave, lane);
   };
   build(0, pa0, pb0);
   if (MODE == GROUP_M) {
@@ -595,11 +604,11 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
     char* sa = smem + (j % NST) * ST;
     char* sb = sa + A_BYTES;
     if (j < nk0) {
-      fill<BM, BK, A_KC>(pa0, j * BK, sa, wave, lane);
-      fill<BN, BK, B_KC>(pb0, j * BK, sb, wave, lane);
+      fill<BM, BK, A_KC, NW>(pa0, j * BK, sa, wave, lane);
+      fill<BN, BK, B_KC, NW>(pb0, j * BK, sb, wave, lane);
     } else {
-      fill<BM, BK, A_KC>(pa1, (j - nk0) * BK, sa, wave, lane);
-      fill<BN, BK, B_KC>(pb1, (j - nk0) * BK, sb, wave, lane);
+      fill<BM, BK, A_KC, NW>(pa1, (j - nk0) * BK, sa, wave, lane);
+      fill<BN, BK, B_KC, NW>(pb1, (j - nk0) * BK, sb, wave, lane);
     }
   };
   // A stage filled only by DMA leaves at least MINW loads per operand outstanding.
@@ -629,76 +638,197 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < nk) issue(s);
-  for (int it = 0; it < nk; ++it) {
-    // stage `it` must have landed; the DMA-only stages after it may stay in flight
-    {
-      int ahead = min(NST - 2, nk - 1 - it);
-      for (int s = 1; s <= ahead; ++s)
-        if (!dma_stage(it + s)) ahead = 0;
-      constexpr int PER = GA::MINW + GB::MINW;
-      switch (ahead) {
-        case 1: wait_vmcnt<PER>(); break;
-        case 2: wait_vmcnt<2 * PER>(); break;
-        case 3: wait_vmcnt<3 * PER>(); break;
-        case 4: wait_vmcnt<4 * PER>(); break;
-        default: wait_vmcnt<0>(); break;
-      }
-    }
-    barrier_lds();
-    // Stage it+NST-1 is refilled while stage `it` is multiplied: its DMA
-    // instructions are spread over the k-steps so that load issue overlaps the
-    // MFMAs instead of stalling in-order issue in one burst.
-    const int jn = it + NST - 1;
-    const bool refill = jn < nk;
-    const bool refill_dma = refill && dma_stage(jn);
-    if (refill && !refill_dma) issue(jn);  // element-wise fill (rare shapes)
-    const bool segn1 = jn >= nk0;
-    const int k0n = (segn1 ? jn - nk0 : jn) * BK;
-    const Plan<BM, BK, A_KC> PA = segn1 ? pa1 : pa0;
-    const Plan<BN, BK, B_KC> PB = segn1 ? pb1 : pb0;
-    char* san = smem + (jn % NST) * ST;
-    char* sbn = san + A_BYTES;
-    const char* sa = smem + (it % NST) * ST;
-    const char* sb = sa + A_BYTES;
+  if constexpr (VST) {
+    // ---- Register-staged main loop: every wave loads its share of a k tile
+    // into VGPRs (16 bytes per lane per 1 KB piece, the same lane offsets as
+    // the DMA plans, out-of-range lanes read zeros) and writes it to the LDS
+    // slot the tile belongs to. Two LDS slots; tile it+1 is written during
+    // tile it's second k-step (its slot was last read before the previous
+    // barrier), and the load of tile it+2 is issued right after, so each load
+    // has a whole tile of MFMAs to arrive.
     constexpr int KS = BK / 16;
-    constexpr int NT = GA::NIW + GB::NIW;
-    // Fragments are double-buffered in registers: the LDS reads of k-step
-    // ks+1 are in flight while the MFMAs of k-step ks run.
-    bf16x8 af[2][MF], bf[2][NF];
+    static_assert(KS % 2 == 0, "fragment double-buffering alternates per k-step");
+    static_assert(NST == 2, "register staging uses two LDS slots");
+    u32x4 ra[GA::NIW], rb[GB::NIW];
+    auto vload = [&](auto& P, int k0, u32x4* r, auto geo) {
+      typedef decltype(geo) G;
+      const bool kc = decltype(geo)::KCV;
+      const uint32_t soff = kc ? static_cast<uint32_t>(k0) * 2
+                               : static_cast<uint32_t>(static_cast<int64_t>(k0) * P.ld * 2);
+      // readfirstlane returns int: widen through uint32_t, never by sign extension
+      const uint64_t base = reinterpret_cast<uint64_t>(P.base);
+      const uint64_t lo = static_cast<uint32_t>(
+          __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base)));
+      const uint64_t hi = static_cast<uint32_t>(
+          __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base >> 32)));
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>((hi << 32) | lo), static_cast<short>(0),
+          __builtin_amdgcn_readfirstlane(P.nrec), 0x00020000);
+      const bool tail = kc && (k0 + BK > P.klim);
 #pragma unroll
-    for (int mi = 0; mi < MF; ++mi) af[0][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], 0);
-#pragma unroll
-    for (int ni = 0; ni < NF; ++ni) bf[0][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], 0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < KS) {
-#pragma unroll
-        for (int mi = 0; mi < MF; ++mi)
-          af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
-#pragma unroll
-        for (int ni = 0; ni < NF; ++ni)
-          bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], ks + 1);
-      }
-      if (refill_dma) {
-#pragma unroll
-        for (int t = ks * NT / KS; t < (ks + 1) * NT / KS; ++t) {
-          if (t < GA::NIW)
-            fill_one<BM, BK, A_KC>(PA, k0n, san, wave, lane, t);
-          else
-            fill_one<BN, BK, B_KC>(PB, k0n, sbn, wave, lane, t - GA::NIW);
+      for (int i = 0; i < G::NIW; ++i) {
+        const int j = wave + NW * i;
+        if (G::TI % NW == 0 || j < G::TI) {
+          uint32_t vo = P.vo[i];
+          if (tail) {
+            const int rr = G::RPI * j + lane / G::CPR;
+            const int c = (lane % G::CPR) ^ kswz<BK>(rr);
+            if (k0 + c * 8 >= P.klim) vo = kOOB;
+          }
+          r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, __builtin_amdgcn_readfirstlane(soff), 0);
         }
       }
+    };
+    auto load_tile = [&](int j) {
+      if (j < nk0) {
+        vload(pa0, j * BK, ra, GeoK<GA, A_KC>());
+        vload(pb0, j * BK, rb, GeoK<GB, B_KC>());
+      } else {
+        vload(pa1, (j - nk0) * BK, ra, GeoK<GA, A_KC>());
+        vload(pb1, (j - nk0) * BK, rb, GeoK<GB, B_KC>());
+      }
+    };
+    auto store_tile = [&](int j) {
+      char* sa = smem + (j % NST) * ST;
+      char* sb = sa + A_BYTES;
 #pragma unroll
-      for (int mi = 0; mi < MF; ++mi)
+      for (int i = 0; i < GA::NIW; ++i) {
+        const int jj = wave + NW * i;
+        if (GA::TI % NW == 0 || jj < GA::TI)
+          *reinterpret_cast<u32x4*>(sa + jj * 1024 + 16 * lane) = ra[i];
+      }
 #pragma unroll
-        for (int ni = 0; ni < NF; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][ni], af[cur][mi],
-                                                                acc[mi][ni], 0, 0, 0);
+      for (int i = 0; i < GB::NIW; ++i) {
+        const int jj = wave + NW * i;
+        if (GB::TI % NW == 0 || jj < GB::TI)
+          *reinterpret_cast<u32x4*>(sb + jj * 1024 + 16 * lane) = rb[i];
+      }
+    };
+    bf16x8 af[2][MF], bf[2][NF];
+    if (nk > 0) {
+      load_tile(0);
+      wait_vmcnt<0>();
+      store_tile(0);
+      if (nk > 1) load_tile(1);
+      __syncthreads();
+#pragma unroll
+      for (int mi = 0; mi < MF; ++mi) af[0][mi] = read_frag<BM, BK, A_KC, MF>(smem, FA, mi, fa_base[mi], 0);
+#pragma unroll
+      for (int ni = 0; ni < NF; ++ni) bf[0][ni] = read_frag<BN, BK, B_KC, NF>(smem + A_BYTES, FB, ni, fb_base[ni], 0);
     }
+    for (int it = 0; it < nk; ++it) {
+      const char* sa = smem + (it % NST) * ST;
+      const char* sb = sa + A_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < KS) {
+#pragma unroll
+          for (int mi = 0; mi < MF; ++mi)
+            af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
+#pragma unroll
+          for (int ni = 0; ni < NF; ++ni)
+            bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], ks + 1);
+        } else if (it + 1 < nk) {
+          // Before the last k-step's MFMAs: every wave has read all of tile
+          // it (its slot may be refilled next) and has written tile it+1, so
+          // one barrier covers both, and the first fragment reads of tile
+          // it+1 overlap this k-step's MFMAs.
+          barrier_lds();
+          const char* na = smem + ((it + 1) % NST) * ST;
+#pragma unroll
+          for (int mi = 0; mi < MF; ++mi)
+            af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(na, FA, mi, fa_base[mi], 0);
+#pragma unroll
+          for (int ni = 0; ni < NF; ++ni)
+            bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(na + A_BYTES, FB, ni, fb_base[ni], 0);
+        }
+        if (ks == 1 && it + 1 < nk) {
+          wait_vmcnt<0>();       // tile it+1 is in registers
+          store_tile(it + 1);    // its slot was last read in tile it-1, before the last barrier
+          if (it + 2 < nk) load_tile(it + 2);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MF; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NF; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][ni], af[cur][mi],
+                                                                  acc[mi][ni], 0, 0, 0);
+      }
+    }
+  } else {
+  #pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < nk) issue(s);
+    for (int it = 0; it < nk; ++it) {
+      // stage `it` must have landed; the DMA-only stages after it may stay in flight
+      {
+        int ahead = min(NST - 2, nk - 1 - it);
+        for (int s = 1; s <= ahead; ++s)
+          if (!dma_stage(it + s)) ahead = 0;
+        constexpr int PER = GA::MINW + GB::MINW;
+        switch (ahead) {
+          case 1: wait_vmcnt<PER>(); break;
+          case 2: wait_vmcnt<2 * PER>(); break;
+          case 3: wait_vmcnt<3 * PER>(); break;
+          case 4: wait_vmcnt<4 * PER>(); break;
+          default: wait_vmcnt<0>(); break;
+        }
+      }
+      barrier_lds();
+      // Stage it+NST-1 is refilled while stage `it` is multiplied: its DMA
+      // instructions are spread over the k-steps so that load issue overlaps the
+      // MFMAs instead of stalling in-order issue in one burst.
+      const int jn = it + NST - 1;
+      const bool refill = jn < nk;
+      const bool refill_dma = refill && dma_stage(jn);
+      if (refill && !refill_dma) issue(jn);  // element-wise fill (rare shapes)
+      const bool segn1 = jn >= nk0;
+      const int k0n = (segn1 ? jn - nk0 : jn) * BK;
+      const Plan<BM, BK, A_KC, NW> PA = segn1 ? pa1 : pa0;
+      const Plan<BN, BK, B_KC, NW> PB = segn1 ? pb1 : pb0;
+      char* san = smem + (jn % NST) * ST;
+      char* sbn = san + A_BYTES;
+      const char* sa = smem + (it % NST) * ST;
+      const char* sb = sa + A_BYTES;
+      constexpr int KS = BK / 16;
+      constexpr int NT = GA::NIW + GB::NIW;
+      // Fragments are double-buffered in registers: the LDS reads of k-step
+      // ks+1 are in flight while the MFMAs of k-step ks run.
+      bf16x8 af[2][MF], bf[2][NF];
+  #pragma unroll
+      for (int mi = 0; mi < MF; ++mi) af[0][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], 0);
+  #pragma unroll
+      for (int ni = 0; ni < NF; ++ni) bf[0][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], 0);
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < KS) {
+  #pragma unroll
+          for (int mi = 0; mi < MF; ++mi)
+            af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
+  #pragma unroll
+          for (int ni = 0; ni < NF; ++ni)
+            bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], ks + 1);
+        }
+        if (refill_dma) {
+  #pragma unroll
+          for (int t = ks * NT / KS; t < (ks + 1) * NT / KS; ++t) {
+            if (t < GA::NIW)
+              fill_one<BM, BK, A_KC, NW>(PA, k0n, san, wave, lane, t);
+            else
+              fill_one<BN, BK, B_KC, NW>(PB, k0n, sbn, wave, lane, t - GA::NIW);
+          }
+        }
+  #pragma unroll
+        for (int mi = 0; mi < MF; ++mi)
+  #pragma unroll
+          for (int ni = 0; ni < NF; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][ni], af[cur][mi],
+                                                                  acc[mi][ni], 0, 0, 0);
+      }
+    }
+
   }
 
   // ---- Epilogue, staged through LDS. After the final wait no DMA is in
@@ -711,7 +841,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_bf16(GemmArgs p) {
   // 32-row slab mi and the columns 8*(v/4) + 4*(lane/32) + v%4 of fragment ni.
   __syncthreads();
   constexpr int SLAB = 32 * WN * 4;
-  static_assert(4 * SLAB <= NST * ST, "epilogue slab does not fit in the LDS ring");
+  static_assert(NW * SLAB <= NST * ST, "epilogue slab does not fit in the LDS ring");
   char* slab = smem + wave * SLAB;
   const int srow = lane & 31, shalf = lane >> 5;
   const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0 && (p.ld_out & 7) == 0 &&
@@ -901,12 +1031,15 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs p) {
 }
 
 // ----------------------------------------------------------------- tile list
-// One block of 1024 threads (E <= 1024): M tiles of `bm` rows per expert, in
-// expert order; empty experts get none.
+// One block of 1024 threads (E <= 1024). Two lists in one launch, for two tile
+// heights: M tiles of `bm` rows per expert, in expert order; empty experts get
+// none.
 __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                     int bm, int4* __restrict__ tiles,
-                                                     int32_t* __restrict__ ntiles) {
-  __shared__ int wsum[1024 / kWave];
+                                                     int bm0, int4* __restrict__ tiles0,
+                                                     int32_t* __restrict__ ntiles0, int bm1,
+                                                     int4* __restrict__ tiles1,
+                                                     int32_t* __restrict__ ntiles1) {
+  __shared__ int wsum[2][1024 / kWave];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int e = threadIdx.x;
   int lo = 0, cnt = 0;
@@ -914,26 +1047,31 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
     lo = offsets[e];
     cnt = offsets[e + 1] - lo;
   }
-  const int nt = (cnt + bm - 1) / bm;
-  int incl = nt;
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += o;
+  for (int l = 0; l < 2; ++l) {
+    const int bm = l ? bm1 : bm0;
+    int4* tiles = l ? tiles1 : tiles0;
+    const int nt = (cnt + bm - 1) / bm;
+    int incl = nt;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      int o = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) wsum[l][wave] = incl;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int w = 0; w < 1024 / kWave; ++w) {
+      if (w < wave) base += wsum[l][w];
+      total += wsum[l][w];
+    }
+    base += incl - nt;
+    for (int i = 0; i < nt; ++i) {
+      const int r = i * bm;
+      tiles[base + i] = make_int4(e, lo + r, min(bm, cnt - r), 0);
+    }
+    if (threadIdx.x == 0) *(l ? ntiles1 : ntiles0) = total;
   }
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  int base = 0, total = 0;
-  for (int w = 0; w < 1024 / kWave; ++w) {
-    if (w < wave) base += wsum[w];
-    total += wsum[w];
-  }
-  base += incl - nt;
-  for (int i = 0; i < nt; ++i) {
-    const int r = i * bm;
-    tiles[base + i] = make_int4(e, lo + r, min(bm, cnt - r), 0);
-  }
-  if (threadIdx.x == 0) *ntiles = total;
 }
 
 // ----------------------------------------------------------------- host side
@@ -959,48 +1097,96 @@ Opnd none() { return Opnd{nullptr, 0, 0, 1, 0}; }
 // Tile list capacity for `bm`-row tiles.
 inline int64_t tile_cap(int64_t N, int E, int bm) { return (N + bm - 1) / bm + E + 1; }
 
-struct WsLayout {
+// Two device-built tile lists: `small` (the LoRA side products and the
+// float32 kernels) and `big` (the four expert GEMMs; its tile height depends
+// on the tile variant).
+struct TileList {
   int4* tiles;
   int32_t* ntiles;
+  int bm;
+};
+
+struct WsLayout {
+  TileList small, big;
   size_t bytes;
 };
 
-inline int tile_rows(int dtype) { return dtype == MOE_BF16 ? 128 : 64; }
+int big_variant();
+inline int small_rows(int dtype) { return dtype == MOE_BF16 ? 128 : 64; }
+// 256-row tiles for the register-staged variants, whose LoRA segment (K = r)
+// must come in 16-byte pieces.
+inline int big_rows(const ExpertDims& d) {
+  if (d.dtype != MOE_BF16) return 64;
+  return big_variant() >= 4 && d.r % 8 == 0 ? 256 : 128;
+}
 
 WsLayout tile_ws(void* ws, const ExpertDims& d) {
   WsLayout L;
-  const int bm = tile_rows(d.dtype);
-  const size_t tb = align_up(static_cast<size_t>(tile_cap(d.N, d.E, bm)) * sizeof(int4));
-  L.tiles = static_cast<int4*>(ws);
-  L.ntiles = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + tb);
-  L.bytes = tb + kAlign;
+  char* p = static_cast<char*>(ws);
+  size_t off = 0;
+  auto list = [&](int bm) {
+    TileList t;
+    t.bm = bm;
+    t.tiles = reinterpret_cast<int4*>(p + off);
+    off += align_up(static_cast<size_t>(tile_cap(d.N, d.E, bm)) * sizeof(int4));
+    t.ntiles = reinterpret_cast<int32_t*>(p + off);
+    off += kAlign;
+    return t;
+  };
+  L.small = list(small_rows(d.dtype));
+  L.big = list(big_rows(d));
+  L.bytes = off;
   return L;
 }
 
-template <typename K>
-hipError_t launch(K kern, int grid, const GemmArgs& a, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
+inline hipError_t build_tiles(const WsLayout& L, const int32_t* offsets, int E, hipStream_t s) {
+  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, L.small.bm,
+                     L.small.tiles, L.small.ntiles, L.big.bm, L.big.tiles, L.big.ntiles);
   return hipGetLastError();
 }
 
-// Tile variants of the four expert GEMMs (128 x 256 tiles, four waves), chosen
-// by measurement on MI355X (variant 1 is the default; MOE_LORA_GEMM_VARIANT
-// overrides it for tuning runs):
-//   0: BK 64, 3 LDS stages (144 KB), one block per CU
-//   1: BK 32, 3 LDS stages (72 KB), two blocks per CU
-//   2: BK 32, 4 LDS stages (96 KB), one block per CU
-//   3: BK 32, 6 LDS stages (144 KB), one block per CU
+template <typename K>
+hipError_t launch(K kern, int grid, const GemmArgs& a, hipStream_t s, int threads = 256) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, a);
+  return hipGetLastError();
+}
+
+// Tile variants of the four expert GEMMs, chosen by measurement on MI355X
+// (variant 5 is the default; MOE_LORA_GEMM_VARIANT overrides it for tuning
+// runs):
+//   0: 128 x 256, four waves, buffer->LDS DMA, BK 64, 3 LDS stages (144 KB), 1 block/CU
+//   1: 128 x 256, four waves, buffer->LDS DMA, BK 32, 3 LDS stages (72 KB), 2 blocks/CU
+//   2: 128 x 256, four waves, buffer->LDS DMA, BK 32, 4 LDS stages (96 KB), 1 block/CU
+//   3: 128 x 256, four waves, buffer->LDS DMA, BK 32, 6 LDS stages (144 KB), 1 block/CU
+//   4: 256 x 256, eight waves (64 x 128 each), BK 64, 2 LDS stages (128 KB),
+//      operands staged through VGPRs (one k tile in flight per wave)
+//   5: as 4 with eight waves of 128 x 64 each
+// Measured: a wave issues buffer->LDS DMA at about a quarter of the rate it
+// issues buffer loads into VGPRs, so the register-staged kernels keep the
+// MFMAs fed with fewer bytes in flight; 256-row tiles also halve the L2
+// traffic per MFMA relative to 128 x 256.
 int big_variant() {
   static int v = [] {
     const char* e = getenv("MOE_LORA_GEMM_VARIANT");
-    return e ? atoi(e) : 1;
+    return e ? atoi(e) : 5;
   }();
   return v;
 }
 
 template <int MODE, int EPI, bool PAIRED, bool A_KC, bool B_KC>
-hipError_t launch_big(int grid, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_big(int grid, const GemmArgs& a, hipStream_t s, int bm) {
+  if (bm == 256) {
+    // The register-staged kernels load every operand in 16-byte pieces; with
+    // an operand that cannot be (unaligned pointer or leading dimension) the
+    // 256-row tiles go to a buffer->LDS kernel with element-wise fills.
+    const bool all_vec = a.a[0].vec && a.b[0].vec && (a.K[1] == 0 || (a.a[1].vec && a.b[1].vec));
+    if (!all_vec)
+      return launch(gemm_bf16<256, 256, 128, 128, 32, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
+    if (big_variant() == 5)
+      return launch(gemm_bf16<256, 256, 128, 64, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, true>, grid, a, s, 512);
+    return launch(gemm_bf16<256, 256, 64, 128, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, true>, grid, a, s, 512);
+  }
   switch (big_variant()) {
     case 0:
       return launch(gemm_bf16<128, 256, 64, 128, 64, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
@@ -1013,19 +1199,19 @@ hipError_t launch_big(int grid, const GemmArgs& a, hipStream_t s) {
   }
 }
 
-// M-tile grid bound for GROUP_M launches (excess blocks exit at once).
-inline int gm_grid(const ExpertDims& d, int ntn) {
-  return static_cast<int>(tile_cap(d.N, d.E, tile_rows(d.dtype)) * ntn);
+// M-tile grid bound for GROUP_M launches over a tile list (excess blocks exit at once).
+inline int gm_grid(const ExpertDims& d, const TileList& t, int ntn) {
+  return static_cast<int>(tile_cap(d.N, d.E, t.bm) * ntn);
 }
 
-GemmArgs base_args(const ExpertDims& d, const int32_t* offsets, const WsLayout& L) {
+GemmArgs base_args(const ExpertDims& d, const int32_t* offsets, const TileList& t) {
   GemmArgs a{};
   a.a[1] = none();
   a.b[1] = none();
   a.E = d.E;
   a.offsets = offsets;
-  a.tiles = L.tiles;
-  a.ntiles = L.ntiles;
+  a.tiles = t.tiles;
+  a.ntiles = t.ntiles;
   a.I = d.I;
   a.scale = 1.0f;
   return a;
@@ -1035,7 +1221,8 @@ GemmArgs base_args(const ExpertDims& d, const int32_t* offsets, const WsLayout& 
 hipError_t side_product(const ExpertDims& d, const int32_t* offsets, const WsLayout& L,
                         const void* A, int K, const void* Lw, int64_t l_estride, int l_kcontig,
                         void* out, hipStream_t s) {
-  GemmArgs a = base_args(d, offsets, L);
+  const TileList& t = L.small;
+  GemmArgs a = base_args(d, offsets, t);
   const bool r_vec = d.r % 8 == 0;
   a.a[0] = opnd(A, 0, K, 1, true);
   a.b[0] = l_kcontig ? opnd(Lw, l_estride, K, 1, true) : opnd(Lw, l_estride, d.r, 0, r_vec);
@@ -1050,18 +1237,18 @@ hipError_t side_product(const ExpertDims& d, const int32_t* offsets, const WsLay
     if (l_kcontig) {
       if (d.r <= 32)
         return launch(gemm_bf16<128, 32, 32, 32, 64, 3, 2, GROUP_M, EPI_STORE, false, true, true>,
-                      gm_grid(d, 1), a, s);
+                      gm_grid(d, t, 1), a, s);
       return launch(gemm_bf16<128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE, false, true, true>,
-                    gm_grid(d, 1), a, s);
+                    gm_grid(d, t, 1), a, s);
     }
     if (d.r <= 32)
       return launch(gemm_bf16<128, 32, 32, 32, 64, 3, 2, GROUP_M, EPI_STORE, false, true, false>,
-                    gm_grid(d, 1), a, s);
+                    gm_grid(d, t, 1), a, s);
     return launch(gemm_bf16<128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE, false, true, false>,
-                  gm_grid(d, 1), a, s);
+                  gm_grid(d, t, 1), a, s);
   }
   a.ntn = ceil_div(d.r, 64);
-  return launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, a.ntn), a, s);
+  return launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, t, a.ntn), a, s);
 }
 
 // out_e[P, Q] = sum over the expert's rows n of L[n, P] R[n, Q]  (L: [rows, P], R: [rows, Q]).
@@ -1129,18 +1316,15 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
                               const moe_weights& w, const moe_saved& sv, void* ws,
                               hipStream_t s, KernelTimer* tm) {
   const WsLayout L = tile_ws(ws, d);
-  const int bm = tile_rows(d.dtype);
   const int H = d.H, I = d.I, r = d.r;
-  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, d.E, bm, L.tiles,
-                     L.ntiles);
-  MOE_TRY(hipGetLastError());
+  MOE_TRY(build_tiles(L, offsets, d.E, s));
   {  // u_gu = s X A_gu^T
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
     MOE_TRY(side_product(d, offsets, L, x_perm, H, w.a_gu, static_cast<int64_t>(r) * H, 1,
                          sv.u_gu, s));
   }
   {  // h = X W_gu^T + u_gu B_gu^T ; act = SwiGLU(h)
-    GemmArgs a = base_args(d, offsets, L);
+    GemmArgs a = base_args(d, offsets, L.big);
     a.a[0] = opnd(x_perm, 0, H, 1, true);
     a.b[0] = opnd(w.w_gu, static_cast<int64_t>(2) * I * H, H, 1, true);
     a.a[1] = opnd(sv.u_gu, 0, r, 1, r % 8 == 0);
@@ -1155,11 +1339,11 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
     TimedScope ts(tm, MOE_K_GATE_UP_FWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(I, 128);
-      MOE_TRY((launch_big<GROUP_M, EPI_SWIGLU, true, true, true>( gm_grid(d, a.ntn),
-                     a, s)));
+      MOE_TRY((launch_big<GROUP_M, EPI_SWIGLU, true, true, true>( gm_grid(d, L.big, a.ntn),
+                     a, s, L.big.bm)));
     } else {
       a.ntn = ceil_div(I, 64);
-      MOE_TRY(launch(gemm_f32<GROUP_M, EPI_SWIGLU, true>, gm_grid(d, a.ntn), a, s));
+      MOE_TRY(launch(gemm_f32<GROUP_M, EPI_SWIGLU, true>, gm_grid(d, L.big, a.ntn), a, s));
     }
   }
   {  // u_d = s act A_d^T
@@ -1168,7 +1352,7 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
                          sv.u_d, s));
   }
   {  // y_exp = act W_d^T + u_d B_d^T
-    GemmArgs a = base_args(d, offsets, L);
+    GemmArgs a = base_args(d, offsets, L.big);
     a.a[0] = opnd(sv.act, 0, I, 1, true);
     a.b[0] = opnd(w.w_d, static_cast<int64_t>(H) * I, I, 1, true);
     a.a[1] = opnd(sv.u_d, 0, r, 1, r % 8 == 0);
@@ -1181,11 +1365,11 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
     TimedScope ts(tm, MOE_K_DOWN_FWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(H, 256);
-      MOE_TRY((launch_big<GROUP_M, EPI_STORE, false, true, true>( gm_grid(d, a.ntn),
-                     a, s)));
+      MOE_TRY((launch_big<GROUP_M, EPI_STORE, false, true, true>( gm_grid(d, L.big, a.ntn),
+                     a, s, L.big.bm)));
     } else {
       a.ntn = ceil_div(H, 64);
-      MOE_TRY(launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, a.ntn), a, s));
+      MOE_TRY(launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, L.big, a.ntn), a, s));
     }
   }
   return hipSuccess;
@@ -1196,7 +1380,6 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
                               const moe_saved& sv, void* dx_perm, const moe_lora_grads& gr,
                               void* ws, hipStream_t s, KernelTimer* tm) {
   const WsLayout L = tile_ws(ws, d);
-  const int bm = tile_rows(d.dtype);
   const int H = d.H, I = d.I, r = d.r;
   const size_t esz = d.dtype == MOE_BF16 ? 2 : 4;
   char* p = static_cast<char*>(ws) + L.bytes;
@@ -1206,15 +1389,13 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
   p += align_up(static_cast<size_t>(d.N) * r * esz);
   void* dh = p;
 
-  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, d.E, bm, L.tiles,
-                     L.ntiles);
-  MOE_TRY(hipGetLastError());
+  MOE_TRY(build_tiles(L, offsets, d.E, s));
   {  // gb = s G B_d      (B_d[e] is [H, r]: K = H rows, r contiguous)
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
     MOE_TRY(side_product(d, offsets, L, g, H, w.b_d, static_cast<int64_t>(H) * r, 0, gb, s));
   }
   {  // dAct = G W_d + gb A_d ; dH = SwiGLU'(h) dAct
-    GemmArgs a = base_args(d, offsets, L);
+    GemmArgs a = base_args(d, offsets, L.big);
     a.a[0] = opnd(g, 0, H, 1, true);
     a.b[0] = opnd(w.w_d, static_cast<int64_t>(H) * I, I, 0, true);   // [K=H][N=I]
     a.a[1] = opnd(gb, 0, r, 1, r % 8 == 0);
@@ -1230,10 +1411,10 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(I, 256);
       MOE_TRY((launch_big<GROUP_M, EPI_SWIGLU_BWD, false, true, false>(
-                     gm_grid(d, a.ntn), a, s)));
+                     gm_grid(d, L.big, a.ntn), a, s, L.big.bm)));
     } else {
       a.ntn = ceil_div(I, 64);
-      MOE_TRY(launch(gemm_f32<GROUP_M, EPI_SWIGLU_BWD, false>, gm_grid(d, a.ntn), a, s));
+      MOE_TRY(launch(gemm_f32<GROUP_M, EPI_SWIGLU_BWD, false>, gm_grid(d, L.big, a.ntn), a, s));
     }
   }
   {  // dB_d = G^T u_d  [H, r] ;  dA_d = gb^T act  [r, I]
@@ -1247,7 +1428,7 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
                          dhb, s));
   }
   {  // dX = dH W_gu + dhb A_gu
-    GemmArgs a = base_args(d, offsets, L);
+    GemmArgs a = base_args(d, offsets, L.big);
     a.a[0] = opnd(dh, 0, 2 * I, 1, true);
     a.b[0] = opnd(w.w_gu, static_cast<int64_t>(2) * I * H, H, 0, true);  // [K=2I][N=H]
     a.a[1] = opnd(dhb, 0, r, 1, r % 8 == 0);
@@ -1260,11 +1441,11 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     TimedScope ts(tm, MOE_K_GATE_UP_BWD, s);
     if (d.dtype == MOE_BF16) {
       a.ntn = ceil_div(H, 256);
-      MOE_TRY((launch_big<GROUP_M, EPI_STORE, false, true, false>( gm_grid(d, a.ntn),
-                     a, s)));
+      MOE_TRY((launch_big<GROUP_M, EPI_STORE, false, true, false>( gm_grid(d, L.big, a.ntn),
+                     a, s, L.big.bm)));
     } else {
       a.ntn = ceil_div(H, 64);
-      MOE_TRY(launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, a.ntn), a, s));
+      MOE_TRY(launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, L.big, a.ntn), a, s));
     }
   }
   {  // dB_gu = dH^T u_gu  [2I, r] ;  dA_gu = dhb^T X  [r, H]
