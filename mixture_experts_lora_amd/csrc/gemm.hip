@@ -35,6 +35,8 @@
 // plain FMA kernel with the same tiling logic.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -481,7 +483,7 @@ __device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int BM, int BN, int WM, int WN, int BK, int NST, int MINB, int MODE, int EPI,
-          bool PAIRED, bool A_KC, bool B_KC, bool VST = false>
+          bool PAIRED, bool A_KC, bool B_KC, int VST = 0>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(GemmArgs p) {
   constexpr int WAVES_N = BN / WN, MF = WM / 32, NF = WN / 32;
   constexpr int NW = (BM / WM) * (BN / WN);
@@ -638,18 +640,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  if constexpr (VST) {
+  if constexpr (VST > 0) {
     // ---- Register-staged main loop: every wave loads its share of a k tile
     // into VGPRs (16 bytes per lane per 1 KB piece, the same lane offsets as
     // the DMA plans, out-of-range lanes read zeros) and writes it to the LDS
-    // slot the tile belongs to. Two LDS slots; tile it+1 is written during
-    // tile it's second k-step (its slot was last read before the previous
-    // barrier), and the load of tile it+2 is issued right after, so each load
-    // has a whole tile of MFMAs to arrive.
+    // slot the tile belongs to. Two LDS slots and NRB register buffers: tile
+    // it+1 is written during tile it's second k-step (its slot was last read
+    // before the previous barrier), and the load of tile it+1+NRB is issued
+    // into the buffer just freed, so each load has NRB tiles of MFMAs to
+    // arrive. Buffer indices are compile-time (the tile loop is unrolled by
+    // NRB); the compiler's own waits on the loaded registers keep the other
+    // buffers' loads in flight.
+    constexpr int NRB = VST;
     constexpr int KS = BK / 16;
     static_assert(KS % 2 == 0, "fragment double-buffering alternates per k-step");
     static_assert(NST == 2, "register staging uses two LDS slots");
-    u32x4 ra[GA::NIW], rb[GB::NIW];
+    u32x4 ra[NRB][GA::NIW], rb[NRB][GB::NIW];
     auto vload = [&](auto& P, int k0, u32x4* r, auto geo) {
       typedef decltype(geo) G;
       const bool kc = decltype(geo)::KCV;
@@ -679,44 +685,47 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
         }
       }
     };
-    auto load_tile = [&](int j) {
+    auto load_tile = [&](int j, u32x4* a, u32x4* b) {
       if (j < nk0) {
-        vload(pa0, j * BK, ra, GeoK<GA, A_KC>());
-        vload(pb0, j * BK, rb, GeoK<GB, B_KC>());
+        vload(pa0, j * BK, a, GeoK<GA, A_KC>());
+        vload(pb0, j * BK, b, GeoK<GB, B_KC>());
       } else {
-        vload(pa1, (j - nk0) * BK, ra, GeoK<GA, A_KC>());
-        vload(pb1, (j - nk0) * BK, rb, GeoK<GB, B_KC>());
+        vload(pa1, (j - nk0) * BK, a, GeoK<GA, A_KC>());
+        vload(pb1, (j - nk0) * BK, b, GeoK<GB, B_KC>());
       }
     };
-    auto store_tile = [&](int j) {
+    auto store_tile = [&](int j, const u32x4* a, const u32x4* b) {
       char* sa = smem + (j % NST) * ST;
       char* sb = sa + A_BYTES;
 #pragma unroll
       for (int i = 0; i < GA::NIW; ++i) {
         const int jj = wave + NW * i;
         if (GA::TI % NW == 0 || jj < GA::TI)
-          *reinterpret_cast<u32x4*>(sa + jj * 1024 + 16 * lane) = ra[i];
+          *reinterpret_cast<u32x4*>(sa + jj * 1024 + 16 * lane) = a[i];
       }
 #pragma unroll
       for (int i = 0; i < GB::NIW; ++i) {
         const int jj = wave + NW * i;
         if (GB::TI % NW == 0 || jj < GB::TI)
-          *reinterpret_cast<u32x4*>(sb + jj * 1024 + 16 * lane) = rb[i];
+          *reinterpret_cast<u32x4*>(sb + jj * 1024 + 16 * lane) = b[i];
       }
     };
     bf16x8 af[2][MF], bf[2][NF];
     if (nk > 0) {
-      load_tile(0);
-      wait_vmcnt<0>();
-      store_tile(0);
-      if (nk > 1) load_tile(1);
+      load_tile(0, ra[0], rb[0]);
+      store_tile(0, ra[0], rb[0]);
+#pragma unroll
+      for (int q = 1; q <= NRB; ++q)
+        if (q < nk) load_tile(q, ra[q % NRB], rb[q % NRB]);
       __syncthreads();
 #pragma unroll
       for (int mi = 0; mi < MF; ++mi) af[0][mi] = read_frag<BM, BK, A_KC, MF>(smem, FA, mi, fa_base[mi], 0);
 #pragma unroll
       for (int ni = 0; ni < NF; ++ni) bf[0][ni] = read_frag<BN, BK, B_KC, NF>(smem + A_BYTES, FB, ni, fb_base[ni], 0);
     }
-    for (int it = 0; it < nk; ++it) {
+    // one k tile; tile it+1 sits in register buffer BUF = (it + 1) % NRB
+    auto ktile = [&](int it, auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
       const char* sa = smem + (it % NST) * ST;
       const char* sb = sa + A_BYTES;
 #pragma unroll
@@ -744,9 +753,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
             bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(na + A_BYTES, FB, ni, fb_base[ni], 0);
         }
         if (ks == 1 && it + 1 < nk) {
-          wait_vmcnt<0>();       // tile it+1 is in registers
-          store_tile(it + 1);    // its slot was last read in tile it-1, before the last barrier
-          if (it + 2 < nk) load_tile(it + 2);
+          // tile it+1's slot was last read in tile it-1, before the last barrier
+          store_tile(it + 1, ra[BUF], rb[BUF]);
+          if (it + 1 + NRB < nk) load_tile(it + 1 + NRB, ra[BUF], rb[BUF]);
         }
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi)
@@ -755,6 +764,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][ni], af[cur][mi],
                                                                   acc[mi][ni], 0, 0, 0);
       }
+    };
+    for (int it = 0; it < nk; it += NRB) {
+      ktile(it, std::integral_constant<int, 1 % NRB>());
+      if (NRB > 1 && it + 1 < nk) ktile(it + 1, std::integral_constant<int, 2 % NRB>());
     }
   } else {
   #pragma unroll
@@ -1183,9 +1196,12 @@ hipError_t launch_big(int grid, const GemmArgs& a, hipStream_t s, int bm) {
     const bool all_vec = a.a[0].vec && a.b[0].vec && (a.K[1] == 0 || (a.a[1].vec && a.b[1].vec));
     if (!all_vec)
       return launch(gemm_bf16<256, 256, 128, 128, 32, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
-    if (big_variant() == 5)
-      return launch(gemm_bf16<256, 256, 128, 64, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, true>, grid, a, s, 512);
-    return launch(gemm_bf16<256, 256, 64, 128, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, true>, grid, a, s, 512);
+    switch (big_variant()) {
+      case 4:
+        return launch(gemm_bf16<256, 256, 64, 128, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 1>, grid, a, s, 512);
+      default:
+        return launch(gemm_bf16<256, 256, 128, 64, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 1>, grid, a, s, 512);
+    }
   }
   switch (big_variant()) {
     case 0:
