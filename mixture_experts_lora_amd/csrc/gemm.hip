@@ -459,9 +459,11 @@ __device__ __forceinline__ void read8_interleaved(const char* slab, int r, int s
 }
 
 // Eight consecutive bf16 as one 16-byte global access (16-byte aligned).
+// Epilogue traffic is streamed once: non-temporal loads and stores keep it
+// from evicting the operand tiles the other blocks are reading from L2.
 __device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
-  const uint4 r = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  const uint32_t w[4] = {r[0], r[1], r[2], r[3]};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     v[2 * j] = __uint_as_float(w[j] << 16);
@@ -475,7 +477,12 @@ __device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
   for (int j = 0; j < 4; ++j)
     w[j] = static_cast<uint32_t>(f32_to_bf16(v[2 * j])) |
            (static_cast<uint32_t>(f32_to_bf16(v[2 * j + 1])) << 16);
-  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  u32x4 q;
+  q[0] = w[0];
+  q[1] = w[1];
+  q[2] = w[2];
+  q[3] = w[3];
+  __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p));
 }
 
 // LDS writes of this wave are complete (and not reordered by the compiler)
