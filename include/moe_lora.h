@@ -115,6 +115,13 @@ typedef struct {
   void *da_gu, *db_gu, *da_d, *db_d;
 } moe_lora_grads;
 
+/* Base-weight gradients for full fine-tuning, shapes of the weights, all of
+ * `dtype`:  dw_gu [E, 2I, H]   dw_d [E, H, I]. Experts that received no rows
+ * get zeros. */
+typedef struct {
+  void *dw_gu, *dw_d;
+} moe_base_grads;
+
 /* Bytes of device scratch each call needs (0 is possible). Host-only, no HIP
  * call. Any pointer may be NULL to skip that figure. */
 moe_status moe_workspace_bytes(const moe_shape *shape, size_t *fwd_ws, size_t *bwd_ws,
@@ -186,6 +193,23 @@ moe_status moe_grouped_lora_bwd(const moe_shape *shape, const void *dy_perm,
                                 void *dx_perm, const moe_lora_grads *grads, void *ws,
                                 size_t ws_bytes, void *stream);
 
+/* Grouped expert backward for full fine-tuning (the faster-moe page lists
+ * full fine-tuning beside LoRA and QLoRA among the modes its kernels serve,
+ * in its introduction, and recommends bf16 LoRA or full fine-tuning for MoE
+ * models in its note on 4-bit QLoRA): everything moe_grouped_lora_bwd
+ * writes, plus the base-weight gradients
+ *   dW_gu[e] = dH_e^T X_e      [2I, H]   (dH = gradient at the gate_up output)
+ *   dW_d[e]  = G_e^T act_e     [H, I]    (G = dy_perm rows of expert e)
+ * each a reduction over the expert's rows, written in full (no accumulation).
+ * Same arguments, workspace and errors as moe_grouped_lora_bwd; `base` and
+ * both its pointers must be non-NULL and may not alias any other buffer.  */
+moe_status moe_grouped_full_bwd(const moe_shape *shape, const void *dy_perm,
+                                const void *x_perm, const int32_t *offsets,
+                                const moe_weights *weights, const moe_saved *saved,
+                                void *dx_perm, const moe_lora_grads *grads,
+                                const moe_base_grads *base, void *ws, size_t ws_bytes,
+                                void *stream);
+
 const char *moe_status_str(moe_status status);
 
 /* Text of the last error raised on the calling thread ("" if none). */
@@ -201,7 +225,7 @@ typedef enum {
   MOE_K_ROUTE = 0, MOE_K_PERMUTE = 1, MOE_K_GATHER = 2, MOE_K_GATE_UP_FWD = 3,
   MOE_K_DOWN_FWD = 4, MOE_K_COMBINE = 5, MOE_K_COMBINE_BWD = 6, MOE_K_ROUTE_BWD = 7,
   MOE_K_DOWN_BWD = 8, MOE_K_GATE_UP_BWD = 9, MOE_K_LORA_SIDE = 10, MOE_K_LORA_WGRAD = 11,
-  MOE_K_UNPERMUTE = 12, MOE_K_COUNT = 13
+  MOE_K_UNPERMUTE = 12, MOE_K_BASE_WGRAD = 13, MOE_K_COUNT = 14
 } moe_kernel_id;
 moe_status moe_kernel_timer_enable(int32_t on);
 moe_status moe_kernel_timer_reset(void);

@@ -22,12 +22,12 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import MoeLoraGrads, MoeSaved, MoeShape, MoeWeights, ROUTER_IDS, check
+from ._lib import MoeBaseGrads, MoeLoraGrads, MoeSaved, MoeShape, MoeWeights, ROUTER_IDS, check
 
 __all__ = [
     "Shape", "moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
     "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
-    "moe_grouped_lora_bwd", "kernel_timer", "ROUTER_IDS", "library_path",
+    "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "kernel_timer", "ROUTER_IDS", "library_path",
 ]
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -195,8 +195,8 @@ def moe_unpermute_combine_bwd(shape: Shape, dy, y_exp, inv_pos, topk_w, dy_perm,
         "moe_unpermute_combine_bwd")
 
 
-def moe_grouped_lora_bwd(shape: Shape, dy_perm, x_perm, offsets, weights: dict, saved: dict,
-                         dx_perm, grads: dict, ws, stream=None):
+def _bwd_args(shape: Shape, dy_perm, x_perm, offsets, weights: dict, saved: dict, dx_perm,
+              grads: dict, ws):
     _, need, _ = moe_workspace_bytes(shape)
     wsp, wsb = _ws(ws, need, "ws")
     E, H, I, r, dt = shape.E, shape.H, shape.I, shape.r, shape.torch_dtype
@@ -206,12 +206,31 @@ def moe_grouped_lora_bwd(shape: Shape, dy_perm, x_perm, offsets, weights: dict, 
                      _ptr(grads["db_gu"], (E, 2 * I, r), dt, "db_gu"),
                      _ptr(grads["da_d"], (E, r, I), dt, "da_d"),
                      _ptr(grads["db_d"], (E, H, r), dt, "db_d"))
-    check(_lib.load().moe_grouped_lora_bwd(
-        ctypes.byref(shape.c()), _ptr(dy_perm, (shape.N, H), dt, "dy_perm"),
-        _ptr(x_perm, (shape.N, H), dt, "x_perm"),
-        _ptr(offsets, (E + 1,), torch.int32, "offsets"), ctypes.byref(w), ctypes.byref(s),
-        _ptr(dx_perm, (shape.N, H), dt, "dx_perm"), ctypes.byref(g), wsp, wsb,
-        _stream(stream)), "moe_grouped_lora_bwd")
+    head = (ctypes.byref(shape.c()), _ptr(dy_perm, (shape.N, H), dt, "dy_perm"),
+            _ptr(x_perm, (shape.N, H), dt, "x_perm"),
+            _ptr(offsets, (E + 1,), torch.int32, "offsets"), ctypes.byref(w), ctypes.byref(s),
+            _ptr(dx_perm, (shape.N, H), dt, "dx_perm"), ctypes.byref(g))
+    return head, (w, s, g), wsp, wsb
+
+
+def moe_grouped_lora_bwd(shape: Shape, dy_perm, x_perm, offsets, weights: dict, saved: dict,
+                         dx_perm, grads: dict, ws, stream=None):
+    head, keep, wsp, wsb = _bwd_args(shape, dy_perm, x_perm, offsets, weights, saved, dx_perm,
+                                     grads, ws)
+    check(_lib.load().moe_grouped_lora_bwd(*head, wsp, wsb, _stream(stream)),
+          "moe_grouped_lora_bwd")
+
+
+def moe_grouped_full_bwd(shape: Shape, dy_perm, x_perm, offsets, weights: dict, saved: dict,
+                         dx_perm, grads: dict, base_grads: dict, ws, stream=None):
+    """moe_grouped_lora_bwd plus the base-weight gradients dw_gu [E, 2I, H], dw_d [E, H, I]."""
+    head, keep, wsp, wsb = _bwd_args(shape, dy_perm, x_perm, offsets, weights, saved, dx_perm,
+                                     grads, ws)
+    E, H, I, dt = shape.E, shape.H, shape.I, shape.torch_dtype
+    b = MoeBaseGrads(_ptr(base_grads["dw_gu"], (E, 2 * I, H), dt, "dw_gu"),
+                     _ptr(base_grads["dw_d"], (E, H, I), dt, "dw_d"))
+    check(_lib.load().moe_grouped_full_bwd(*head, ctypes.byref(b), wsp, wsb, _stream(stream)),
+          "moe_grouped_full_bwd")
 
 
 class kernel_timer:

@@ -13,11 +13,11 @@ ROUTER_IDS = {"softmax_topk": 0, "softmax_topk_renorm": 1, "topk_softmax": 2,
               "sigmoid_topk_renorm": 3}
 KERNEL_IDS = {"route": 0, "permute": 1, "gather": 2, "gate_up_fwd": 3, "down_fwd": 4,
               "combine": 5, "combine_bwd": 6, "route_bwd": 7, "down_bwd": 8, "gate_up_bwd": 9,
-              "lora_side": 10, "lora_wgrad": 11, "unpermute": 12}
+              "lora_side": 10, "lora_wgrad": 11, "unpermute": 12, "base_wgrad": 13}
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
            "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
-           "moe_grouped_lora_bwd", "moe_status_str", "moe_last_error",
+           "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_status_str", "moe_last_error",
            "moe_kernel_timer_enable", "moe_kernel_timer_reset", "moe_kernel_timer_read")
 
 
@@ -37,6 +37,10 @@ class MoeSaved(ctypes.Structure):
 
 class MoeLoraGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("da_gu", "db_gu", "da_d", "db_d")]
+
+
+class MoeBaseGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dw_gu", "dw_d")]
 
 
 _lib = None

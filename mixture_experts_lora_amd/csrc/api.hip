@@ -284,11 +284,12 @@ moe_status moe_unpermute_combine_bwd(const moe_shape* shape, const void* dy,
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_unpermute_combine_bwd");
 }
 
-moe_status moe_grouped_lora_bwd(const moe_shape* shape, const void* dy_perm,
-                                const void* x_perm, const int32_t* offsets,
-                                const moe_weights* weights, const moe_saved* saved,
-                                void* dx_perm, const moe_lora_grads* grads, void* ws,
-                                size_t ws_bytes, void* stream) {
+namespace {
+
+moe_status grouped_bwd(const char* name, const moe_shape* shape, const void* dy_perm,
+                       const void* x_perm, const int32_t* offsets, const moe_weights* weights,
+                       const moe_saved* saved, void* dx_perm, const moe_lora_grads* grads,
+                       const moe_base_grads* base, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   CHECK_PTR(dy_perm);
@@ -315,13 +316,50 @@ moe_status moe_grouped_lora_bwd(const moe_shape* shape, const void* dy_perm,
   CHECK_PTR(ws);
   if (dx_perm == dy_perm || dx_perm == x_perm)
     return fail(MOE_ERR_INVALID_ARG, "dx_perm aliases an input");
+  if (base) {
+    CHECK_PTR(base->dw_gu);
+    CHECK_PTR(base->dw_d);
+    const void* outs[] = {dx_perm, grads->da_gu, grads->db_gu, grads->da_d, grads->db_d};
+    const void* ins[] = {dy_perm, x_perm, saved->act, saved->h, weights->w_gu, weights->w_d};
+    for (const void* b : {static_cast<const void*>(base->dw_gu), static_cast<const void*>(base->dw_d)}) {
+      for (const void* o : outs)
+        if (b == o) return fail(MOE_ERR_INVALID_ARG, "a base gradient aliases another output");
+      for (const void* i : ins)
+        if (b == i) return fail(MOE_ERR_INVALID_ARG, "a base gradient aliases an input");
+    }
+    if (base->dw_gu == base->dw_d)
+      return fail(MOE_ERR_INVALID_ARG, "dw_gu and dw_d alias");
+  }
   const moe::ExpertDims d = dims_of(shape);
   const size_t need = moe::experts_bwd_ws_bytes(d);
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "backward workspace needs " + std::to_string(need) + " bytes");
   hipError_t e = moe::launch_experts_bwd(d, dy_perm, x_perm, offsets, *weights, *saved, dx_perm,
-                                         *grads, ws, as_stream(stream), moe::active_timer());
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_lora_bwd");
+                                         *grads, base, ws, as_stream(stream),
+                                         moe::active_timer());
+  return e == hipSuccess ? MOE_OK : hip_fail(e, name);
+}
+
+}  // namespace
+
+moe_status moe_grouped_lora_bwd(const moe_shape* shape, const void* dy_perm,
+                                const void* x_perm, const int32_t* offsets,
+                                const moe_weights* weights, const moe_saved* saved,
+                                void* dx_perm, const moe_lora_grads* grads, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return grouped_bwd("moe_grouped_lora_bwd", shape, dy_perm, x_perm, offsets, weights, saved,
+                     dx_perm, grads, nullptr, ws, ws_bytes, stream);
+}
+
+moe_status moe_grouped_full_bwd(const moe_shape* shape, const void* dy_perm,
+                                const void* x_perm, const int32_t* offsets,
+                                const moe_weights* weights, const moe_saved* saved,
+                                void* dx_perm, const moe_lora_grads* grads,
+                                const moe_base_grads* base, void* ws, size_t ws_bytes,
+                                void* stream) {
+  CHECK_PTR(base);
+  return grouped_bwd("moe_grouped_full_bwd", shape, dy_perm, x_perm, offsets, weights, saved,
+                     dx_perm, grads, base, ws, ws_bytes, stream);
 }
 
 moe_status moe_kernel_timer_enable(int32_t on) {

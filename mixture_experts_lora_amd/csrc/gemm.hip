@@ -1300,6 +1300,12 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
       a.ntm = ceil_div(P, 256);
       return launch(gemm_bf16<256, 64, 64, 64, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm, a, s);
     }
+    if (P >= 256 && Q >= 256) {  // [big, big]: full fine-tuning weight gradients
+      a.ntm = ceil_div(P, 128);
+      a.ntn = ceil_div(Q, 256);
+      return launch(gemm_bf16<128, 256, 64, 128, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>,
+                    d.E * a.ntm * a.ntn, a, s);
+    }
     // [r, big] (or both small)
     a.ntn = ceil_div(Q, 256);
     if (P <= 32) {
@@ -1401,7 +1407,8 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
 hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_perm,
                               const int32_t* offsets, const moe_weights& w,
                               const moe_saved& sv, void* dx_perm, const moe_lora_grads& gr,
-                              void* ws, hipStream_t s, KernelTimer* tm) {
+                              const moe_base_grads* base, void* ws, hipStream_t s,
+                              KernelTimer* tm) {
   const WsLayout L = tile_ws(ws, d);
   const int H = d.H, I = d.I, r = d.r;
   const size_t esz = d.dtype == MOE_BF16 ? 2 : 4;
@@ -1445,6 +1452,10 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     MOE_TRY(weight_grad(d, offsets, g, H, sv.u_d, r, gr.db_d, s));
     MOE_TRY(weight_grad(d, offsets, gb, r, sv.act, I, gr.da_d, s));
   }
+  if (base) {  // full fine-tuning: dW_d = G^T act  [H, I]
+    TimedScope ts(tm, MOE_K_BASE_WGRAD, s);
+    MOE_TRY(weight_grad(d, offsets, g, H, sv.act, I, base->dw_d, s));
+  }
   {  // dhb = s dH B_gu   (B_gu[e] is [2I, r])
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
     MOE_TRY(side_product(d, offsets, L, dh, 2 * I, w.b_gu, static_cast<int64_t>(2) * I * r, 0,
@@ -1475,6 +1486,10 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
     MOE_TRY(weight_grad(d, offsets, dh, 2 * I, sv.u_gu, r, gr.db_gu, s));
     MOE_TRY(weight_grad(d, offsets, dhb, r, x_perm, H, gr.da_gu, s));
+  }
+  if (base) {  // full fine-tuning: dW_gu = dH^T X  [2I, H]
+    TimedScope ts(tm, MOE_K_BASE_WGRAD, s);
+    MOE_TRY(weight_grad(d, offsets, dh, 2 * I, x_perm, H, base->dw_gu, s));
   }
   return hipSuccess;
 }

@@ -66,9 +66,11 @@ size_t experts_bwd_ws_bytes(const ExpertDims& d);
 hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int32_t* offsets,
                               const moe_weights& w, const moe_saved& sv, void* ws,
                               hipStream_t s, KernelTimer* tm);
+// `base` may be null (LoRA only); otherwise the base-weight gradients are written too.
 hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_perm,
                               const int32_t* offsets, const moe_weights& w,
                               const moe_saved& sv, void* dx_perm, const moe_lora_grads& gr,
-                              void* ws, hipStream_t s, KernelTimer* tm);
+                              const moe_base_grads* base, void* ws, hipStream_t s,
+                              KernelTimer* tm);
 
 }  // namespace moe

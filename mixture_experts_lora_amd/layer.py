@@ -15,17 +15,19 @@ from __future__ import annotations
 
 import torch
 
-from . import (Shape, moe_grouped_lora_bwd, moe_grouped_lora_fwd, moe_permute, moe_route,
-               moe_route_bwd, moe_unpermute_combine, moe_unpermute_combine_bwd,
-               moe_workspace_bytes)
+from . import (Shape, moe_grouped_full_bwd, moe_grouped_lora_bwd, moe_grouped_lora_fwd,
+               moe_permute, moe_route, moe_route_bwd, moe_unpermute_combine,
+               moe_unpermute_combine_bwd, moe_workspace_bytes)
 
 WEIGHT_NAMES = ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")
 GRAD_NAMES = ("da_gu", "db_gu", "da_d", "db_d")
 
 
 class MoELoRALayer:
-    def __init__(self, shape: Shape, router: str, device="cuda"):
-        self.shape, self.router = shape, router
+    """full_ft=True also computes the base-weight gradients (full fine-tuning)."""
+
+    def __init__(self, shape: Shape, router: str, device="cuda", full_ft: bool = False):
+        self.shape, self.router, self.full_ft = shape, router, full_ft
         T, H, I, E, k, r, N = shape.T, shape.H, shape.I, shape.E, shape.k, shape.r, shape.N
         dt = shape.torch_dtype
         z = lambda *s, dtype=dt: torch.empty(s, device=device, dtype=dtype)  # noqa: E731
@@ -41,6 +43,7 @@ class MoELoRALayer:
         self.dx_perm, self.dx = z(N, H), z(T, H)
         self.grads = {"da_gu": z(E, r, H), "db_gu": z(E, 2 * I, r), "da_d": z(E, r, I),
                       "db_d": z(E, H, r)}
+        self.base_grads = ({"dw_gu": z(E, 2 * I, H), "dw_d": z(E, H, I)} if full_ft else None)
         fwd, bwd, perm = moe_workspace_bytes(shape)
         self.ws_fwd = z(max(fwd, 1), dtype=torch.uint8)
         self.ws_bwd = z(max(bwd, 1), dtype=torch.uint8)
@@ -62,8 +65,12 @@ class MoELoRALayer:
                                   self.dy_perm, self.d_topk_w, stream)
         moe_route_bwd(logits, self.topk_ids, self.d_topk_w, s.k, self.router, self.d_logits,
                       stream)
-        moe_grouped_lora_bwd(s, self.dy_perm, self.x_perm, self.offsets, weights, self.saved,
-                             self.dx_perm, self.grads, self.ws_bwd, stream)
+        if self.full_ft:
+            moe_grouped_full_bwd(s, self.dy_perm, self.x_perm, self.offsets, weights, self.saved,
+                                 self.dx_perm, self.grads, self.base_grads, self.ws_bwd, stream)
+        else:
+            moe_grouped_lora_bwd(s, self.dy_perm, self.x_perm, self.offsets, weights, self.saved,
+                                 self.dx_perm, self.grads, self.ws_bwd, stream)
         moe_unpermute_combine(s, self.dx_perm, self.inv_pos, None, self.dx, stream)
         return self.dx, self.d_logits, self.grads
 
@@ -74,7 +81,9 @@ class MoELoRALayer:
 
 
 class MoELoRAFunction(torch.autograd.Function):
-    """Y = layer(x, logits); gradients for x, logits and the LoRA A/B (W frozen)."""
+    """Y = layer(x, logits); gradients for x, logits and the LoRA A/B. The base
+    weights are frozen unless w_gu or w_d requires grad (full fine-tuning), in
+    which case their gradients are computed too."""
 
     @staticmethod
     def forward(ctx, x, logits, w_gu, a_gu, b_gu, w_d, a_d, b_d, router, k, lora_scale=1.0):
@@ -83,7 +92,8 @@ class MoELoRAFunction(torch.autograd.Function):
         I = w_gu.shape[1] // 2
         dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}[x.dtype]
         shape = Shape(T, H, I, E, k, r, dtype, lora_scale)
-        layer = MoELoRALayer(shape, router, device=x.device)
+        full = bool(ctx.needs_input_grad[2] or ctx.needs_input_grad[5])
+        layer = MoELoRALayer(shape, router, device=x.device, full_ft=full)
         weights = dict(zip(WEIGHT_NAMES, (w_gu, a_gu, b_gu, w_d, a_d, b_d)))
         y = layer.forward(x.contiguous(), logits.contiguous(), weights).clone()
         ctx.layer, ctx.weights, ctx.logits = layer, weights, logits.contiguous()
@@ -91,6 +101,10 @@ class MoELoRAFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, dy):
-        dx, dl, g = ctx.layer.backward(dy.contiguous(), ctx.logits, ctx.weights)
-        return (dx.clone(), dl.clone(), None, g["da_gu"].clone(), g["db_gu"].clone(), None,
+        layer = ctx.layer
+        dx, dl, g = layer.backward(dy.contiguous(), ctx.logits, ctx.weights)
+        bg = layer.base_grads
+        dw_gu = bg["dw_gu"].clone() if bg is not None and ctx.needs_input_grad[2] else None
+        dw_d = bg["dw_d"].clone() if bg is not None and ctx.needs_input_grad[5] else None
+        return (dx.clone(), dl.clone(), dw_gu, g["da_gu"].clone(), g["db_gu"].clone(), dw_d,
                 g["da_d"].clone(), g["db_d"].clone(), None, None, None)

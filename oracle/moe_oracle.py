@@ -190,12 +190,16 @@ def expert_forward(X_e, w_gu, a_gu, b_gu, w_d, a_d, b_d, s=1.0, dtype=np.float32
 
 
 def expert_backward(X_e, G_e, fwd, w_gu, a_gu, b_gu, w_d, a_d, b_d, s=1.0,
-                    dtype=np.float32):
+                    dtype=np.float32, base_grads=False):
     """Backward of `expert_forward` for upstream gradient G_e = dL/dy [n, H].
 
-    Base weights are frozen ([moe], "Implementation details": only the rank-r
-    adapters are trained), so there is no dW. Returns dict with
+    With LoRA the base weights are frozen ([moe], "Implementation details":
+    only the rank-r adapters are trained), so there is no dW. Returns dict with
     dx [n, H], da_gu [r, H], db_gu [2I, r], da_d [r, I], db_d [H, r], dh [n, 2I].
+    base_grads=True adds the base-weight gradients of full fine-tuning (a mode
+    the [moe] page's introduction lists beside LoRA): dw_gu [2I, H] = dh^T X and
+    dw_d [H, I] = G^T a (the chain rule through X W^T; the LoRA scale does not
+    enter).
     """
     X = np.asarray(X_e, dtype=dtype)
     G = np.asarray(G_e, dtype=dtype)
@@ -220,8 +224,11 @@ def expert_backward(X_e, G_e, fwd, w_gu, a_gu, b_gu, w_d, a_d, b_d, s=1.0,
     dx = dh @ W1 + s * (dhb @ A1)                 # [n, H]
     db_gu = s * (dh.T @ u_gu)                     # [2I, r]
     da_gu = s * (dhb.T @ X)                       # [r, H]
-    return {"dx": dx, "da_gu": da_gu, "db_gu": db_gu, "da_d": da_d, "db_d": db_d,
-            "dh": dh}
+    out = {"dx": dx, "da_gu": da_gu, "db_gu": db_gu, "da_d": da_d, "db_d": db_d, "dh": dh}
+    if base_grads:
+        out["dw_gu"] = dh.T @ X                   # [2I, H]
+        out["dw_d"] = G.T @ a                     # [H, I]
+    return out
 
 
 # ------------------------------------------------------------------------- combine
@@ -290,10 +297,11 @@ def layer_forward(x, logits, weights, k, router, s=1.0, dtype=np.float32):
     return Y, cache
 
 
-def layer_backward(dY, cache):
+def layer_backward(dY, cache, base_grads=False):
     """Whole backward. Returns dict with dx [T, H], dlogits [T, E], and the LoRA
     gradients da_gu [E, r, H], db_gu [E, 2I, r], da_d [E, r, I], db_d [E, H, r]
-    (zeros for experts that received no rows)."""
+    (zeros for experts that received no rows); base_grads=True adds
+    dw_gu [E, 2I, H] and dw_d [E, H, I] (full fine-tuning)."""
     dtype = cache["dtype"]
     x, k, s, wts = cache["x"], cache["k"], cache["s"], cache["weights"]
     T, H = x.shape
@@ -305,6 +313,10 @@ def layer_backward(dY, cache):
              "db_gu": np.zeros((E,) + b_gu0.shape, dtype),
              "da_d": np.zeros((E,) + a_d0.shape, dtype),
              "db_d": np.zeros((E,) + b_d0.shape, dtype)}
+    if base_grads:
+        w_gu0, w_d0 = (np.asarray(wts[n][0]) for n in ("w_gu", "w_d"))
+        grads["dw_gu"] = np.zeros((E,) + w_gu0.shape, dtype)
+        grads["dw_d"] = np.zeros((E,) + w_d0.shape, dtype)
     N = T * k
     dx_perm = np.zeros((N, H), dtype=dtype)
     offsets, sorted_pair = cache["offsets"], cache["sorted_pair"]
@@ -314,7 +326,8 @@ def layer_backward(dY, cache):
             continue
         X_e = x[sorted_pair[lo:hi] // k]
         we = {n: wts[n][e] for n in ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")}
-        b = expert_backward(X_e, G[lo:hi], cache["per_expert"][e], **we, s=s, dtype=dtype)
+        b = expert_backward(X_e, G[lo:hi], cache["per_expert"][e], **we, s=s, dtype=dtype,
+                            base_grads=base_grads)
         dx_perm[lo:hi] = b["dx"]
         for n in grads:
             grads[n][e] = b[n]
@@ -352,7 +365,8 @@ def merged_forward(x, logits, weights, k, router, s=1.0, dtype=np.float32):
     return combine(y_perm, inv_pos, w, T, k, dtype)
 
 
-def layer_forward_backward(x, logits, dY, weights, k, router, s=1.0, dtype=np.float32):
+def layer_forward_backward(x, logits, dY, weights, k, router, s=1.0, dtype=np.float32,
+                           base_grads=False):
     """Forward then backward; returns (Y, grads dict, cache)."""
     Y, cache = layer_forward(x, logits, weights, k, router, s, dtype)
-    return Y, layer_backward(dY, cache), cache
+    return Y, layer_backward(dY, cache, base_grads), cache

@@ -82,3 +82,34 @@ def test_full_size_layer(name):
     for n in ("da_gu", "db_gu", "da_d", "db_d"):
         if dead.size:
             assert float(layer.grads[n][torch.from_numpy(dead).cuda()].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("name", ["gpt-oss-20b", "qwen3-30b-a3b"])
+def test_full_size_full_fine_tuning(name):
+    """Base-weight gradients of full fine-tuning at full size, on sampled experts."""
+    import mixture_experts_lora_amd as mel
+    cfg = CONFIGS[name]
+    say(f"[fullsize full-ft] {name}")
+    inp = gpu_inputs(cfg, SEED)
+    layer = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=True)
+    layer.step(inp["x"], inp["logits"], inp["dy"], {n: inp[n] for n in WEIGHTS})
+    torch.cuda.synchronize()
+    tol = TOL[cfg.dtype]
+    counts = to_numpy(layer.counts)
+    offsets = to_numpy(layer.offsets)
+    sp = to_numpy(layer.sorted_pair)
+    wts = {n: ExpertSlices(inp[n]) for n in WEIGHTS}
+    wn = to_numpy(layer.topk_w)
+    nz = np.where(counts > 0)[0]
+    for e in sorted({int(nz[0]), int(nz[-1])}):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        pairs = sp[lo:hi]
+        toks = torch.from_numpy(pairs // cfg.k).cuda()
+        X_e = to_numpy(inp["x"][toks])
+        G_e = wn.reshape(-1)[pairs][:, None] * to_numpy(inp["dy"][toks])
+        we = {n: wts[n][e] for n in WEIGHTS}
+        f = oracle.expert_forward(X_e, **we, s=cfg.lora_scale)
+        b = oracle.expert_backward(X_e, G_e, f, **we, s=cfg.lora_scale, base_grads=True)
+        close(f"dw_gu[e={e}]", to_numpy(layer.base_grads["dw_gu"][e]), b["dw_gu"], tol)
+        close(f"dw_d[e={e}]", to_numpy(layer.base_grads["dw_d"][e]), b["dw_d"], tol)
+        say(f"  expert {e} ({hi - lo} rows) ok")

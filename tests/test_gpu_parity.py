@@ -71,6 +71,32 @@ def test_layer_matches_oracle(name, seed):
         assert (to_numpy(layer.grads[n])[dead] == 0).all()
 
 
+@pytest.mark.parametrize("name", ["tiny", "mini-bf16", "mini-skew", "mini-f32", "mini-k1",
+                                  "mini-renorm"])
+def test_full_fine_tuning_base_grads(name):
+    """Full fine-tuning: dW_gu and dW_d against the oracle; every other output
+    bit-identical to the LoRA-only backward."""
+    mel = _mel()
+    cfg = PARITY_CONFIGS[name]
+    say(f"[full-ft] {name}")
+    inp = gpu_inputs(cfg, 5)
+    full = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=True)
+    full.step(inp["x"], inp["logits"], inp["dy"], {n: inp[n] for n in WEIGHTS})
+    torch.cuda.synchronize()
+    h = {n: to_numpy(v) for n, v in inp.items()}
+    _, g, c = oracle.layer_forward_backward(h["x"], h["logits"], h["dy"], h, cfg.k, cfg.router,
+                                            cfg.lora_scale, base_grads=True)
+    tol = TOL[cfg.dtype]
+    dead = np.where(c["counts"] == 0)[0]
+    for n in ("dw_gu", "dw_d"):
+        close(n, to_numpy(full.base_grads[n]), g[n], tol)
+        assert (to_numpy(full.base_grads[n])[dead] == 0).all()
+    lora = run_gpu(mel.MoELoRALayer, mel.Shape.of(cfg), cfg, inp)
+    for a, b in [(full.dx, lora.dx), (full.d_logits, lora.d_logits)] + \
+            [(full.grads[n], lora.grads[n]) for n in lora.grads]:
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("name", ["mini-bf16", "mini-skew", "tiny"])
 def test_layer_is_deterministic(name):
     """Atomic-free kernels: two runs give bit-identical outputs."""
@@ -102,3 +128,24 @@ def test_autograd_function_matches_layer():
     assert torch.equal(lg.grad, layer.d_logits)
     for n in ("a_gu", "b_gu", "a_d", "b_d"):
         assert torch.equal(ps[n].grad, layer.grads["d" + n])
+    assert ps["w_gu"].grad is None and ps["w_d"].grad is None  # frozen: no base gradients
+
+
+def test_autograd_function_full_fine_tuning():
+    """With the base weights requiring grad, the autograd wrapper returns dW too."""
+    mel = _mel()
+    cfg = PARITY_CONFIGS["mini-bf16"]
+    say("[autograd full-ft] mini-bf16")
+    inp = gpu_inputs(cfg, 2)
+    full = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=True)
+    full.step(inp["x"], inp["logits"], inp["dy"], {n: inp[n] for n in WEIGHTS})
+    torch.cuda.synchronize()
+    x = inp["x"].clone().requires_grad_(True)
+    lg = inp["logits"].clone().requires_grad_(True)
+    ps = {n: inp[n].clone().requires_grad_(True) for n in WEIGHTS}
+    y = mel.MoELoRAFunction.apply(x, lg, *[ps[n] for n in WEIGHTS], cfg.router, cfg.k,
+                                  cfg.lora_scale)
+    y.backward(inp["dy"])
+    assert torch.equal(x.grad, full.dx)
+    assert torch.equal(ps["w_gu"].grad, full.base_grads["dw_gu"])
+    assert torch.equal(ps["w_d"].grad, full.base_grads["dw_d"])

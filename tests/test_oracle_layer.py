@@ -179,11 +179,11 @@ def test_backward_central_finite_differences(router):
     T, H, I, E, k, r, s = 8, 16, 8, 4, 2, 4, 1.5
     d = rand_layer(T, H, I, E, k, r, router, seed=13)
     _, g, _ = oracle.layer_forward_backward(d["x"], d["logits"], d["dy"], d, k, router, s,
-                                            np.float64)
+                                            np.float64, base_grads=True)
     rng = np.random.default_rng(0)
     h = 1e-6
     for name, gname in (("x", "dx"), ("a_gu", "da_gu"), ("b_gu", "db_gu"),
-                        ("a_d", "da_d"), ("b_d", "db_d")):
+                        ("a_d", "da_d"), ("b_d", "db_d"), ("w_gu", "dw_gu"), ("w_d", "dw_d")):
         # full element-wise FD on a few random coordinates plus one random direction
         base = d[name]
         flat_idx = rng.choice(base.size, size=min(12, base.size), replace=False)
@@ -246,7 +246,7 @@ def test_backward_matches_torch_autograd(router):
     T, H, I, E, k, r, s = 24, 32, 16, 6, 3, 5, 2.0
     d = rand_layer(T, H, I, E, k, r, router, seed=29)
     _, g, _ = oracle.layer_forward_backward(d["x"], d["logits"], d["dy"], d, k, router, s,
-                                            np.float64)
+                                            np.float64, base_grads=True)
     tp = {n: torch.tensor(d[n], dtype=torch.float64, requires_grad=True) for n in WNAMES}
     x = torch.tensor(d["x"], requires_grad=True)
     lg = torch.tensor(d["logits"].astype(np.float64), requires_grad=True)
@@ -254,6 +254,5 @@ def test_backward_matches_torch_autograd(router):
     (Y * torch.tensor(d["dy"])).sum().backward()
     np.testing.assert_allclose(g["dx"], x.grad.numpy(), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(g["dlogits"], lg.grad.numpy(), rtol=1e-9, atol=1e-12)
-    for n in ("a_gu", "b_gu", "a_d", "b_d"):
+    for n in ("a_gu", "b_gu", "a_d", "b_d", "w_gu", "w_d"):
         np.testing.assert_allclose(g["d" + n], tp[n].grad.numpy(), rtol=1e-10, atol=1e-12)
-    assert tp["w_gu"].grad is not None   # (frozen in the layer; torch still computes it)

@@ -53,6 +53,9 @@ MUTATIONS = [
      'dw[:, j] = np.einsum("th,th->t", dY, y_perm[pos[:, 0]])'),
     ("unpermute_weighted", 'dx = combine(dx_perm, cache["inv_pos"], None, T, k, dtype)',
      'dx = combine(dx_perm, cache["inv_pos"], cache["w"], T, k, dtype)'),
+    ("dw_gu_without_swiglu_derivative", 'out["dw_gu"] = dh.T @ X',
+     'out["dw_gu"] = np.concatenate([da, da], axis=1).T @ X'),
+    ("dw_d_scaled_by_lora_scale", 'out["dw_d"] = G.T @ a', 'out["dw_d"] = s * (G.T @ a)'),
 ]
 
 # Runs the pin tests with the oracle package taken from argv[1].
