@@ -37,7 +37,9 @@ PEAK_F32_TFLOPS = 157.3        # fp32 vector
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE-LoRA layer fwd+bwd TFLOP/s and tokens/s on 1 MI355X; % bf16 MFMA peak"
 
-GEMM_KERNELS = ("gate_up_fwd", "down_fwd", "down_bwd", "gate_up_bwd")
+GEMM_KERNELS = ("gate_up_fwd", "down_fwd", "down_bwd", "gate_up_bwd", "base_wgrad")
+METRIC_FULL_FT = ("MoE expert layer full fine-tuning fwd+bwd (LoRA plus base-weight gradients) "
+                  "TFLOP/s and tokens/s on 1 MI355X; % bf16 MFMA peak")
 
 
 def kernel_flops(name, cfg):
@@ -48,6 +50,7 @@ def kernel_flops(name, cfg):
         "down_fwd": 2 * N * H * (I + r),            # act W^T + U B^T over H outputs
         "down_bwd": 2 * N * I * (H + r),            # G W + GB A over I outputs
         "gate_up_bwd": 2 * N * H * (2 * I + r),     # dH W + dHB A over H outputs
+        "base_wgrad": 3 * N * H * I,                # mean of dW_d = G^T act (2NHI), dW_gu = dH^T X (4NHI)
     }[name]
 
 
@@ -142,7 +145,7 @@ def write_traffic(d, workload):
         print(json.dumps(rec))
 
 
-def cpu_baseline(cfg, inp, sample_tokens):
+def cpu_baseline(cfg, inp, sample_tokens, full_ft=False):
     import numpy as np
     import oracle
     from workloads.synth import to_numpy
@@ -158,12 +161,14 @@ def cpu_baseline(cfg, inp, sample_tokens):
     x, lg, dy = to_numpy(inp["x"][S]), to_numpy(inp["logits"][S]), to_numpy(inp["dy"][S])
     w = min(256, Ts)  # warm-up on a few tokens (BLAS threads, page faults)
     oracle.layer_forward_backward(x[:w], lg[:w], dy[:w], h, cfg.k, cfg.router, cfg.lora_scale,
-                                  np.float32)
+                                  np.float32, base_grads=full_ft)
     t0 = time.perf_counter()
-    oracle.layer_forward_backward(x, lg, dy, h, cfg.k, cfg.router, cfg.lora_scale, np.float32)
+    oracle.layer_forward_backward(x, lg, dy, h, cfg.k, cfg.router, cfg.lora_scale, np.float32,
+                                  base_grads=full_ft)
     dt = time.perf_counter() - t0
     sub = cfg.with_(T=Ts)
-    return {"value": round(sub.flops_fwd_bwd() / dt / 1e12, 4), "unit": "TFLOP/s",
+    flops = sub.flops_fwd_bwd() + (6 * sub.N * sub.H * sub.I if full_ft else 0)
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s",
             "cores": int(threads), "kind": "oracle",
             "seconds": round(dt, 3), "tokens_per_s": round(Ts / dt, 1),
             "sample": f"first {Ts} of {cfg.T} tokens of the same layer (same weights, routing "
@@ -183,6 +188,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB mebibytes device-to-device once (HBM counter calibration)")
+    ap.add_argument("--full-ft", action="store_true",
+                    help="full fine-tuning step: also the base-weight gradients (F += 6 N H I)")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
                     help="only write profiles/traffic_*.json from rocprofv3 counter runs in DIR")
     args = ap.parse_args()
@@ -215,7 +222,7 @@ def main():
     weights = {n: inp[n] for n in ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")}
     shape = mel.Shape.of(cfg)
     torch.cuda.reset_peak_memory_stats()
-    layer = mel.MoELoRALayer(shape, cfg.router)
+    layer = mel.MoELoRALayer(shape, cfg.router, full_ft=args.full_ft)
     for _ in range(args.warmup):
         layer.step(inp["x"], inp["logits"], inp["dy"], weights)
     torch.cuda.synchronize()
@@ -252,7 +259,7 @@ def main():
                          "ms_per_launch": round(tot / n, 4)}
     peak_bytes = torch.cuda.max_memory_allocated()
 
-    F = cfg.flops_fwd_bwd()
+    F = cfg.flops_fwd_bwd() + (6 * cfg.N * cfg.H * cfg.I if args.full_ft else 0)
     tflops = F / (ms / 1e3) / 1e12
     bf16 = cfg.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
@@ -271,13 +278,15 @@ def main():
             hbm[name] = {"bytes_per_launch": nb, "GB/s": round(gbs, 1),
                          "frac": round(gbs / PEAK_HBM_GBS, 4)}
     out = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC_FULL_FT if args.full_ft else METRIC, "value": round(tflops, 2),
+        "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "ms_median": round(step_ms[len(step_ms) // 2], 4), "ms_min": round(step_ms[0], 4),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
-        "config": {"workload": f"{cfg.name}-shaped MoE-LoRA expert layer fwd+bwd",
+        "config": {"workload": f"{cfg.name}-shaped MoE-LoRA expert layer fwd+bwd"
+                               + (", full fine-tuning" if args.full_ft else ""),
                    "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "r": cfg.r,
                    "router": cfg.router, "lora_scale": cfg.lora_scale, "seed": args.seed},
         "tokens_per_s": round(cfg.T / (ms / 1e3), 1),
@@ -289,7 +298,7 @@ def main():
         "kernels": kms,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens, args.full_ft)
     print(json.dumps(out), flush=True)
 
 
