@@ -188,6 +188,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB mebibytes device-to-device once (HBM counter calibration)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="activation-lean mode: h and act recomputed in the backward")
     ap.add_argument("--full-ft", action="store_true",
                     help="full fine-tuning step: also the base-weight gradients (F += 6 N H I)")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
@@ -222,7 +224,7 @@ def main():
     weights = {n: inp[n] for n in ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")}
     shape = mel.Shape.of(cfg)
     torch.cuda.reset_peak_memory_stats()
-    layer = mel.MoELoRALayer(shape, cfg.router, full_ft=args.full_ft)
+    layer = mel.MoELoRALayer(shape, cfg.router, full_ft=args.full_ft, recompute=args.recompute)
     for _ in range(args.warmup):
         layer.step(inp["x"], inp["logits"], inp["dy"], weights)
     torch.cuda.synchronize()
@@ -286,13 +288,15 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
         "config": {"workload": f"{cfg.name}-shaped MoE-LoRA expert layer fwd+bwd"
-                               + (", full fine-tuning" if args.full_ft else ""),
+                               + (", full fine-tuning" if args.full_ft else "")
+                               + (", h and act recomputed in backward" if args.recompute else ""),
                    "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "r": cfg.r,
                    "router": cfg.router, "lora_scale": cfg.lora_scale, "seed": args.seed},
         "tokens_per_s": round(cfg.T / (ms / 1e3), 1),
         "mfma_peak_frac": round(tflops / peak, 4),
         "flops_per_step": F,
         "peak_hbm_bytes": int(peak_bytes),
+        "saved_activation_bytes": int(layer.saved_bytes()),
         "roofline": roofline,
         "hbm": hbm,
         "kernels": kms,

@@ -210,6 +210,34 @@ moe_status moe_grouped_full_bwd(const moe_shape *shape, const void *dy_perm,
                                 const moe_base_grads *base, void *ws, size_t ws_bytes,
                                 void *stream);
 
+/* Activation-lean mode for long contexts (the faster-moe page claims longer
+ * contexts from lower memory in its introduction and gpt-oss benchmark
+ * section, and its usage example at the end of "Faster LoRA MoE training"
+ * turns on gradient checkpointing to cut memory): the forward keeps
+ * h and act in its own workspace instead of `saved`, and the backward
+ * recomputes them from x_perm and the saved u_gu with the same gate_up
+ * kernel, so only u_gu, u_d and y_exp are held between forward and backward
+ * (h [N, 2I] and act [N, I] are not). Outputs and gradients are bit-identical
+ * to the saving mode; the backward does one more gate_up GEMM.
+ *   moe_workspace_bytes_lean  workspace sizes of the two calls below
+ *   moe_grouped_lora_fwd_lean    as moe_grouped_lora_fwd; saved->h and
+ *                                saved->act are not used (may be NULL)
+ *   moe_grouped_lora_bwd_recompute  as moe_grouped_lora_bwd (base NULL) or
+ *                                moe_grouped_full_bwd (base non-NULL), from the
+ *                                lean forward's saved fields
+ * Same argument rules and errors as the saving-mode calls.  */
+moe_status moe_workspace_bytes_lean(const moe_shape *shape, size_t *fwd_ws, size_t *bwd_ws);
+moe_status moe_grouped_lora_fwd_lean(const moe_shape *shape, const void *x_perm,
+                                     const int32_t *offsets, const moe_weights *weights,
+                                     const moe_saved *saved, void *ws, size_t ws_bytes,
+                                     void *stream);
+moe_status moe_grouped_lora_bwd_recompute(const moe_shape *shape, const void *dy_perm,
+                                          const void *x_perm, const int32_t *offsets,
+                                          const moe_weights *weights, const moe_saved *saved,
+                                          void *dx_perm, const moe_lora_grads *grads,
+                                          const moe_base_grads *base, void *ws, size_t ws_bytes,
+                                          void *stream);
+
 const char *moe_status_str(moe_status status);
 
 /* Text of the last error raised on the calling thread ("" if none). */

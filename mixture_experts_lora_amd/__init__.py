@@ -27,7 +27,9 @@ from ._lib import MoeBaseGrads, MoeLoraGrads, MoeSaved, MoeShape, MoeWeights, RO
 __all__ = [
     "Shape", "moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
     "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
-    "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "kernel_timer", "ROUTER_IDS", "library_path",
+    "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_workspace_bytes_lean",
+    "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute", "kernel_timer", "ROUTER_IDS",
+    "library_path",
 ]
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -153,10 +155,12 @@ def _weights(shape: Shape, w: dict) -> MoeWeights:
         _ptr(w["a_d"], (E, r, I), dt, "a_d"), _ptr(w["b_d"], (E, H, r), dt, "b_d"))
 
 
-def _saved(shape: Shape, s: dict, need_y=True) -> MoeSaved:
+def _saved(shape: Shape, s: dict, need_y=True, lean=False) -> MoeSaved:
+    """lean: h and act are not part of `s` (activation-lean mode)."""
     N, H, I, r, dt = shape.N, shape.H, shape.I, shape.r, shape.torch_dtype
     return MoeSaved(
-        _ptr(s["h"], (N, 2 * I), dt, "h"), _ptr(s["act"], (N, I), dt, "act"),
+        _ptr(s.get("h"), (N, 2 * I), dt, "h", optional=lean),
+        _ptr(s.get("act"), (N, I), dt, "act", optional=lean),
         _ptr(s["u_gu"], (N, r), dt, "u_gu"), _ptr(s["u_d"], (N, r), dt, "u_d"),
         _ptr(s.get("y_exp"), (N, H), dt, "y_exp", optional=not need_y))
 
@@ -171,6 +175,27 @@ def moe_grouped_lora_fwd(shape: Shape, x_perm, offsets, weights: dict, saved: di
         ctypes.byref(shape.c()), _ptr(x_perm, (shape.N, shape.H), shape.torch_dtype, "x_perm"),
         _ptr(offsets, (shape.E + 1,), torch.int32, "offsets"), ctypes.byref(w), ctypes.byref(s),
         wsp, wsb, _stream(stream)), "moe_grouped_lora_fwd")
+
+
+def moe_workspace_bytes_lean(shape: Shape):
+    """(forward, backward) workspace bytes of the activation-lean calls."""
+    f, b = ctypes.c_size_t(), ctypes.c_size_t()
+    check(_lib.load().moe_workspace_bytes_lean(ctypes.byref(shape.c()), ctypes.byref(f),
+                                               ctypes.byref(b)), "moe_workspace_bytes_lean")
+    return f.value, b.value
+
+
+def moe_grouped_lora_fwd_lean(shape: Shape, x_perm, offsets, weights: dict, saved: dict, ws,
+                              stream=None):
+    """moe_grouped_lora_fwd that keeps h and act in `ws`; saved needs u_gu, u_d, y_exp."""
+    need, _ = moe_workspace_bytes_lean(shape)
+    wsp, wsb = _ws(ws, need, "ws")
+    w = _weights(shape, weights)
+    s = _saved(shape, saved, lean=True)
+    check(_lib.load().moe_grouped_lora_fwd_lean(
+        ctypes.byref(shape.c()), _ptr(x_perm, (shape.N, shape.H), shape.torch_dtype, "x_perm"),
+        _ptr(offsets, (shape.E + 1,), torch.int32, "offsets"), ctypes.byref(w), ctypes.byref(s),
+        wsp, wsb, _stream(stream)), "moe_grouped_lora_fwd_lean")
 
 
 def moe_unpermute_combine(shape: Shape, y_perm, inv_pos, topk_w, y, stream=None):
@@ -196,12 +221,12 @@ def moe_unpermute_combine_bwd(shape: Shape, dy, y_exp, inv_pos, topk_w, dy_perm,
 
 
 def _bwd_args(shape: Shape, dy_perm, x_perm, offsets, weights: dict, saved: dict, dx_perm,
-              grads: dict, ws):
-    _, need, _ = moe_workspace_bytes(shape)
+              grads: dict, ws, lean=False):
+    need = moe_workspace_bytes_lean(shape)[1] if lean else moe_workspace_bytes(shape)[1]
     wsp, wsb = _ws(ws, need, "ws")
     E, H, I, r, dt = shape.E, shape.H, shape.I, shape.r, shape.torch_dtype
     w = _weights(shape, weights)
-    s = _saved(shape, saved, need_y=False)
+    s = _saved(shape, saved, need_y=False, lean=lean)
     g = MoeLoraGrads(_ptr(grads["da_gu"], (E, r, H), dt, "da_gu"),
                      _ptr(grads["db_gu"], (E, 2 * I, r), dt, "db_gu"),
                      _ptr(grads["da_d"], (E, r, I), dt, "da_d"),
@@ -231,6 +256,23 @@ def moe_grouped_full_bwd(shape: Shape, dy_perm, x_perm, offsets, weights: dict, 
                      _ptr(base_grads["dw_d"], (E, H, I), dt, "dw_d"))
     check(_lib.load().moe_grouped_full_bwd(*head, ctypes.byref(b), wsp, wsb, _stream(stream)),
           "moe_grouped_full_bwd")
+
+
+def moe_grouped_lora_bwd_recompute(shape: Shape, dy_perm, x_perm, offsets, weights: dict,
+                                   saved: dict, dx_perm, grads: dict, ws, base_grads=None,
+                                   stream=None):
+    """Backward of the activation-lean forward: recomputes h and act in `ws`.
+    base_grads (dw_gu, dw_d) optional: full fine-tuning."""
+    head, keep, wsp, wsb = _bwd_args(shape, dy_perm, x_perm, offsets, weights, saved, dx_perm,
+                                     grads, ws, lean=True)
+    b = None
+    if base_grads is not None:
+        E, H, I, dt = shape.E, shape.H, shape.I, shape.torch_dtype
+        b = MoeBaseGrads(_ptr(base_grads["dw_gu"], (E, 2 * I, H), dt, "dw_gu"),
+                         _ptr(base_grads["dw_d"], (E, H, I), dt, "dw_d"))
+    check(_lib.load().moe_grouped_lora_bwd_recompute(
+        *head, ctypes.byref(b) if b is not None else None, wsp, wsb, _stream(stream)),
+        "moe_grouped_lora_bwd_recompute")
 
 
 class kernel_timer:

@@ -17,7 +17,9 @@ KERNEL_IDS = {"route": 0, "permute": 1, "gather": 2, "gate_up_fwd": 3, "down_fwd
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
            "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
-           "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_status_str", "moe_last_error",
+           "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_workspace_bytes_lean",
+           "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute", "moe_status_str",
+           "moe_last_error",
            "moe_kernel_timer_enable", "moe_kernel_timer_reset", "moe_kernel_timer_read")
 
 
@@ -75,6 +77,22 @@ def load() -> ctypes.CDLL:
         "moe_grouped_lora_bwd": (st, [ctypes.POINTER(MoeShape), P, P, P,
                                       ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeSaved), P,
                                       ctypes.POINTER(MoeLoraGrads), P, ctypes.c_size_t, P]),
+        "moe_grouped_full_bwd": (st, [ctypes.POINTER(MoeShape), P, P, P,
+                                      ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeSaved), P,
+                                      ctypes.POINTER(MoeLoraGrads), ctypes.POINTER(MoeBaseGrads),
+                                      P, ctypes.c_size_t, P]),
+        "moe_workspace_bytes_lean": (st, [ctypes.POINTER(MoeShape),
+                                          ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_grouped_lora_fwd_lean": (st, [ctypes.POINTER(MoeShape), P, P,
+                                           ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeSaved),
+                                           P, ctypes.c_size_t, P]),
+        "moe_grouped_lora_bwd_recompute": (st, [ctypes.POINTER(MoeShape), P, P, P,
+                                                ctypes.POINTER(MoeWeights),
+                                                ctypes.POINTER(MoeSaved), P,
+                                                ctypes.POINTER(MoeLoraGrads),
+                                                ctypes.POINTER(MoeBaseGrads), P, ctypes.c_size_t,
+                                                P]),
         "moe_status_str": (ctypes.c_char_p, [st]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_kernel_timer_enable": (st, [I32]),
@@ -82,6 +100,8 @@ def load() -> ctypes.CDLL:
         "moe_kernel_timer_read": (st, [I32, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int32)]),
     }
+    # every export gets an explicit signature (sizes are 64-bit size_t)
+    assert set(sig) == set(EXPORTS), sorted(set(EXPORTS) ^ set(sig))
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype = res

@@ -155,6 +155,15 @@ moe_status moe_workspace_bytes(const moe_shape* shape, size_t* fwd_ws, size_t* b
   return MOE_OK;
 }
 
+moe_status moe_workspace_bytes_lean(const moe_shape* shape, size_t* fwd_ws, size_t* bwd_ws) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe::ExpertDims d = dims_of(shape);
+  if (fwd_ws) *fwd_ws = moe::experts_fwd_lean_ws_bytes(d);
+  if (bwd_ws) *bwd_ws = moe::experts_bwd_lean_ws_bytes(d);
+  return MOE_OK;
+}
+
 moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t router,
                      int32_t* topk_ids, float* topk_w, void* stream) {
   moe_status st = check_routing_dims(T, E, k);
@@ -217,10 +226,11 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, const vo
   return MOE_OK;
 }
 
-moe_status moe_grouped_lora_fwd(const moe_shape* shape, const void* x_perm,
-                                const int32_t* offsets, const moe_weights* weights,
-                                const moe_saved* saved, void* ws, size_t ws_bytes,
-                                void* stream) {
+namespace {
+
+moe_status grouped_fwd(const char* name, bool lean, const moe_shape* shape, const void* x_perm,
+                       const int32_t* offsets, const moe_weights* weights, const moe_saved* saved,
+                       void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   CHECK_PTR(x_perm);
@@ -233,21 +243,43 @@ moe_status moe_grouped_lora_fwd(const moe_shape* shape, const void* x_perm,
   CHECK_PTR(weights->w_d);
   CHECK_PTR(weights->a_d);
   CHECK_PTR(weights->b_d);
-  CHECK_PTR(saved->h);
-  CHECK_PTR(saved->act);
+  if (!lean) {
+    CHECK_PTR(saved->h);
+    CHECK_PTR(saved->act);
+  }
   CHECK_PTR(saved->u_gu);
   CHECK_PTR(saved->u_d);
   CHECK_PTR(saved->y_exp);
   CHECK_PTR(ws);
   const moe::ExpertDims d = dims_of(shape);
-  const size_t need = moe::experts_fwd_ws_bytes(d);
+  const size_t need = lean ? moe::experts_fwd_lean_ws_bytes(d) : moe::experts_fwd_ws_bytes(d);
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "forward workspace needs " + std::to_string(need) + " bytes");
-  if (saved->h == x_perm || saved->y_exp == x_perm || saved->act == x_perm)
+  if ((!lean && (saved->h == x_perm || saved->act == x_perm)) || saved->y_exp == x_perm)
     return fail(MOE_ERR_INVALID_ARG, "a saved activation aliases x_perm");
-  hipError_t e = moe::launch_experts_fwd(d, x_perm, offsets, *weights, *saved, ws,
-                                         as_stream(stream), moe::active_timer());
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_lora_fwd");
+  hipError_t e = lean ? moe::launch_experts_fwd_lean(d, x_perm, offsets, *weights, *saved, ws,
+                                                     as_stream(stream), moe::active_timer())
+                      : moe::launch_experts_fwd(d, x_perm, offsets, *weights, *saved, ws,
+                                                as_stream(stream), moe::active_timer());
+  return e == hipSuccess ? MOE_OK : hip_fail(e, name);
+}
+
+}  // namespace
+
+moe_status moe_grouped_lora_fwd(const moe_shape* shape, const void* x_perm,
+                                const int32_t* offsets, const moe_weights* weights,
+                                const moe_saved* saved, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return grouped_fwd("moe_grouped_lora_fwd", false, shape, x_perm, offsets, weights, saved, ws,
+                     ws_bytes, stream);
+}
+
+moe_status moe_grouped_lora_fwd_lean(const moe_shape* shape, const void* x_perm,
+                                     const int32_t* offsets, const moe_weights* weights,
+                                     const moe_saved* saved, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  return grouped_fwd("moe_grouped_lora_fwd_lean", true, shape, x_perm, offsets, weights, saved,
+                     ws, ws_bytes, stream);
 }
 
 moe_status moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
@@ -286,10 +318,11 @@ moe_status moe_unpermute_combine_bwd(const moe_shape* shape, const void* dy,
 
 namespace {
 
-moe_status grouped_bwd(const char* name, const moe_shape* shape, const void* dy_perm,
-                       const void* x_perm, const int32_t* offsets, const moe_weights* weights,
-                       const moe_saved* saved, void* dx_perm, const moe_lora_grads* grads,
-                       const moe_base_grads* base, void* ws, size_t ws_bytes, void* stream) {
+moe_status grouped_bwd(const char* name, bool lean, const moe_shape* shape,
+                       const void* dy_perm, const void* x_perm, const int32_t* offsets,
+                       const moe_weights* weights, const moe_saved* saved, void* dx_perm,
+                       const moe_lora_grads* grads, const moe_base_grads* base, void* ws,
+                       size_t ws_bytes, void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   CHECK_PTR(dy_perm);
@@ -305,8 +338,10 @@ moe_status grouped_bwd(const char* name, const moe_shape* shape, const void* dy_
   CHECK_PTR(weights->w_d);
   CHECK_PTR(weights->a_d);
   CHECK_PTR(weights->b_d);
-  CHECK_PTR(saved->h);
-  CHECK_PTR(saved->act);
+  if (!lean) {
+    CHECK_PTR(saved->h);
+    CHECK_PTR(saved->act);
+  }
   CHECK_PTR(saved->u_gu);
   CHECK_PTR(saved->u_d);
   CHECK_PTR(grads->da_gu);
@@ -320,7 +355,8 @@ moe_status grouped_bwd(const char* name, const moe_shape* shape, const void* dy_
     CHECK_PTR(base->dw_gu);
     CHECK_PTR(base->dw_d);
     const void* outs[] = {dx_perm, grads->da_gu, grads->db_gu, grads->da_d, grads->db_d};
-    const void* ins[] = {dy_perm, x_perm, saved->act, saved->h, weights->w_gu, weights->w_d};
+    const void* ins[] = {dy_perm, x_perm, weights->w_gu, weights->w_d, lean ? nullptr : saved->act,
+                         lean ? nullptr : saved->h};
     for (const void* b : {static_cast<const void*>(base->dw_gu), static_cast<const void*>(base->dw_d)}) {
       for (const void* o : outs)
         if (b == o) return fail(MOE_ERR_INVALID_ARG, "a base gradient aliases another output");
@@ -331,12 +367,15 @@ moe_status grouped_bwd(const char* name, const moe_shape* shape, const void* dy_
       return fail(MOE_ERR_INVALID_ARG, "dw_gu and dw_d alias");
   }
   const moe::ExpertDims d = dims_of(shape);
-  const size_t need = moe::experts_bwd_ws_bytes(d);
+  const size_t need = lean ? moe::experts_bwd_lean_ws_bytes(d) : moe::experts_bwd_ws_bytes(d);
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "backward workspace needs " + std::to_string(need) + " bytes");
-  hipError_t e = moe::launch_experts_bwd(d, dy_perm, x_perm, offsets, *weights, *saved, dx_perm,
-                                         *grads, base, ws, as_stream(stream),
-                                         moe::active_timer());
+  hipError_t e =
+      lean ? moe::launch_experts_bwd_recompute(d, dy_perm, x_perm, offsets, *weights, *saved,
+                                               dx_perm, *grads, base, ws, as_stream(stream),
+                                               moe::active_timer())
+           : moe::launch_experts_bwd(d, dy_perm, x_perm, offsets, *weights, *saved, dx_perm,
+                                     *grads, base, ws, as_stream(stream), moe::active_timer());
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
 }
 
@@ -347,8 +386,8 @@ moe_status moe_grouped_lora_bwd(const moe_shape* shape, const void* dy_perm,
                                 const moe_weights* weights, const moe_saved* saved,
                                 void* dx_perm, const moe_lora_grads* grads, void* ws,
                                 size_t ws_bytes, void* stream) {
-  return grouped_bwd("moe_grouped_lora_bwd", shape, dy_perm, x_perm, offsets, weights, saved,
-                     dx_perm, grads, nullptr, ws, ws_bytes, stream);
+  return grouped_bwd("moe_grouped_lora_bwd", false, shape, dy_perm, x_perm, offsets, weights,
+                     saved, dx_perm, grads, nullptr, ws, ws_bytes, stream);
 }
 
 moe_status moe_grouped_full_bwd(const moe_shape* shape, const void* dy_perm,
@@ -358,8 +397,18 @@ moe_status moe_grouped_full_bwd(const moe_shape* shape, const void* dy_perm,
                                 const moe_base_grads* base, void* ws, size_t ws_bytes,
                                 void* stream) {
   CHECK_PTR(base);
-  return grouped_bwd("moe_grouped_full_bwd", shape, dy_perm, x_perm, offsets, weights, saved,
-                     dx_perm, grads, base, ws, ws_bytes, stream);
+  return grouped_bwd("moe_grouped_full_bwd", false, shape, dy_perm, x_perm, offsets, weights,
+                     saved, dx_perm, grads, base, ws, ws_bytes, stream);
+}
+
+moe_status moe_grouped_lora_bwd_recompute(const moe_shape* shape, const void* dy_perm,
+                                          const void* x_perm, const int32_t* offsets,
+                                          const moe_weights* weights, const moe_saved* saved,
+                                          void* dx_perm, const moe_lora_grads* grads,
+                                          const moe_base_grads* base, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  return grouped_bwd("moe_grouped_lora_bwd_recompute", true, shape, dy_perm, x_perm, offsets,
+                     weights, saved, dx_perm, grads, base, ws, ws_bytes, stream);
 }
 
 moe_status moe_kernel_timer_enable(int32_t on) {

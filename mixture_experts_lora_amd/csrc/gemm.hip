@@ -1341,6 +1341,53 @@ size_t experts_bwd_ws_bytes(const ExpertDims& d) {
   return b;
 }
 
+namespace {
+
+// h = X W_gu^T + u_gu B_gu^T ; act = SwiGLU(h)   (tile lists already built)
+hipError_t launch_gate_up(const ExpertDims& d, const WsLayout& L, const void* x_perm,
+                          const int32_t* offsets, const moe_weights& w, const void* u_gu,
+                          void* h, void* act, hipStream_t s, KernelTimer* tm) {
+  const int H = d.H, I = d.I, r = d.r;
+  GemmArgs a = base_args(d, offsets, L.big);
+  a.a[0] = opnd(x_perm, 0, H, 1, true);
+  a.b[0] = opnd(w.w_gu, static_cast<int64_t>(2) * I * H, H, 1, true);
+  a.a[1] = opnd(u_gu, 0, r, 1, r % 8 == 0);
+  a.b[1] = opnd(w.b_gu, static_cast<int64_t>(2) * I * r, r, 1, r % 8 == 0);
+  a.K[0] = H;
+  a.K[1] = r;
+  a.N = 2 * I;
+  a.out = h;
+  a.ld_out = 2 * I;
+  a.out2 = act;
+  a.ld_out2 = I;
+  TimedScope ts(tm, MOE_K_GATE_UP_FWD, s);
+  if (d.dtype == MOE_BF16) {
+    a.ntn = ceil_div(I, 128);
+    return launch_big<GROUP_M, EPI_SWIGLU, true, true, true>(gm_grid(d, L.big, a.ntn), a, s,
+                                                              L.big.bm);
+  }
+  a.ntn = ceil_div(I, 64);
+  return launch(gemm_f32<GROUP_M, EPI_SWIGLU, true>, gm_grid(d, L.big, a.ntn), a, s);
+}
+
+// Recompute mode: h [N, 2I] and act [N, I] live in scratch after `base_bytes`.
+inline size_t lean_extra_bytes(const ExpertDims& d) {
+  const size_t esz = d.dtype == MOE_BF16 ? 2 : 4;
+  return align_up(static_cast<size_t>(d.N) * 2 * d.I * esz) +
+         align_up(static_cast<size_t>(d.N) * d.I * esz);
+}
+
+inline moe_saved lean_saved(const ExpertDims& d, const moe_saved& sv, void* ws, size_t base_bytes) {
+  const size_t esz = d.dtype == MOE_BF16 ? 2 : 4;
+  moe_saved out = sv;
+  char* p = static_cast<char*>(ws) + align_up(base_bytes);
+  out.h = p;
+  out.act = p + align_up(static_cast<size_t>(d.N) * 2 * d.I * esz);
+  return out;
+}
+
+}  // namespace
+
 hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int32_t* offsets,
                               const moe_weights& w, const moe_saved& sv, void* ws,
                               hipStream_t s, KernelTimer* tm) {
@@ -1352,29 +1399,7 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
     MOE_TRY(side_product(d, offsets, L, x_perm, H, w.a_gu, static_cast<int64_t>(r) * H, 1,
                          sv.u_gu, s));
   }
-  {  // h = X W_gu^T + u_gu B_gu^T ; act = SwiGLU(h)
-    GemmArgs a = base_args(d, offsets, L.big);
-    a.a[0] = opnd(x_perm, 0, H, 1, true);
-    a.b[0] = opnd(w.w_gu, static_cast<int64_t>(2) * I * H, H, 1, true);
-    a.a[1] = opnd(sv.u_gu, 0, r, 1, r % 8 == 0);
-    a.b[1] = opnd(w.b_gu, static_cast<int64_t>(2) * I * r, r, 1, r % 8 == 0);
-    a.K[0] = H;
-    a.K[1] = r;
-    a.N = 2 * I;
-    a.out = sv.h;
-    a.ld_out = 2 * I;
-    a.out2 = sv.act;
-    a.ld_out2 = I;
-    TimedScope ts(tm, MOE_K_GATE_UP_FWD, s);
-    if (d.dtype == MOE_BF16) {
-      a.ntn = ceil_div(I, 128);
-      MOE_TRY((launch_big<GROUP_M, EPI_SWIGLU, true, true, true>( gm_grid(d, L.big, a.ntn),
-                     a, s, L.big.bm)));
-    } else {
-      a.ntn = ceil_div(I, 64);
-      MOE_TRY(launch(gemm_f32<GROUP_M, EPI_SWIGLU, true>, gm_grid(d, L.big, a.ntn), a, s));
-    }
-  }
+  MOE_TRY(launch_gate_up(d, L, x_perm, offsets, w, sv.u_gu, sv.h, sv.act, s, tm));
   {  // u_d = s act A_d^T
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
     MOE_TRY(side_product(d, offsets, L, sv.act, I, w.a_d, static_cast<int64_t>(r) * I, 1,
@@ -1492,6 +1517,34 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     MOE_TRY(weight_grad(d, offsets, dh, 2 * I, x_perm, H, base->dw_gu, s));
   }
   return hipSuccess;
+}
+
+size_t experts_fwd_lean_ws_bytes(const ExpertDims& d) {
+  return align_up(experts_fwd_ws_bytes(d)) + lean_extra_bytes(d);
+}
+
+size_t experts_bwd_lean_ws_bytes(const ExpertDims& d) {
+  return align_up(experts_bwd_ws_bytes(d)) + lean_extra_bytes(d);
+}
+
+hipError_t launch_experts_fwd_lean(const ExpertDims& d, const void* x_perm,
+                                   const int32_t* offsets, const moe_weights& w,
+                                   const moe_saved& sv, void* ws, hipStream_t s,
+                                   KernelTimer* tm) {
+  const moe_saved full = lean_saved(d, sv, ws, experts_fwd_ws_bytes(d));
+  return launch_experts_fwd(d, x_perm, offsets, w, full, ws, s, tm);
+}
+
+hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, const void* x_perm,
+                                        const int32_t* offsets, const moe_weights& w,
+                                        const moe_saved& sv, void* dx_perm,
+                                        const moe_lora_grads& gr, const moe_base_grads* base,
+                                        void* ws, hipStream_t s, KernelTimer* tm) {
+  const moe_saved full = lean_saved(d, sv, ws, experts_bwd_ws_bytes(d));
+  const WsLayout L = tile_ws(ws, d);
+  MOE_TRY(build_tiles(L, offsets, d.E, s));
+  MOE_TRY(launch_gate_up(d, L, x_perm, offsets, w, sv.u_gu, full.h, full.act, s, tm));
+  return launch_experts_bwd(d, g, x_perm, offsets, w, full, dx_perm, gr, base, ws, s, tm);
 }
 
 }  // namespace moe

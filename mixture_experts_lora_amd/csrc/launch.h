@@ -73,4 +73,18 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
                               const moe_base_grads* base, void* ws, hipStream_t s,
                               KernelTimer* tm);
 
+// Recompute (activation-lean) mode: the forward keeps h and act in its
+// workspace instead of `saved`; the backward recomputes them into its own.
+size_t experts_fwd_lean_ws_bytes(const ExpertDims& d);
+size_t experts_bwd_lean_ws_bytes(const ExpertDims& d);
+hipError_t launch_experts_fwd_lean(const ExpertDims& d, const void* x_perm,
+                                   const int32_t* offsets, const moe_weights& w,
+                                   const moe_saved& sv, void* ws, hipStream_t s,
+                                   KernelTimer* tm);
+hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, const void* x_perm,
+                                        const int32_t* offsets, const moe_weights& w,
+                                        const moe_saved& sv, void* dx_perm,
+                                        const moe_lora_grads& gr, const moe_base_grads* base,
+                                        void* ws, hipStream_t s, KernelTimer* tm);
+
 }  // namespace moe

@@ -117,6 +117,46 @@ def test_short_workspace_rejected(lib):
                                     None) == 3
 
 
+def test_full_ft_and_lean_entry_points_validate(lib):
+    """The full fine-tuning and activation-lean calls check their extra
+    arguments (and workspace sizes) before anything is launched."""
+    P = ctypes.c_void_p
+    fake = P(0x10000)
+    sh = shape()
+    from mixture_experts_lora_amd._lib import MoeBaseGrads, MoeLoraGrads, MoeSaved, MoeWeights
+    w = MoeWeights(*(0x10000,) * 6)
+    sv = MoeSaved(*(0x30000 + i * 0x1000 for i in range(5)))
+    g = MoeLoraGrads(*(0x50000 + i * 0x1000 for i in range(4)))
+    _, f, b, _ = ws(lib, sh)
+    fl, bl = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.moe_workspace_bytes_lean(ctypes.byref(sh), ctypes.byref(fl), ctypes.byref(bl)) == 0
+    # the lean calls hold h [N, 2I] and act [N, I] in their workspaces
+    extra = sh.T * sh.k * 3 * sh.I * 2
+    assert fl.value >= f + extra and bl.value >= b + extra
+    args = (ctypes.byref(sh), fake, P(0x60000), fake, ctypes.byref(w), ctypes.byref(sv),
+            P(0x70000), ctypes.byref(g))
+    # full fine-tuning: base grads required, not aliased
+    assert lib.moe_grouped_full_bwd(*args, None, fake, 1 << 40, None) == 1
+    assert lib.moe_grouped_full_bwd(*args, ctypes.byref(MoeBaseGrads(0x80000, None)), fake,
+                                    1 << 40, None) == 1
+    assert lib.moe_grouped_full_bwd(*args, ctypes.byref(MoeBaseGrads(0x80000, 0x80000)), fake,
+                                    1 << 40, None) == 1
+    assert lib.moe_grouped_full_bwd(*args, ctypes.byref(MoeBaseGrads(0x80000, 0x70000)), fake,
+                                    1 << 40, None) == 1          # dw_d aliases dx_perm
+    assert lib.moe_grouped_full_bwd(*args, ctypes.byref(MoeBaseGrads(0x80000, 0x90000)), fake,
+                                    b - 1, None) == 3
+    # lean mode: h and act may be NULL; the larger workspace is required
+    lean = MoeSaved(None, None, 0x30000, 0x31000, 0x32000)
+    assert lib.moe_grouped_lora_fwd_lean(ctypes.byref(sh), fake, fake, ctypes.byref(w),
+                                         ctypes.byref(lean), fake, fl.value - 1, None) == 3
+    assert lib.moe_grouped_lora_fwd(ctypes.byref(sh), fake, fake, ctypes.byref(w),
+                                    ctypes.byref(lean), fake, 1 << 40, None) == 1
+    assert lib.moe_grouped_lora_bwd_recompute(ctypes.byref(sh), fake, P(0x60000), fake,
+                                              ctypes.byref(w), ctypes.byref(lean), P(0x70000),
+                                              ctypes.byref(g), None, fake, bl.value - 1,
+                                              None) == 3
+
+
 def test_aliasing_rejected(lib):
     P = ctypes.c_void_p
     fake = P(0x10000)

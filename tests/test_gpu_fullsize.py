@@ -113,3 +113,25 @@ def test_full_size_full_fine_tuning(name):
         close(f"dw_gu[e={e}]", to_numpy(layer.base_grads["dw_gu"][e]), b["dw_gu"], tol)
         close(f"dw_d[e={e}]", to_numpy(layer.base_grads["dw_d"][e]), b["dw_d"], tol)
         say(f"  expert {e} ({hi - lo} rows) ok")
+
+
+def test_full_size_recompute_long_context():
+    """Activation-lean mode at the long-context size: bit-identical to the
+    saving mode, with h and act no longer held between forward and backward."""
+    import mixture_experts_lora_amd as mel
+    cfg = CONFIGS["gpt-oss-20b-long"]
+    say(f"[fullsize recompute] {cfg.name} T={cfg.T}")
+    inp = gpu_inputs(cfg, SEED)
+    w = {n: inp[n] for n in WEIGHTS}
+    b = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, recompute=True)
+    b.step(inp["x"], inp["logits"], inp["dy"], w)
+    torch.cuda.synchronize()
+    a = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router)
+    a.step(inp["x"], inp["logits"], inp["dy"], w)
+    torch.cuda.synchronize()
+    saved_a, saved_b = a.saved_bytes(), b.saved_bytes()
+    say(f"  saved bytes: {saved_a / 1e9:.2f} GB -> {saved_b / 1e9:.2f} GB")
+    assert saved_a - saved_b == cfg.N * 3 * cfg.I * 2
+    for t1, t2 in [(a.y, b.y), (a.dx, b.dx), (a.d_logits, b.d_logits)] + \
+            [(a.grads[n], b.grads[n]) for n in a.grads]:
+        assert torch.equal(t1, t2)

@@ -97,6 +97,32 @@ def test_full_fine_tuning_base_grads(name):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["tiny", "mini-bf16", "mini-skew", "mini-r1", "mini-f32"])
+@pytest.mark.parametrize("full_ft", [False, True])
+def test_recompute_mode_is_bit_identical(name, full_ft):
+    """Activation-lean mode (h and act recomputed in the backward by the same
+    kernel): every output and gradient equals the saving mode's bit for bit."""
+    mel = _mel()
+    cfg = PARITY_CONFIGS[name]
+    say(f"[recompute] {name} full_ft={full_ft}")
+    inp = gpu_inputs(cfg, 7)
+    w = {n: inp[n] for n in WEIGHTS}
+    a = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=full_ft)
+    b = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=full_ft, recompute=True)
+    a.step(inp["x"], inp["logits"], inp["dy"], w)
+    b.step(inp["x"], inp["logits"], inp["dy"], w)
+    torch.cuda.synchronize()
+    assert "h" not in b.saved and "act" not in b.saved
+    assert b.saved_bytes() < a.saved_bytes()
+    pairs = [(a.y, b.y), (a.dx, b.dx), (a.d_logits, b.d_logits), (a.saved["y_exp"], b.saved["y_exp"]),
+             (a.saved["u_gu"], b.saved["u_gu"]), (a.saved["u_d"], b.saved["u_d"])]
+    pairs += [(a.grads[n], b.grads[n]) for n in a.grads]
+    if full_ft:
+        pairs += [(a.base_grads[n], b.base_grads[n]) for n in a.base_grads]
+    for t1, t2 in pairs:
+        assert torch.equal(t1, t2)
+
+
 @pytest.mark.parametrize("name", ["mini-bf16", "mini-skew", "tiny"])
 def test_layer_is_deterministic(name):
     """Atomic-free kernels: two runs give bit-identical outputs."""
