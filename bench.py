@@ -66,7 +66,29 @@ def kernel_bytes(name, cfg):
         "combine_bwd": T * H * es + 2 * N * H * es + N * 12,  # dY, Yexp in; G out; idx, w, dw
         "route_bwd": 2 * T * E * 4 + T * k * 8,                # logits in, dlogits out; ids, dw
         "unpermute": N * H * es + T * H * es + N * 4,         # dX_perm in, dX out, inv_pos
+        "router_fwd": T * H * es + E * H * es + T * E * 4,    # x, W_r in; logits out
+        "router_bwd": T * E * 4 + E * H * es + 2 * T * H * es,  # dlogits, W_r in; dx in and out
+        "accumulate": 3 * T * H * es,                          # src, dst in; dst out
     }.get(name)
+
+
+def block_parts(cfg, shared_I):
+    """(routed layer, shared expert as a one-expert k = 1 layer or None)."""
+    return cfg, (cfg.with_(name=cfg.name + "-shared", E=1, k=1, I=shared_I) if shared_I else None)
+
+
+def step_flops(cfg, full_ft, shared_I=None, block=False):
+    """Algorithmic FLOPs of one step: the routed layer, plus in block mode the
+    router projection (2 T E H forward, 2 T E H for dx) and the shared expert
+    (the layer formula with E = 1, k = 1, width shared_I)."""
+    routed, shared = block_parts(cfg, shared_I)
+    F = 0
+    for c in (routed, shared) if block else (routed,):
+        if c is not None:
+            F += c.flops_fwd_bwd() + (6 * c.N * c.H * c.I if full_ft else 0)
+    if block:
+        F += 4 * cfg.T * cfg.E * cfg.H
+    return F
 
 
 def source_hash():
@@ -97,8 +119,8 @@ def classify_gemm(kernel_name):
         return None
     a = [x.strip() for x in m.group(1).split(",")]
     bm, bn, mode, epi, b_kc = int(a[0]), int(a[1]), int(a[7]), int(a[8]), a[11] == "true"
-    if mode != 0 or bn < 128:
-        return None  # LoRA side products and weight gradients
+    if mode != 0 or bn < 128 or epi > 2:
+        return None  # LoRA side products, weight gradients, router projection
     if epi == 1:
         return "gate_up_fwd"
     if epi == 2:
@@ -145,16 +167,44 @@ def write_traffic(d, workload):
         print(json.dumps(rec))
 
 
+def cpu_baseline_block(cfg, inp, sample_tokens, shared_I):
+    """The oracle of the whole block (router projection, routed experts, shared
+    expert) on the first sample_tokens tokens."""
+    import numpy as np
+    import oracle
+    from workloads.synth import to_numpy
+    names = ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")
+    Ts = min(sample_tokens, cfg.T)
+    h = {n: to_numpy(inp[n]) for n in names}
+    sh = {n: to_numpy(inp["shared_" + n]) for n in names} if shared_I else None
+    x, dy, w_r = to_numpy(inp["x"][:Ts]), to_numpy(inp["dy"][:Ts]), to_numpy(inp["w_r"])
+    w = min(256, Ts)
+    oracle.layer_with_router_and_shared(x[:w], w_r, dy[:w], h, sh, cfg.k, cfg.router,
+                                        cfg.lora_scale)
+    t0 = time.perf_counter()
+    oracle.layer_with_router_and_shared(x, w_r, dy, h, sh, cfg.k, cfg.router, cfg.lora_scale)
+    dt = time.perf_counter() - t0
+    flops = step_flops(cfg.with_(T=Ts), False, shared_I, block=True)
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": _blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 3), "tokens_per_s": round(Ts / dt, 1),
+            "sample": f"first {Ts} of {cfg.T} tokens of the same block (router projection, "
+                      f"routed experts, shared expert), NumPy float32, forward+backward"}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()
+                        if i.get("user_api") == "blas"] or [1]))
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
 def cpu_baseline(cfg, inp, sample_tokens, full_ft=False):
     import numpy as np
     import oracle
     from workloads.synth import to_numpy
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads = _blas_threads()
     Ts = min(sample_tokens, cfg.T)
     S = slice(0, Ts)
     h = {n: to_numpy(inp[n]) for n in ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")}
@@ -192,6 +242,11 @@ def main():
                     help="activation-lean mode: h and act recomputed in the backward")
     ap.add_argument("--full-ft", action="store_true",
                     help="full fine-tuning step: also the base-weight gradients (F += 6 N H I)")
+    ap.add_argument("--block", action="store_true",
+                    help="whole MoE block: router projection from hidden states, routed "
+                         "experts, and a shared expert (width --shared-I)")
+    ap.add_argument("--shared-I", type=int, default=None,
+                    help="shared expert width in --block mode (default I; 0: none)")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
                     help="only write profiles/traffic_*.json from rocprofv3 counter runs in DIR")
     args = ap.parse_args()
@@ -216,17 +271,39 @@ def main():
                           "source_hash": source_hash()}))
         return
     import mixture_experts_lora_amd as mel
-    from workloads import BENCH_CONFIG, get_config, make_inputs
+    from workloads import BENCH_CONFIG, get_config, make_block_inputs, make_inputs
 
     cfg = get_config(args.config or BENCH_CONFIG)
     torch.cuda.set_device(0)
-    inp = make_inputs(cfg, args.seed, device="cuda")
-    weights = {n: inp[n] for n in ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")}
+    names = ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")
     shape = mel.Shape.of(cfg)
+    shared_I = None
+    if args.block:
+        shared_I = cfg.I if args.shared_I is None else (args.shared_I or None)
+        inp = make_block_inputs(cfg, args.seed, device="cuda", shared_I=shared_I)
+        sw = {n: inp["shared_" + n] for n in names} if shared_I else None
+    else:
+        inp = make_inputs(cfg, args.seed, device="cuda")
+    weights = {n: inp[n] for n in names}
     torch.cuda.reset_peak_memory_stats()
-    layer = mel.MoELoRALayer(shape, cfg.router, full_ft=args.full_ft, recompute=args.recompute)
+    if args.block:
+        layer = mel.MoELoRABlock(shape, cfg.router, shared_I, full_ft=args.full_ft,
+                                 recompute=args.recompute)
+        step = lambda: layer.step(inp["x"], inp["w_r"], inp["dy"], weights, sw)  # noqa: E731
+        fwd = lambda: layer.forward(inp["x"], inp["w_r"], weights, sw)  # noqa: E731
+        bwd = lambda: layer.backward(inp["dy"], inp["x"], inp["w_r"], weights, sw)  # noqa: E731
+        saved = layer.routed.saved_bytes() + (
+            sum(v.numel() * v.element_size() for v in layer.shared.saved.values())
+            if layer.shared is not None else 0)
+    else:
+        layer = mel.MoELoRALayer(shape, cfg.router, full_ft=args.full_ft,
+                                 recompute=args.recompute)
+        step = lambda: layer.step(inp["x"], inp["logits"], inp["dy"], weights)  # noqa: E731
+        fwd = lambda: layer.forward(inp["x"], inp["logits"], weights)  # noqa: E731
+        bwd = lambda: layer.backward(inp["dy"], inp["logits"], weights)  # noqa: E731
+        saved = layer.saved_bytes()
     for _ in range(args.warmup):
-        layer.step(inp["x"], inp["logits"], inp["dy"], weights)
+        step()
     torch.cuda.synchronize()
 
     # timed region: K steps, kernel timer live (HIP events on the launch stream)
@@ -235,7 +312,7 @@ def main():
         torch.cuda.synchronize()
         ev[0].record()
         for i in range(args.steps):
-            layer.step(inp["x"], inp["logits"], inp["dy"], weights)
+            step()
             ev[i + 1].record()
         torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
@@ -251,8 +328,8 @@ def main():
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
-    fwd_ms = timed(lambda: layer.forward(inp["x"], inp["logits"], weights))
-    bwd_ms = timed(lambda: layer.backward(inp["dy"], inp["logits"], weights))
+    fwd_ms = timed(fwd)
+    bwd_ms = timed(bwd)
     kms = {}
     for name in mel._lib.KERNEL_IDS:
         tot, n = kt.read(name)
@@ -261,17 +338,23 @@ def main():
                          "ms_per_launch": round(tot / n, 4)}
     peak_bytes = torch.cuda.max_memory_allocated()
 
-    F = cfg.flops_fwd_bwd() + (6 * cfg.N * cfg.H * cfg.I if args.full_ft else 0)
+    F = step_flops(cfg, args.full_ft, shared_I, args.block)
     tflops = F / (ms / 1e3) / 1e12
     bf16 = cfg.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     dom = max((k for k in GEMM_KERNELS if k in kms), key=lambda k: kms[k]["ms_per_step"])
-    dom_ms = kms[dom]["ms_per_launch"]
-    dom_tf = kernel_flops(dom, cfg) / (dom_ms / 1e3) / 1e12
+    # FLOPs of the dominant kernel per step (block mode: its routed and shared
+    # launches together) over its summed launch time per step
+    parts = [c for c in block_parts(cfg, shared_I) if c is not None] if args.block else [cfg]
+    dom_flops_step = sum(kernel_flops(dom, c) * (2 if dom == "base_wgrad" else 1)
+                         for c in parts)
+    dom_launches = kms[dom]["launches"] / args.steps
+    dom_tf = dom_flops_step / (kms[dom]["ms_per_step"] / 1e3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(dom_tf / peak, 4),
-                "traffic": traffic_for(dom, cfg.name),
-                "flops_per_launch": kernel_flops(dom, cfg), "ms_per_launch": dom_ms}
+                "traffic": None if args.block else traffic_for(dom, cfg.name),
+                "flops_per_launch": int(dom_flops_step / dom_launches),
+                "ms_per_launch": kms[dom]["ms_per_launch"]}
     hbm = {}
     for name, kv in kms.items():
         nb = kernel_bytes(name, cfg)
@@ -287,7 +370,11 @@ def main():
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
-        "config": {"workload": f"{cfg.name}-shaped MoE-LoRA expert layer fwd+bwd"
+        "config": {"workload": f"{cfg.name}-shaped MoE-LoRA "
+                               + ("block (router projection, routed experts"
+                                  + (f", shared expert of width {shared_I})" if shared_I else ")")
+                                  if args.block else "expert layer")
+                               + " fwd+bwd"
                                + (", full fine-tuning" if args.full_ft else "")
                                + (", h and act recomputed in backward" if args.recompute else ""),
                    "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "r": cfg.r,
@@ -296,13 +383,15 @@ def main():
         "mfma_peak_frac": round(tflops / peak, 4),
         "flops_per_step": F,
         "peak_hbm_bytes": int(peak_bytes),
-        "saved_activation_bytes": int(layer.saved_bytes()),
+        "saved_activation_bytes": int(saved),
         "roofline": roofline,
         "hbm": hbm,
         "kernels": kms,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens, args.full_ft)
+        out["cpu_baseline"] = (cpu_baseline_block(cfg, inp, args.cpu_tokens, shared_I)
+                               if args.block and not args.full_ft
+                               else cpu_baseline(cfg, inp, args.cpu_tokens, args.full_ft))
     print(json.dumps(out), flush=True)
 
 

@@ -238,6 +238,29 @@ moe_status moe_grouped_lora_bwd_recompute(const moe_shape *shape, const void *dy
                                           const moe_base_grads *base, void *ws, size_t ws_bytes,
                                           void *stream);
 
+/* Router projection and its input gradient, for callers that start from
+ * hidden states rather than logits. The pages keep the router frozen (faster-
+ * moe page, "Implementation details"), so there is no router weight
+ * gradient; the logits' gradient flows back into x:
+ *   logits = x W_r^T        x [T, H] dtype, w_r [E, H] dtype, logits [T, E] float32
+ *   dx    += d_logits W_r   d_logits [T, E] float32 in, dx [T, H] dtype accumulated
+ * Float32 accumulation (bf16 layers: d_logits is rounded to bf16 to feed the
+ * MFMA; dx is read, added to in float32 and rounded once). ws is the router
+ * workspace (moe_router_workspace_bytes). Errors as for the layer calls; H
+ * must be a multiple of 8 and 1 <= E <= 1024.  */
+moe_status moe_router_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t dtype,
+                                      size_t *ws_bytes);
+moe_status moe_router_fwd(const void *x, const void *w_r, int32_t T, int32_t H, int32_t E,
+                          int32_t dtype, float *logits, void *ws, size_t ws_bytes, void *stream);
+moe_status moe_router_bwd(const float *d_logits, const void *w_r, int32_t T, int32_t H,
+                          int32_t E, int32_t dtype, void *dx, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* dst[i] += src[i] for i < n, elements of `dtype`, sum in float32, one
+ * rounding (adds a shared expert's output to the routed output, and its input
+ * gradient to dx). src and dst may not alias.  */
+moe_status moe_accumulate(int32_t dtype, int64_t n, const void *src, void *dst, void *stream);
+
 const char *moe_status_str(moe_status status);
 
 /* Text of the last error raised on the calling thread ("" if none). */
@@ -253,7 +276,8 @@ typedef enum {
   MOE_K_ROUTE = 0, MOE_K_PERMUTE = 1, MOE_K_GATHER = 2, MOE_K_GATE_UP_FWD = 3,
   MOE_K_DOWN_FWD = 4, MOE_K_COMBINE = 5, MOE_K_COMBINE_BWD = 6, MOE_K_ROUTE_BWD = 7,
   MOE_K_DOWN_BWD = 8, MOE_K_GATE_UP_BWD = 9, MOE_K_LORA_SIDE = 10, MOE_K_LORA_WGRAD = 11,
-  MOE_K_UNPERMUTE = 12, MOE_K_BASE_WGRAD = 13, MOE_K_COUNT = 14
+  MOE_K_UNPERMUTE = 12, MOE_K_BASE_WGRAD = 13, MOE_K_ROUTER_FWD = 14, MOE_K_ROUTER_BWD = 15,
+  MOE_K_ACCUMULATE = 16, MOE_K_COUNT = 17
 } moe_kernel_id;
 moe_status moe_kernel_timer_enable(int32_t on);
 moe_status moe_kernel_timer_reset(void);

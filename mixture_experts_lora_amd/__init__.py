@@ -28,7 +28,8 @@ __all__ = [
     "Shape", "moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
     "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
     "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_workspace_bytes_lean",
-    "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute", "kernel_timer", "ROUTER_IDS",
+    "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute", "moe_router_workspace_bytes",
+    "moe_router_fwd", "moe_router_bwd", "moe_accumulate", "kernel_timer", "ROUTER_IDS",
     "library_path",
 ]
 
@@ -275,6 +276,52 @@ def moe_grouped_lora_bwd_recompute(shape: Shape, dy_perm, x_perm, offsets, weigh
         "moe_grouped_lora_bwd_recompute")
 
 
+def _dtype_of(t, name):
+    for key, dt in _TORCH_DTYPES.items():
+        if t.dtype == dt:
+            return key, dt
+    raise ValueError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+
+
+def moe_router_workspace_bytes(T: int, H: int, E: int, dtype: str) -> int:
+    n = ctypes.c_size_t()
+    check(_lib.load().moe_router_workspace_bytes(T, H, E, _ABI_DTYPES[dtype], ctypes.byref(n)),
+          "moe_router_workspace_bytes")
+    return n.value
+
+
+def moe_router_fwd(x, w_r, logits, ws, stream=None):
+    """logits [T, E] float32 = x [T, H] W_r [E, H]^T (frozen router projection)."""
+    T, H = x.shape
+    E = w_r.shape[0]
+    key, dt = _dtype_of(x, "x")
+    wsp, wsb = _ws(ws, moe_router_workspace_bytes(T, H, E, key), "ws")
+    check(_lib.load().moe_router_fwd(
+        _ptr(x, (T, H), dt, "x"), _ptr(w_r, (E, H), dt, "w_r"), T, H, E, _ABI_DTYPES[key],
+        _ptr(logits, (T, E), torch.float32, "logits"), wsp, wsb, _stream(stream)),
+        "moe_router_fwd")
+
+
+def moe_router_bwd(d_logits, w_r, dx, ws, stream=None):
+    """dx [T, H] += d_logits [T, E] W_r [E, H] (the router projection's input gradient)."""
+    T, H = dx.shape
+    E = w_r.shape[0]
+    key, dt = _dtype_of(dx, "dx")
+    wsp, wsb = _ws(ws, moe_router_workspace_bytes(T, H, E, key), "ws")
+    check(_lib.load().moe_router_bwd(
+        _ptr(d_logits, (T, E), torch.float32, "d_logits"), _ptr(w_r, (E, H), dt, "w_r"),
+        T, H, E, _ABI_DTYPES[key], _ptr(dx, (T, H), dt, "dx"), wsp, wsb, _stream(stream)),
+        "moe_router_bwd")
+
+
+def moe_accumulate(src, dst, stream=None):
+    """dst += src, element-wise (float32 sum, one rounding)."""
+    key, dt = _dtype_of(dst, "dst")
+    check(_lib.load().moe_accumulate(
+        _ABI_DTYPES[key], dst.numel(), _ptr(src, tuple(dst.shape), dt, "src"),
+        _ptr(dst, tuple(dst.shape), dt, "dst"), _stream(stream)), "moe_accumulate")
+
+
 class kernel_timer:
     """Per-kernel HIP-event timer of the library (see moe_kernel_timer_* in the header).
 
@@ -313,6 +360,6 @@ try:
 except RuntimeError:
     pass
 
-from .layer import MoELoRALayer, MoELoRAFunction  # noqa: E402
+from .layer import MoELoRABlock, MoELoRALayer, MoELoRAFunction  # noqa: E402
 
-__all__ += ["MoELoRALayer", "MoELoRAFunction"]
+__all__ += ["MoELoRABlock", "MoELoRALayer", "MoELoRAFunction"]

@@ -411,6 +411,74 @@ moe_status moe_grouped_lora_bwd_recompute(const moe_shape* shape, const void* dy
                      weights, saved, dx_perm, grads, base, ws, ws_bytes, stream);
 }
 
+namespace {
+
+moe_status check_router_dims(int32_t T, int32_t H, int32_t E, int32_t dtype) {
+  if (T < 1 || H < 1 || E < 1 || E > 1024)
+    return fail(MOE_ERR_INVALID_ARG, "need T >= 1, H >= 1, 1 <= E <= 1024");
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (H % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "H must be a multiple of 8");
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_router_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t dtype,
+                                      size_t* ws_bytes) {
+  moe_status st = check_router_dims(T, H, E, dtype);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(ws_bytes);
+  *ws_bytes = moe::router_ws_bytes(T, E, dtype);
+  return MOE_OK;
+}
+
+moe_status moe_router_fwd(const void* x, const void* w_r, int32_t T, int32_t H, int32_t E,
+                          int32_t dtype, float* logits, void* ws, size_t ws_bytes,
+                          void* stream) {
+  moe_status st = check_router_dims(T, H, E, dtype);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(x);
+  CHECK_PTR(w_r);
+  CHECK_PTR(logits);
+  CHECK_PTR(ws);
+  if (logits == x || logits == w_r) return fail(MOE_ERR_INVALID_ARG, "logits aliases an input");
+  const size_t need = moe::router_ws_bytes(T, E, dtype);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "router workspace needs " + std::to_string(need) + " bytes");
+  hipError_t e = moe::launch_router_fwd(x, w_r, T, H, E, dtype, logits, ws, as_stream(stream),
+                                        moe::active_timer());
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_router_fwd");
+}
+
+moe_status moe_router_bwd(const float* d_logits, const void* w_r, int32_t T, int32_t H,
+                          int32_t E, int32_t dtype, void* dx, void* ws, size_t ws_bytes,
+                          void* stream) {
+  moe_status st = check_router_dims(T, H, E, dtype);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(d_logits);
+  CHECK_PTR(w_r);
+  CHECK_PTR(dx);
+  CHECK_PTR(ws);
+  if (dx == d_logits || dx == w_r) return fail(MOE_ERR_INVALID_ARG, "dx aliases an input");
+  const size_t need = moe::router_ws_bytes(T, E, dtype);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "router workspace needs " + std::to_string(need) + " bytes");
+  hipError_t e = moe::launch_router_bwd(d_logits, w_r, T, H, E, dtype, dx, ws,
+                                        as_stream(stream), moe::active_timer());
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_router_bwd");
+}
+
+moe_status moe_accumulate(int32_t dtype, int64_t n, const void* src, void* dst, void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (n < 0) return fail(MOE_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return MOE_OK;
+  CHECK_PTR(src);
+  CHECK_PTR(dst);
+  if (src == dst) return fail(MOE_ERR_INVALID_ARG, "src and dst alias");
+  hipError_t e = moe::launch_accumulate(dtype, n, src, dst, as_stream(stream), moe::active_timer());
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_accumulate");
+}
+
 moe_status moe_kernel_timer_enable(int32_t on) {
   TimerState& t = timer();
   std::lock_guard<std::mutex> lk(t.mu);

@@ -45,7 +45,9 @@ namespace moe {
 namespace {
 
 enum Mode { GROUP_M = 0, GROUP_K = 1 };
-enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2 };
+// EPI_STORE_F32: float32 output (router logits); EPI_ADD: out += result (bf16
+// read-modify-write, the sum formed in float32, one rounding).
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2, EPI_STORE_F32 = 3, EPI_ADD = 4 };
 
 struct Opnd {
   const void* ptr;
@@ -135,11 +137,15 @@ __device__ __forceinline__ void epi_store(const GemmArgs& p, int e, int64_t row0
   if (m_local >= rows) return;
   if (MODE == GROUP_M) {
     const int64_t row = row0 + m_local;
-    if (EPI == EPI_STORE) {
+    if (EPI == EPI_STORE || EPI == EPI_STORE_F32 || EPI == EPI_ADD) {
       float o[4];
+      T* rp = static_cast<T*>(p.out) + row * p.ld_out;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = v[j] * p.scale;
-      store4<T>(static_cast<T*>(p.out) + row * p.ld_out, n_col, p.N, (p.ld_out & 3) == 0, o);
+      for (int j = 0; j < 4; ++j) {
+        o[j] = v[j] * p.scale;
+        if (EPI == EPI_ADD && n_col + j < p.N) o[j] += to_f32<T>(rp[n_col + j]);
+      }
+      store4<T>(rp, n_col, p.N, (p.ld_out & 3) == 0, o);
     } else if (EPI == EPI_SWIGLU_BWD) {
       if (n_col >= p.N) return;  // N = I (multiple of 8)
       const T* hr = static_cast<const T*>(p.aux) + row * p.ld_aux;
@@ -866,6 +872,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
   const int srow = lane & 31, shalf = lane >> 5;
   const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0 && (p.ld_out & 7) == 0 &&
                        (p.out_estride & 7) == 0;
+  const bool out_vec4 = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0 && (p.ld_out & 3) == 0;
 #pragma unroll
   for (int mi = 0; mi < MF; ++mi) {
     if (mi) wave_lds_sync();  // previous slab fully read
@@ -923,6 +930,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
           bf16_t* dr = static_cast<bf16_t*>(p.out) + row * p.ld_out;
           store8(dr + col, dg);
           store8(dr + p.I + col, du);
+        } else if (MODE == GROUP_M && EPI == EPI_STORE_F32) {
+          float* rp = static_cast<float*>(p.out) + (row0 + m_local) * p.ld_out;
+          if (out_vec4 && col + 8 <= p.N) {
+            float4* q = reinterpret_cast<float4*>(rp + col);
+            q[0] = make_float4(v[0] * p.scale, v[1] * p.scale, v[2] * p.scale, v[3] * p.scale);
+            q[1] = make_float4(v[4] * p.scale, v[5] * p.scale, v[6] * p.scale, v[7] * p.scale);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (col + j < p.N) rp[col + j] = v[j] * p.scale;
+          }
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] *= p.scale;
@@ -932,11 +950,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
                            : static_cast<bf16_t*>(p.out) + static_cast<int64_t>(e) * p.out_estride +
                                  static_cast<int64_t>(m0 + m_local) * p.ld_out;
           if (out_vec && col + 8 <= p.N) {
+            if (EPI == EPI_ADD) {
+              float o[8];
+              load8(rp + col, o);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) v[j] += o[j];
+            }
             store8(rp + col, v);
           } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-              if (col + j < p.N) rp[col + j] = f32_to_bf16(v[j]);
+              if (col + j < p.N)
+                rp[col + j] = f32_to_bf16(EPI == EPI_ADD ? v[j] + bf16_to_f32(rp[col + j]) : v[j]);
           }
         }
       }
@@ -1545,6 +1570,139 @@ hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, cons
   MOE_TRY(build_tiles(L, offsets, d.E, s));
   MOE_TRY(launch_gate_up(d, L, x_perm, offsets, w, sv.u_gu, full.h, full.act, s, tm));
   return launch_experts_bwd(d, g, x_perm, offsets, w, full, dx_perm, gr, base, ws, s, tm);
+}
+
+// ----------------------------------------------------------------- router projection
+// logits = x W_r^T (float32 out) and its input gradient dx += d_logits W_r, as
+// grouped GEMMs over a single group of all T rows (tile list built on the
+// device from offsets {0, T}).
+namespace {
+
+__global__ void range_offsets_kernel(int32_t* off, int T) {
+  if (threadIdx.x == 0) {
+    off[0] = 0;
+    off[1] = T;
+  }
+}
+
+__global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ src,
+                                                        bf16_t* __restrict__ dst, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = f32_to_bf16(src[i]);
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(256) void accumulate_kernel(const Elem* __restrict__ src,
+                                                         Elem* __restrict__ dst, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = from_f32<Elem>(to_f32<Elem>(dst[i]) + to_f32<Elem>(src[i]));
+}
+
+struct RouterWs {
+  int32_t* offsets;
+  WsLayout L;
+  bf16_t* dl16;  // d_logits in bf16 (backward, bf16 layers)
+  size_t bytes;
+};
+
+RouterWs router_ws(void* ws, int T, int E, int dtype) {
+  ExpertDims d{};
+  d.N = T;
+  d.E = 1;
+  d.dtype = dtype;
+  d.r = 8;  // tile heights as for a LoRA-friendly rank: 128-row small list
+  RouterWs R;
+  char* p = static_cast<char*>(ws);
+  R.offsets = reinterpret_cast<int32_t*>(p);
+  size_t off = kAlign;
+  R.L = tile_ws(p ? p + off : nullptr, d);
+  off += align_up(R.L.bytes);
+  R.dl16 = reinterpret_cast<bf16_t*>(p ? p + off : nullptr);
+  off += dtype == MOE_BF16 ? align_up(static_cast<size_t>(T) * E * 2) : 0;
+  R.bytes = off;
+  return R;
+}
+
+GemmArgs router_args(const RouterWs& R, int T) {
+  GemmArgs a{};
+  a.a[1] = none();
+  a.b[1] = none();
+  a.E = 1;
+  a.offsets = R.offsets;
+  a.tiles = R.L.small.tiles;
+  a.ntiles = R.L.small.ntiles;
+  a.K[1] = 0;
+  a.scale = 1.0f;
+  return a;
+}
+
+}  // namespace
+
+size_t router_ws_bytes(int T, int E, int dtype) { return router_ws(nullptr, T, E, dtype).bytes; }
+
+hipError_t launch_router_fwd(const void* x, const void* w_r, int T, int H, int E, int dtype,
+                             float* logits, void* ws, hipStream_t s, KernelTimer* tm) {
+  const RouterWs R = router_ws(ws, T, E, dtype);
+  TimedScope ts(tm, MOE_K_ROUTER_FWD, s);
+  hipLaunchKernelGGL(range_offsets_kernel, dim3(1), dim3(64), 0, s, R.offsets, T);
+  MOE_TRY(build_tiles(R.L, R.offsets, 1, s));
+  GemmArgs a = router_args(R, T);
+  a.a[0] = opnd(x, 0, H, 1, true);
+  a.b[0] = opnd(w_r, 0, H, 1, true);
+  a.K[0] = H;
+  a.N = E;
+  a.out = logits;
+  a.ld_out = E;
+  if (dtype == MOE_BF16) {
+    a.ntn = ceil_div(E, 64);
+    return launch(gemm_bf16<128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE_F32, false, true, true>,
+                  static_cast<int>(tile_cap(T, 1, R.L.small.bm)) * a.ntn, a, s);
+  }
+  a.ntn = ceil_div(E, 64);
+  return launch(gemm_f32<GROUP_M, EPI_STORE, false>,
+                static_cast<int>(tile_cap(T, 1, R.L.small.bm)) * a.ntn, a, s);
+}
+
+hipError_t launch_router_bwd(const float* d_logits, const void* w_r, int T, int H, int E,
+                             int dtype, void* dx, void* ws, hipStream_t s, KernelTimer* tm) {
+  const RouterWs R = router_ws(ws, T, E, dtype);
+  TimedScope ts(tm, MOE_K_ROUTER_BWD, s);
+  hipLaunchKernelGGL(range_offsets_kernel, dim3(1), dim3(64), 0, s, R.offsets, T);
+  MOE_TRY(build_tiles(R.L, R.offsets, 1, s));
+  GemmArgs a = router_args(R, T);
+  a.K[0] = E;
+  a.N = H;
+  a.out = dx;
+  a.ld_out = H;
+  if (dtype == MOE_BF16) {
+    const int64_t n = static_cast<int64_t>(T) * E;
+    hipLaunchKernelGGL(cast_bf16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                       0, s, d_logits, R.dl16, n);
+    a.a[0] = opnd(R.dl16, 0, E, 1, true);
+    a.b[0] = opnd(w_r, 0, H, 0, true);  // [K = E][N = H]
+    a.ntn = ceil_div(H, 256);
+    return launch(gemm_bf16<128, 256, 64, 128, 32, 3, 2, GROUP_M, EPI_ADD, false, true, false>,
+                  static_cast<int>(tile_cap(T, 1, R.L.small.bm)) * a.ntn, a, s);
+  }
+  a.a[0] = opnd(d_logits, 0, E, 1, true);
+  a.b[0] = opnd(w_r, 0, H, 0, true);
+  a.ntn = ceil_div(H, 64);
+  return launch(gemm_f32<GROUP_M, EPI_ADD, false>,
+                static_cast<int>(tile_cap(T, 1, R.L.small.bm)) * a.ntn, a, s);
+}
+
+hipError_t launch_accumulate(int dtype, int64_t n, const void* src, void* dst, hipStream_t s,
+                             KernelTimer* tm) {
+  if (n <= 0) return hipSuccess;
+  TimedScope ts(tm, MOE_K_ACCUMULATE, s);
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(accumulate_kernel<bf16_t>, grid, dim3(256), 0, s,
+                       static_cast<const bf16_t*>(src), static_cast<bf16_t*>(dst), n);
+  else
+    hipLaunchKernelGGL(accumulate_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(src), static_cast<float*>(dst), n);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -87,4 +87,13 @@ hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, cons
                                         const moe_lora_grads& gr, const moe_base_grads* base,
                                         void* ws, hipStream_t s, KernelTimer* tm);
 
+// ---- router projection and element-wise accumulate
+size_t router_ws_bytes(int T, int E, int dtype);
+hipError_t launch_router_fwd(const void* x, const void* w_r, int T, int H, int E, int dtype,
+                             float* logits, void* ws, hipStream_t s, KernelTimer* tm);
+hipError_t launch_router_bwd(const float* d_logits, const void* w_r, int T, int H, int E,
+                             int dtype, void* dx, void* ws, hipStream_t s, KernelTimer* tm);
+hipError_t launch_accumulate(int dtype, int64_t n, const void* src, void* dst, hipStream_t s,
+                             KernelTimer* tm);
+
 }  // namespace moe

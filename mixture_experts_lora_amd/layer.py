@@ -10,14 +10,22 @@ so nothing is allocated inside a step) and issues, on torch's current stream:
 
 MoELoRAFunction wraps the same calls as a torch.autograd.Function whose
 gradients are dX, d logits and the four LoRA gradients (base weights frozen).
+
+MoELoRABlock is the block a model sees: it starts from hidden states, makes the
+logits with the frozen router projection (moe_router_fwd), runs the routed
+layer, and adds an optional always-on shared expert (a dense LoRA SwiGLU MLP
+over every token: the grouped calls with one expert, k = 1 and the tokens in
+their own order); its backward adds the router's and the shared expert's input
+gradients to dX (moe_router_bwd, moe_accumulate).
 """
 from __future__ import annotations
 
 import torch
 
-from . import (Shape, moe_grouped_full_bwd, moe_grouped_lora_bwd, moe_grouped_lora_bwd_recompute,
-               moe_grouped_lora_fwd, moe_grouped_lora_fwd_lean, moe_permute, moe_route,
-               moe_route_bwd, moe_unpermute_combine, moe_unpermute_combine_bwd,
+from . import (Shape, moe_accumulate, moe_grouped_full_bwd, moe_grouped_lora_bwd,
+               moe_grouped_lora_bwd_recompute, moe_grouped_lora_fwd, moe_grouped_lora_fwd_lean,
+               moe_permute, moe_route, moe_route_bwd, moe_router_bwd, moe_router_fwd,
+               moe_router_workspace_bytes, moe_unpermute_combine, moe_unpermute_combine_bwd,
                moe_workspace_bytes, moe_workspace_bytes_lean)
 
 WEIGHT_NAMES = ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")
@@ -97,6 +105,96 @@ class MoELoRALayer:
         """One forward and backward pass."""
         self.forward(x, logits, weights, stream)
         return self.backward(dy, logits, weights, stream)
+
+
+def _one_expert(w: dict) -> dict:
+    """A single expert's weights as the stacked [1, ...] tensors the grouped calls take."""
+    return {n: v.unsqueeze(0) for n, v in w.items()}
+
+
+class _DenseExpertBuffers:
+    """Saved activations, gradients and workspace of one expert run over all
+    tokens (the grouped calls with E = 1, k = 1)."""
+
+    def __init__(self, shape: Shape, device, full_ft: bool, recompute: bool):
+        T, H, I, r = shape.T, shape.H, shape.I, shape.r
+        z = lambda *s: torch.empty(s, device=device, dtype=shape.torch_dtype)  # noqa: E731
+        self.full_ft, self.recompute = full_ft, recompute
+        self.saved = {"u_gu": z(T, r), "u_d": z(T, r), "y_exp": z(T, H)}
+        if not recompute:
+            self.saved.update(h=z(T, 2 * I), act=z(T, I))
+        self.grads = {"da_gu": z(1, r, H), "db_gu": z(1, 2 * I, r), "da_d": z(1, r, I),
+                      "db_d": z(1, H, r)}
+        self.base_grads = {"dw_gu": z(1, 2 * I, H), "dw_d": z(1, H, I)} if full_ft else None
+        fwd, bwd, _ = moe_workspace_bytes(shape)
+        if recompute:
+            fwd, bwd = moe_workspace_bytes_lean(shape)
+        self.ws_fwd = self.ws_bwd = torch.empty(max(fwd, bwd, 1), device=device,
+                                                dtype=torch.uint8)
+
+
+class MoELoRABlock:
+    """Router projection + routed MoE-LoRA layer + optional shared expert.
+
+    shared_I: intermediate width of the shared expert (None: no shared expert).
+    The shared expert carries its own LoRA adapters of rank shape.r and the
+    same scale; its weights are passed as a dict of w_gu [2 shared_I, H],
+    a_gu, b_gu, w_d [H, shared_I], a_d, b_d. full_ft and recompute apply to
+    the routed and the shared experts alike."""
+
+    def __init__(self, shape: Shape, router: str, shared_I: int | None = None, device="cuda",
+                 full_ft: bool = False, recompute: bool = False):
+        self.shape, self.shared_I = shape, shared_I
+        self.routed = MoELoRALayer(shape, router, device, full_ft, recompute)
+        T, H, E = shape.T, shape.H, shape.E
+        self.logits = torch.empty(T, E, device=device, dtype=torch.float32)
+        self.ws_router = torch.empty(max(moe_router_workspace_bytes(T, H, E, shape.dtype), 1),
+                                     device=device, dtype=torch.uint8)
+        self.shared = None
+        if shared_I:
+            # one expert over all T tokens in token order: x is its own x_perm
+            self.shared_shape = Shape(T, H, int(shared_I), 1, 1, shape.r, shape.dtype,
+                                      shape.lora_scale)
+            self.shared = _DenseExpertBuffers(self.shared_shape, device, full_ft, recompute)
+            self.shared_offsets = torch.tensor([0, T], device=device, dtype=torch.int32)
+            self.shared_dx = torch.empty(T, H, device=device, dtype=shape.torch_dtype)
+
+    def forward(self, x, w_r, weights: dict, shared_weights: dict | None = None, stream=None):
+        moe_router_fwd(x, w_r, self.logits, self.ws_router, stream)
+        y = self.routed.forward(x, self.logits, weights, stream)
+        if self.shared is not None:
+            L, sh = self.shared, self.shared_shape
+            fwd = moe_grouped_lora_fwd_lean if L.recompute else moe_grouped_lora_fwd
+            fwd(sh, x, self.shared_offsets, _one_expert(shared_weights), L.saved, L.ws_fwd,
+                stream)
+            moe_accumulate(L.saved["y_exp"], y, stream)
+        return y
+
+    def backward(self, dy, x, w_r, weights: dict, shared_weights: dict | None = None,
+                 stream=None):
+        """Returns (dx, d_logits, routed LoRA grads, shared LoRA grads or None)."""
+        dx, dl, g = self.routed.backward(dy, self.logits, weights, stream)
+        moe_router_bwd(dl, w_r, dx, self.ws_router, stream)
+        if self.shared is None:
+            return dx, dl, g, None
+        L, sh = self.shared, self.shared_shape
+        shared_weights = _one_expert(shared_weights)
+        if L.recompute:
+            moe_grouped_lora_bwd_recompute(sh, dy, x, self.shared_offsets, shared_weights,
+                                           L.saved, self.shared_dx, L.grads, L.ws_bwd,
+                                           L.base_grads, stream)
+        elif L.full_ft:
+            moe_grouped_full_bwd(sh, dy, x, self.shared_offsets, shared_weights, L.saved,
+                                 self.shared_dx, L.grads, L.base_grads, L.ws_bwd, stream)
+        else:
+            moe_grouped_lora_bwd(sh, dy, x, self.shared_offsets, shared_weights, L.saved,
+                                 self.shared_dx, L.grads, L.ws_bwd, stream)
+        moe_accumulate(self.shared_dx, dx, stream)
+        return dx, dl, g, {n: v[0] for n, v in L.grads.items()}
+
+    def step(self, x, w_r, dy, weights: dict, shared_weights: dict | None = None, stream=None):
+        self.forward(x, w_r, weights, shared_weights, stream)
+        return self.backward(dy, x, w_r, weights, shared_weights, stream)
 
 
 class MoELoRAFunction(torch.autograd.Function):

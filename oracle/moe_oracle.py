@@ -370,3 +370,49 @@ def layer_forward_backward(x, logits, dY, weights, k, router, s=1.0, dtype=np.fl
     """Forward then backward; returns (Y, grads dict, cache)."""
     Y, cache = layer_forward(x, logits, weights, k, router, s, dtype)
     return Y, layer_backward(dY, cache, base_grads), cache
+
+
+# ------------------------------------------------------- router projection, shared expert
+def router_logits(x, w_r, dtype=np.float32):
+    """logits [T, E] = x W_r^T: the router projection whose output the routing
+    consumes ([moe], "What is torch._grouped_mm?": the expert mask comes from
+    the router's scores; "Implementation details": the router is frozen)."""
+    return np.asarray(x, dtype) @ np.asarray(w_r, dtype).T
+
+
+def router_input_grad(dlogits, w_r, dtype=np.float32):
+    """dL/dx contribution of the router projection: dlogits [T, E] W_r [E, H]
+    (the router weight itself is frozen, so it gets no gradient)."""
+    return np.asarray(dlogits, dtype) @ np.asarray(w_r, dtype)
+
+
+def layer_with_router_and_shared(x, w_r, dY, weights, shared, k, router, s=1.0,
+                                 dtype=np.float32, logits=None):
+    """The layer as a model block sees it: logits from the router projection,
+    the routed experts, plus an always-on shared expert (a dense LoRA SwiGLU
+    MLP over every token, as in the DeepSeek-style MoE the [moe] page describes
+    for GLM-4.7-Flash: routed experts plus one shared expert, section "GLM 4.7
+    benchmark"). shared: dict of one expert's w_gu, a_gu, b_gu, w_d, a_d, b_d, or
+    None. Returns (Y, grads) with grads: dx (routed + shared + router), dlogits,
+    the routed LoRA gradients, and shared_* for the shared expert's LoRA
+    gradients. The routing selects on float32 logits; `logits`, when given, are
+    those float32 logits (a caller comparing against another implementation
+    passes that implementation's rounding of x W_r^T, so that both take the
+    same top-k decisions), else x W_r^T is formed here in float64 and rounded
+    to float32."""
+    if logits is None:
+        logits = router_logits(x, w_r, np.float64).astype(np.float32)
+    logits = np.asarray(logits, np.float32)
+    Y, g, _ = layer_forward_backward(x, logits, dY, weights, k, router, s, dtype)
+    g = dict(g)
+    g["dx"] = g["dx"] + router_input_grad(g["dlogits"], w_r, dtype)
+    g["logits"] = logits
+    if shared is not None:
+        X = np.asarray(x, dtype)
+        f = expert_forward(X, **shared, s=s, dtype=dtype)
+        b = expert_backward(X, np.asarray(dY, dtype), f, **shared, s=s, dtype=dtype)
+        Y = Y + f["y"]
+        g["dx"] = g["dx"] + b["dx"]
+        for n in ("da_gu", "db_gu", "da_d", "db_d"):
+            g["shared_" + n] = b[n]
+    return Y, g

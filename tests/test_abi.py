@@ -157,6 +157,35 @@ def test_full_ft_and_lean_entry_points_validate(lib):
                                               None) == 3
 
 
+def test_router_and_accumulate_validate(lib):
+    """Router projection and accumulate: dimensions, dtype, workspace and
+    aliasing are checked on the host before any launch."""
+    P = ctypes.c_void_p
+    fake = P(0x10000)
+    n = ctypes.c_size_t()
+    assert lib.moe_router_workspace_bytes(4096, 2880, 32, 1, ctypes.byref(n)) == 0
+    need_bf16 = n.value
+    assert need_bf16 >= 4096 * 32 * 2            # bf16 copy of d_logits for the MFMA
+    assert lib.moe_router_workspace_bytes(4096, 2880, 32, 0, ctypes.byref(n)) == 0
+    assert n.value < need_bf16
+    assert lib.moe_router_workspace_bytes(4096, 2882, 32, 1, ctypes.byref(n)) == 2  # H % 8
+    assert lib.moe_router_workspace_bytes(4096, 2880, 1025, 1, ctypes.byref(n)) == 1
+    assert lib.moe_router_workspace_bytes(0, 2880, 32, 1, ctypes.byref(n)) == 1
+    assert lib.moe_router_workspace_bytes(16, 64, 8, 7, ctypes.byref(n)) == 1       # dtype
+    assert lib.moe_router_workspace_bytes(16, 64, 8, 1, None) == 1
+    args = (fake, P(0x20000), 4096, 2880, 32, 1)
+    assert lib.moe_router_fwd(*args, P(0x30000), P(0x40000), need_bf16 - 1, None) == 3
+    assert lib.moe_router_fwd(*args, None, P(0x40000), need_bf16, None) == 1
+    assert lib.moe_router_fwd(*args, fake, P(0x40000), need_bf16, None) == 1  # logits is x
+    assert lib.moe_router_bwd(*args, P(0x30000), None, need_bf16, None) == 1
+    assert lib.moe_router_bwd(*args, P(0x30000), P(0x40000), need_bf16 - 1, None) == 3
+    assert lib.moe_router_bwd(*args, fake, P(0x40000), need_bf16, None) == 1  # dx is d_logits
+    assert lib.moe_accumulate(1, 0, None, None, None) == 0                 # empty: nothing to do
+    assert lib.moe_accumulate(1, -1, fake, P(0x20000), None) == 1
+    assert lib.moe_accumulate(2, 16, fake, P(0x20000), None) == 1
+    assert lib.moe_accumulate(1, 16, fake, fake, None) == 1
+
+
 def test_aliasing_rejected(lib):
     P = ctypes.c_void_p
     fake = P(0x10000)

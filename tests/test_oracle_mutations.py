@@ -17,7 +17,8 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PIN_TESTS = ["tests/test_oracle_layer.py", "tests/test_oracle_route_permute.py"]
+PIN_TESTS = ["tests/test_oracle_layer.py", "tests/test_oracle_route_permute.py",
+             "tests/test_oracle_router_shared.py"]
 
 # (name, text in oracle/moe_oracle.py, replacement)
 MUTATIONS = [
@@ -56,6 +57,14 @@ MUTATIONS = [
     ("dw_gu_without_swiglu_derivative", 'out["dw_gu"] = dh.T @ X',
      'out["dw_gu"] = np.concatenate([da, da], axis=1).T @ X'),
     ("dw_d_scaled_by_lora_scale", 'out["dw_d"] = G.T @ a', 'out["dw_d"] = s * (G.T @ a)'),
+    ("router_logits_negated", "return np.asarray(x, dtype) @ np.asarray(w_r, dtype).T",
+     "return -(np.asarray(x, dtype) @ np.asarray(w_r, dtype).T)"),
+    ("router_grad_dropped", 'g["dx"] = g["dx"] + router_input_grad(g["dlogits"], w_r, dtype)',
+     'g["dx"] = g["dx"]'),
+    ("router_grad_halved", "return np.asarray(dlogits, dtype) @ np.asarray(w_r, dtype)",
+     "return np.asarray(dlogits, dtype) @ np.asarray(w_r, dtype) * 0.5"),
+    ("shared_output_dropped", 'Y = Y + f["y"]', "Y = Y"),
+    ("shared_dx_dropped", 'g["dx"] = g["dx"] + b["dx"]', 'g["dx"] = g["dx"]'),
 ]
 
 # Runs the pin tests with the oracle package taken from argv[1].

@@ -6,9 +6,9 @@ which are an input to the layer) and hands them to whichever side asks, the
 CPU oracle or the HIP library.
 """
 from .configs import LayerConfig, CONFIGS, PARITY_CONFIGS, BENCH_CONFIG, get_config
-from .synth import make_inputs, seed_for, expert_histogram
+from .synth import make_inputs, make_block_inputs, seed_for, expert_histogram
 
 __all__ = [
     "LayerConfig", "CONFIGS", "PARITY_CONFIGS", "BENCH_CONFIG", "get_config",
-    "make_inputs", "seed_for", "expert_histogram",
+    "make_inputs", "make_block_inputs", "seed_for", "expert_histogram",
 ]

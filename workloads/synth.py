@@ -33,7 +33,9 @@ import torch
 from .configs import LayerConfig
 
 TENSOR_IDS = {"x": 0, "w_r": 1, "w_gu": 2, "w_d": 3, "a_gu": 4, "b_gu": 5,
-              "a_d": 6, "b_d": 7, "dy": 8, "zipf": 9}
+              "a_d": 6, "b_d": 7, "dy": 8, "zipf": 9,
+              "shared_w_gu": 10, "shared_w_d": 11, "shared_a_gu": 12, "shared_b_gu": 13,
+              "shared_a_d": 14, "shared_b_d": 15}
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -102,6 +104,28 @@ def make_inputs(cfg: LayerConfig, seed: int, device="cpu", with_dy=True) -> dict
     return out
 
 
+def make_block_inputs(cfg: LayerConfig, seed: int, device="cpu", shared_I: int | None = None,
+                      with_dy=True) -> dict:
+    """make_inputs plus what a whole MoE block starts from: the router weight
+    w_r [E, H] (the very draw the logits were made from) and, when shared_I is
+    given, one always-on shared expert with intermediate width shared_I:
+    shared_w_gu [2 shared_I, H], shared_a_gu [r, H], shared_b_gu [2 shared_I, r],
+    shared_w_d [H, shared_I], shared_a_d [r, shared_I], shared_b_d [H, r], drawn
+    with the routed experts' distributions."""
+    dev = torch.device(device)
+    dt = TORCH_DTYPE[cfg.dtype]
+    out = make_inputs(cfg, seed, device, with_dy)
+    H, r = cfg.H, cfg.r
+    out["w_r"] = _normal((cfg.E, H), 0.02, seed_for(seed, "w_r"), dev, dt)
+    if shared_I:
+        Is = int(shared_I)
+        for n, shp, std in (("w_gu", (2 * Is, H), 0.02), ("w_d", (H, Is), 0.02),
+                            ("a_gu", (r, H), 1.0 / r), ("b_gu", (2 * Is, r), 0.02),
+                            ("a_d", (r, Is), 1.0 / r), ("b_d", (H, r), 0.02)):
+            out["shared_" + n] = _normal(shp, std, seed_for(seed, "shared_" + n), dev, dt)
+    return out
+
+
 def to_numpy(t: torch.Tensor) -> np.ndarray:
     """Host float32 (or integer) copy of a tensor; bf16 values are exact in float32."""
     if t.dtype in (torch.bfloat16, torch.float16):
@@ -114,5 +138,5 @@ def expert_histogram(topk_ids: np.ndarray, E: int) -> np.ndarray:
     return np.bincount(np.asarray(topk_ids).ravel(), minlength=E)
 
 
-__all__ = ["make_inputs", "seed_for", "zipf_offsets", "to_numpy", "expert_histogram",
+__all__ = ["make_inputs", "make_block_inputs", "seed_for", "zipf_offsets", "to_numpy", "expert_histogram",
            "TENSOR_IDS", "TORCH_DTYPE"]
