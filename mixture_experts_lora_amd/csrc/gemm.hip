@@ -35,6 +35,7 @@
 // plain FMA kernel with the same tiling logic.
 #include <stdlib.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -872,7 +873,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
   const int srow = lane & 31, shalf = lane >> 5;
   const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0 && (p.ld_out & 7) == 0 &&
                        (p.out_estride & 7) == 0;
-  const bool out_vec4 = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0 && (p.ld_out & 3) == 0;
+  const bool out_vec4 = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0 && (p.ld_out & 3) == 0 &&
+                        (p.out_estride & 3) == 0;
 #pragma unroll
   for (int mi = 0; mi < MF; ++mi) {
     if (mi) wave_lds_sync();  // previous slab fully read
@@ -930,8 +932,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
           bf16_t* dr = static_cast<bf16_t*>(p.out) + row * p.ld_out;
           store8(dr + col, dg);
           store8(dr + p.I + col, du);
-        } else if (MODE == GROUP_M && EPI == EPI_STORE_F32) {
-          float* rp = static_cast<float*>(p.out) + (row0 + m_local) * p.ld_out;
+        } else if (EPI == EPI_STORE_F32) {
+          // GROUP_M: router logits; GROUP_K: split-K partial weight gradients
+          float* rp = MODE == GROUP_M
+                          ? static_cast<float*>(p.out) + (row0 + m_local) * p.ld_out
+                          : static_cast<float*>(p.out) + static_cast<int64_t>(e) * p.out_estride +
+                                static_cast<int64_t>(m0 + m_local) * p.ld_out;
           if (out_vec4 && col + 8 <= p.N) {
             float4* q = reinterpret_cast<float4*>(rp + col);
             q[0] = make_float4(v[0] * p.scale, v[1] * p.scale, v[2] * p.scale, v[3] * p.scale);
@@ -1299,51 +1305,148 @@ hipError_t side_product(const ExpertDims& d, const int32_t* offsets, const WsLay
   return launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, t, a.ntn), a, s);
 }
 
-// out_e[P, Q] = sum over the expert's rows n of L[n, P] R[n, Q]  (L: [rows, P], R: [rows, Q]).
-hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* Lm, int P,
-                       const void* Rm, int Q, void* out, hipStream_t s) {
-  GemmArgs a{};
-  a.a[1] = none();
-  a.b[1] = none();
-  a.E = d.E;
-  a.offsets = offsets;
-  a.M = P;
-  a.N = Q;
-  a.scale = 1.0f;
-  a.out = out;
-  a.out_estride = static_cast<int64_t>(P) * Q;
-  a.ld_out = Q;
-  a.a[0] = opnd(Lm, 0, P, 0, P % 8 == 0);
-  a.b[0] = opnd(Rm, 0, Q, 0, Q % 8 == 0);
+// ---- weight gradients: out_e[P, Q] = sum over the expert's rows n of L[n, P] R[n, Q]
+// (L: [rows, P], R: [rows, Q]). One workgroup owns an output tile and runs
+// over all the expert's rows, so no atomics are needed and the result does not
+// depend on scheduling. When the experts are too few to give every CU a tile
+// (a shared expert is one expert over all T tokens), each expert's rows are
+// cut into S contiguous chunks that act as experts of their own, every chunk
+// writes a float32 partial into the workspace, and a second kernel sums the S
+// partials of each expert in chunk order (still deterministic).
+
+// Tiles per expert of the kernel weight_grad picks for [P, Q].
+int wgrad_tiles(const ExpertDims& d, int P, int Q) {
+  if (d.dtype != MOE_BF16) return ceil_div(P, 64) * ceil_div(Q, 64);
+  if (Q <= 64 && P > 64) return ceil_div(P, 256);
+  if (P >= 256 && Q >= 256) return ceil_div(P, 128) * ceil_div(Q, 256);
+  return (P <= 32 ? 1 : ceil_div(P, 64)) * ceil_div(Q, 256);
+}
+
+// Row chunks per expert: enough to reach ~512 workgroups when fewer than 256
+// would run, never chunks of fewer than 256 rows on average, and none for the
+// full fine-tuning gradients (P, Q >= 256: tiles enough, partials too large).
+int wgrad_splits(const ExpertDims& d, int P, int Q) {
+  if (P >= 256 && Q >= 256) return 1;
+  const int64_t blocks = static_cast<int64_t>(d.E) * wgrad_tiles(d, P, Q);
+  if (blocks >= 256) return 1;
+  const int64_t by_rows = static_cast<int64_t>(d.N) / (static_cast<int64_t>(d.E) * 256);
+  const int64_t want = (512 + blocks - 1) / blocks;
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({want, by_rows, 64})));
+}
+
+// Workspace for the split path of one [P, Q] gradient: chunk offsets, then partials.
+size_t wgrad_split_bytes(const ExpertDims& d, int P, int Q) {
+  const int S = wgrad_splits(d, P, Q);
+  if (S <= 1) return 0;
+  const int64_t G = static_cast<int64_t>(d.E) * S;
+  return align_up(static_cast<size_t>(G + 1) * 4) + align_up(static_cast<size_t>(G) * P * Q * 4);
+}
+
+// The largest split workspace over the four LoRA gradients of the backward.
+size_t lora_wgrad_split_bytes(const ExpertDims& d) {
+  const int H = d.H, I = d.I, r = d.r;
+  return std::max({wgrad_split_bytes(d, H, r), wgrad_split_bytes(d, r, I),
+                   wgrad_split_bytes(d, 2 * I, r), wgrad_split_bytes(d, r, H)});
+}
+
+// Chunk c of expert e covers rows [off[e] + cnt_e c / S, off[e] + cnt_e (c + 1) / S).
+__global__ void split_offsets_kernel(const int32_t* __restrict__ off, int E, int S,
+                                     int32_t* __restrict__ voff) {
+  for (int i = threadIdx.x; i < E * S; i += blockDim.x) {
+    const int e = i / S, c = i - e * S;
+    const int64_t cnt = off[e + 1] - off[e];
+    voff[i] = off[e] + static_cast<int32_t>(cnt * c / S);
+  }
+  if (threadIdx.x == 0) voff[E * S] = off[E];
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part,
+                                                            Elem* __restrict__ out, int S,
+                                                            int64_t PQ, int64_t total) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t e = i / PQ, q = i - e * PQ;
+  const float* p = part + e * S * PQ + q;
+  float acc = 0.f;
+  for (int c = 0; c < S; ++c) acc += p[c * PQ];
+  out[i] = from_f32<Elem>(acc);
+}
+
+template <int EPI>
+hipError_t weight_grad_launch(const ExpertDims& d, GemmArgs& a, int E, int P, int Q,
+                              hipStream_t s) {
   if (d.dtype == MOE_BF16) {
     if (Q <= 64 && P > 64) {  // [big, r]
       a.ntn = 1;
-      if (Q <= 32) {
-        a.ntm = ceil_div(P, 256);
-        return launch(gemm_bf16<256, 32, 64, 32, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm, a, s);
-      }
       a.ntm = ceil_div(P, 256);
-      return launch(gemm_bf16<256, 64, 64, 64, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm, a, s);
+      if (Q <= 32)
+        return launch(gemm_bf16<256, 32, 64, 32, 32, 3, 2, GROUP_K, EPI, false, false, false>,
+                      E * a.ntm, a, s);
+      return launch(gemm_bf16<256, 64, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false>,
+                    E * a.ntm, a, s);
     }
     if (P >= 256 && Q >= 256) {  // [big, big]: full fine-tuning weight gradients
       a.ntm = ceil_div(P, 128);
       a.ntn = ceil_div(Q, 256);
-      return launch(gemm_bf16<128, 256, 64, 128, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>,
-                    d.E * a.ntm * a.ntn, a, s);
+      return launch(gemm_bf16<128, 256, 64, 128, 32, 3, 2, GROUP_K, EPI, false, false, false>,
+                    E * a.ntm * a.ntn, a, s);
     }
     // [r, big] (or both small)
     a.ntn = ceil_div(Q, 256);
     if (P <= 32) {
       a.ntm = 1;
-      return launch(gemm_bf16<32, 256, 32, 64, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntn, a, s);
+      return launch(gemm_bf16<32, 256, 32, 64, 32, 3, 2, GROUP_K, EPI, false, false, false>,
+                    E * a.ntn, a, s);
     }
     a.ntm = ceil_div(P, 64);
-    return launch(gemm_bf16<64, 256, 64, 64, 32, 3, 2, GROUP_K, EPI_STORE, false, false, false>, d.E * a.ntm * a.ntn, a,
-                  s);
+    return launch(gemm_bf16<64, 256, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false>,
+                  E * a.ntm * a.ntn, a, s);
   }
   a.ntm = ceil_div(P, 64);
   a.ntn = ceil_div(Q, 64);
-  return launch(gemm_f32<GROUP_K, EPI_STORE, false>, d.E * a.ntm * a.ntn, a, s);
+  return launch(gemm_f32<GROUP_K, EPI_STORE, false>, E * a.ntm * a.ntn, a, s);
+}
+
+// split_ws: at least wgrad_split_bytes(d, P, Q) bytes (unused when that is 0).
+hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* Lm, int P,
+                       const void* Rm, int Q, void* out, hipStream_t s, void* split_ws) {
+  GemmArgs a{};
+  a.a[1] = none();
+  a.b[1] = none();
+  a.M = P;
+  a.N = Q;
+  a.scale = 1.0f;
+  a.out_estride = static_cast<int64_t>(P) * Q;
+  a.ld_out = Q;
+  a.a[0] = opnd(Lm, 0, P, 0, P % 8 == 0);
+  a.b[0] = opnd(Rm, 0, Q, 0, Q % 8 == 0);
+  const int S = wgrad_splits(d, P, Q);
+  if (S <= 1) {
+    a.E = d.E;
+    a.offsets = offsets;
+    a.out = out;
+    return weight_grad_launch<EPI_STORE>(d, a, d.E, P, Q, s);
+  }
+  const int G = d.E * S;
+  int32_t* voff = static_cast<int32_t*>(split_ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(split_ws) +
+                                         align_up(static_cast<size_t>(G + 1) * 4));
+  hipLaunchKernelGGL(split_offsets_kernel, dim3(1), dim3(256), 0, s, offsets, d.E, S, voff);
+  a.E = G;
+  a.offsets = voff;
+  a.out = part;
+  hipError_t e = weight_grad_launch<EPI_STORE_F32>(d, a, G, P, Q, s);
+  if (e != hipSuccess) return e;
+  const int64_t PQ = static_cast<int64_t>(P) * Q, total = static_cast<int64_t>(d.E) * PQ;
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  if (d.dtype == MOE_BF16)
+    hipLaunchKernelGGL(reduce_splits_kernel<bf16_t>, grid, dim3(256), 0, s, part,
+                       static_cast<bf16_t*>(out), S, PQ, total);
+  else
+    hipLaunchKernelGGL(reduce_splits_kernel<float>, grid, dim3(256), 0, s, part,
+                       static_cast<float*>(out), S, PQ, total);
+  return hipGetLastError();
 }
 
 #define MOE_TRY(x)                      \
@@ -1363,6 +1466,7 @@ size_t experts_bwd_ws_bytes(const ExpertDims& d) {
   size_t b = tile_ws(nullptr, d).bytes;
   b += align_up(static_cast<size_t>(d.N) * d.r * esz) * 2;        // G B_d, dH B_gu
   b += align_up(static_cast<size_t>(d.N) * 2 * d.I * esz);         // dH
+  b += align_up(lora_wgrad_split_bytes(d));                         // split-K partials
   return b;
 }
 
@@ -1468,6 +1572,8 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
   void* dhb = p;
   p += align_up(static_cast<size_t>(d.N) * r * esz);
   void* dh = p;
+  p += align_up(static_cast<size_t>(d.N) * 2 * I * esz);
+  void* split = p;
 
   MOE_TRY(build_tiles(L, offsets, d.E, s));
   {  // gb = s G B_d      (B_d[e] is [H, r]: K = H rows, r contiguous)
@@ -1499,12 +1605,12 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
   }
   {  // dB_d = G^T u_d  [H, r] ;  dA_d = gb^T act  [r, I]
     TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
-    MOE_TRY(weight_grad(d, offsets, g, H, sv.u_d, r, gr.db_d, s));
-    MOE_TRY(weight_grad(d, offsets, gb, r, sv.act, I, gr.da_d, s));
+    MOE_TRY(weight_grad(d, offsets, g, H, sv.u_d, r, gr.db_d, s, split));
+    MOE_TRY(weight_grad(d, offsets, gb, r, sv.act, I, gr.da_d, s, split));
   }
   if (base) {  // full fine-tuning: dW_d = G^T act  [H, I]
     TimedScope ts(tm, MOE_K_BASE_WGRAD, s);
-    MOE_TRY(weight_grad(d, offsets, g, H, sv.act, I, base->dw_d, s));
+    MOE_TRY(weight_grad(d, offsets, g, H, sv.act, I, base->dw_d, s, nullptr));
   }
   {  // dhb = s dH B_gu   (B_gu[e] is [2I, r])
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
@@ -1534,12 +1640,12 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
   }
   {  // dB_gu = dH^T u_gu  [2I, r] ;  dA_gu = dhb^T X  [r, H]
     TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
-    MOE_TRY(weight_grad(d, offsets, dh, 2 * I, sv.u_gu, r, gr.db_gu, s));
-    MOE_TRY(weight_grad(d, offsets, dhb, r, x_perm, H, gr.da_gu, s));
+    MOE_TRY(weight_grad(d, offsets, dh, 2 * I, sv.u_gu, r, gr.db_gu, s, split));
+    MOE_TRY(weight_grad(d, offsets, dhb, r, x_perm, H, gr.da_gu, s, split));
   }
   if (base) {  // full fine-tuning: dW_gu = dH^T X  [2I, H]
     TimedScope ts(tm, MOE_K_BASE_WGRAD, s);
-    MOE_TRY(weight_grad(d, offsets, dh, 2 * I, x_perm, H, base->dw_gu, s));
+    MOE_TRY(weight_grad(d, offsets, dh, 2 * I, x_perm, H, base->dw_gu, s, nullptr));
   }
   return hipSuccess;
 }

@@ -100,6 +100,12 @@ PARITY_CONFIGS = {
                             dtype="bf16", router="softmax_topk"),
     "mini-f32": LayerConfig("mini-f32", T=333, H=200, I=136, E=5, k=3, r=16,
                             dtype="f32", router="topk_softmax", lora_scale=0.5),
+    # few experts with many rows each: the LoRA weight gradients split every
+    # expert's rows into chunks (one expert empty, skewed counts)
+    "mini-split": LayerConfig("mini-split", T=2000, H=320, I=192, E=4, k=2, r=16,
+                              dtype="bf16", router="sigmoid_topk_renorm", zipf_s=1.2, n_dead=1),
+    "mini-f32-split": LayerConfig("mini-f32-split", T=1500, H=136, I=72, E=2, k=1, r=8,
+                                  dtype="f32", router="softmax_topk"),
 }
 
 
