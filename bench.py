@@ -227,6 +227,52 @@ def cpu_baseline(cfg, inp, sample_tokens, full_ft=False):
             "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
+def bench_merge(mel, cfg, args):
+    """Merged export W' = W + s B A of every expert's gate_up and down weights:
+    HBM-bound (each base weight read once and each merged weight written once;
+    the rank-r product is 2 r FLOPs per element)."""
+    import torch
+    from workloads import make_inputs
+    names = ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")
+    inp = make_inputs(cfg, args.seed, device="cuda", with_dy=False)
+    w = {n: inp[n] for n in names}
+    shape = mel.Shape.of(cfg)
+    ws = torch.empty(max(mel.moe_merge_workspace_bytes(shape), 1), device="cuda",
+                     dtype=torch.uint8)
+    out_gu, out_d = torch.empty_like(w["w_gu"]), torch.empty_like(w["w_d"])
+    for _ in range(args.warmup):
+        mel.moe_merge_lora(shape, w, out_gu, out_d, ws)
+    torch.cuda.synchronize()
+    with mel.kernel_timer() as kt:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            mel.moe_merge_lora(shape, w, out_gu, out_d, ws)
+        b.record()
+        torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    kms, n = kt.read("merge")
+    es = 2 if cfg.dtype == "bf16" else 4
+    base = cfg.E * 3 * cfg.I * cfg.H * es                  # W_gu [E, 2I, H] + W_d [E, H, I]
+    lora = sum(w[n].numel() for n in ("a_gu", "b_gu", "a_d", "b_d")) * es
+    nbytes = 2 * base + lora
+    gbs = nbytes / (ms / 1e3) / 1e9
+    kgbs = nbytes / (kms / n / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "MoE-LoRA merged export (W + s B A, every expert, both projections) GB/s "
+                  "on 1 MI355X; % HBM peak",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}-shaped expert weights, merged export",
+                   "H": cfg.H, "I": cfg.I, "E": cfg.E, "r": cfg.r, "lora_scale": cfg.lora_scale},
+        "roofline": {"bound": "hbm", "kernel": "merge", "achieved": round(kgbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "bytes_per_launch": nbytes,
+                     "ms_per_launch": round(kms / n, 4)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +293,8 @@ def main():
                          "experts, and a shared expert (width --shared-I)")
     ap.add_argument("--shared-I", type=int, default=None,
                     help="shared expert width in --block mode (default I; 0: none)")
+    ap.add_argument("--merge", action="store_true",
+                    help="only time the merged export W + s B A of both projections")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
                     help="only write profiles/traffic_*.json from rocprofv3 counter runs in DIR")
     args = ap.parse_args()
@@ -276,6 +324,9 @@ def main():
     cfg = get_config(args.config or BENCH_CONFIG)
     torch.cuda.set_device(0)
     names = ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")
+    if args.merge:
+        bench_merge(mel, cfg, args)
+        return
     shape = mel.Shape.of(cfg)
     shared_I = None
     if args.block:

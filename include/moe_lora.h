@@ -256,6 +256,22 @@ moe_status moe_router_bwd(const float *d_logits, const void *w_r, int32_t T, int
                           int32_t E, int32_t dtype, void *dx, void *ws, size_t ws_bytes,
                           void *stream);
 
+/* Merged export of the adapters into the base weights, for inference or
+ * saving a merged 16-bit model (the winningdata.io hands-on page, section
+ * "4. Salvando o modelo", saves with the merged 16-bit method), per expert e:
+ *   w_gu_merged[e] = w_gu[e] + s b_gu[e] a_gu[e]     [2I, H]
+ *   w_d_merged[e]  = w_d[e]  + s b_d[e]  a_d[e]      [H, I]
+ * where s = shape->lora_scale. The product is formed in float32 and the sum is
+ * rounded once to `dtype`. Only E, H, I, r, dtype and lora_scale of `shape`
+ * are read (T and k are ignored). Either output may be NULL (that projection
+ * is skipped), and an output may be the base weight itself (in-place merge);
+ * an output may not alias a LoRA parameter or the other projection. ws is the
+ * merge workspace (moe_merge_workspace_bytes). Errors as for the layer calls;
+ * E * max(2I, H) must be below 2^31.  */
+moe_status moe_merge_workspace_bytes(const moe_shape *shape, size_t *ws_bytes);
+moe_status moe_merge_lora(const moe_shape *shape, const moe_weights *weights, void *w_gu_merged,
+                          void *w_d_merged, void *ws, size_t ws_bytes, void *stream);
+
 /* dst[i] += src[i] for i < n, elements of `dtype`, sum in float32, one
  * rounding (adds a shared expert's output to the routed output, and its input
  * gradient to dx). src and dst may not alias.  */
@@ -277,7 +293,7 @@ typedef enum {
   MOE_K_DOWN_FWD = 4, MOE_K_COMBINE = 5, MOE_K_COMBINE_BWD = 6, MOE_K_ROUTE_BWD = 7,
   MOE_K_DOWN_BWD = 8, MOE_K_GATE_UP_BWD = 9, MOE_K_LORA_SIDE = 10, MOE_K_LORA_WGRAD = 11,
   MOE_K_UNPERMUTE = 12, MOE_K_BASE_WGRAD = 13, MOE_K_ROUTER_FWD = 14, MOE_K_ROUTER_BWD = 15,
-  MOE_K_ACCUMULATE = 16, MOE_K_COUNT = 17
+  MOE_K_ACCUMULATE = 16, MOE_K_MERGE = 17, MOE_K_COUNT = 18
 } moe_kernel_id;
 moe_status moe_kernel_timer_enable(int32_t on);
 moe_status moe_kernel_timer_reset(void);

@@ -29,7 +29,8 @@ __all__ = [
     "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
     "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_workspace_bytes_lean",
     "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute", "moe_router_workspace_bytes",
-    "moe_router_fwd", "moe_router_bwd", "moe_accumulate", "kernel_timer", "ROUTER_IDS",
+    "moe_router_fwd", "moe_router_bwd", "moe_accumulate", "moe_merge_workspace_bytes",
+    "moe_merge_lora", "kernel_timer", "ROUTER_IDS",
     "library_path",
 ]
 
@@ -320,6 +321,26 @@ def moe_accumulate(src, dst, stream=None):
     check(_lib.load().moe_accumulate(
         _ABI_DTYPES[key], dst.numel(), _ptr(src, tuple(dst.shape), dt, "src"),
         _ptr(dst, tuple(dst.shape), dt, "dst"), _stream(stream)), "moe_accumulate")
+
+
+def moe_merge_workspace_bytes(shape: Shape) -> int:
+    n = ctypes.c_size_t()
+    check(_lib.load().moe_merge_workspace_bytes(ctypes.byref(shape.c()), ctypes.byref(n)),
+          "moe_merge_workspace_bytes")
+    return n.value
+
+
+def moe_merge_lora(shape: Shape, weights: dict, w_gu_merged=None, w_d_merged=None, ws=None,
+                   stream=None):
+    """Merged export: w_gu_merged = w_gu + s b_gu a_gu, w_d_merged = w_d + s b_d a_d, per
+    expert. Either output may be None (skipped) or the base weight itself (in place)."""
+    E, H, I, dt = shape.E, shape.H, shape.I, shape.torch_dtype
+    wsp, wsb = _ws(ws, moe_merge_workspace_bytes(shape), "ws")
+    check(_lib.load().moe_merge_lora(
+        ctypes.byref(shape.c()), ctypes.byref(_weights(shape, weights)),
+        _ptr(w_gu_merged, (E, 2 * I, H), dt, "w_gu_merged", optional=True),
+        _ptr(w_d_merged, (E, H, I), dt, "w_d_merged", optional=True), wsp, wsb,
+        _stream(stream)), "moe_merge_lora")
 
 
 class kernel_timer:

@@ -14,13 +14,14 @@ ROUTER_IDS = {"softmax_topk": 0, "softmax_topk_renorm": 1, "topk_softmax": 2,
 KERNEL_IDS = {"route": 0, "permute": 1, "gather": 2, "gate_up_fwd": 3, "down_fwd": 4,
               "combine": 5, "combine_bwd": 6, "route_bwd": 7, "down_bwd": 8, "gate_up_bwd": 9,
               "lora_side": 10, "lora_wgrad": 11, "unpermute": 12, "base_wgrad": 13,
-              "router_fwd": 14, "router_bwd": 15, "accumulate": 16}
+              "router_fwd": 14, "router_bwd": 15, "accumulate": 16, "merge": 17}
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
            "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
            "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_workspace_bytes_lean",
            "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute",
            "moe_router_workspace_bytes", "moe_router_fwd", "moe_router_bwd", "moe_accumulate",
+           "moe_merge_workspace_bytes", "moe_merge_lora",
            "moe_status_str",
            "moe_last_error",
            "moe_kernel_timer_enable", "moe_kernel_timer_reset", "moe_kernel_timer_read")
@@ -100,6 +101,10 @@ def load() -> ctypes.CDLL:
         "moe_router_fwd": (st, [P, P, I32, I32, I32, I32, P, P, ctypes.c_size_t, P]),
         "moe_router_bwd": (st, [P, P, I32, I32, I32, I32, P, P, ctypes.c_size_t, P]),
         "moe_accumulate": (st, [I32, ctypes.c_int64, P, P, P]),
+        "moe_merge_workspace_bytes": (st, [ctypes.POINTER(MoeShape),
+                                           ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_merge_lora": (st, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), P, P, P,
+                                ctypes.c_size_t, P]),
         "moe_status_str": (ctypes.c_char_p, [st]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_kernel_timer_enable": (st, [I32]),

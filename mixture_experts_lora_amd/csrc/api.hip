@@ -1,6 +1,7 @@
 // C ABI of the MoE-LoRA expert layer: argument checks, workspace carving and
 // launches on the caller's stream. Declarations and the contract of every
 // entry point are in include/moe_lora.h.
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -466,6 +467,77 @@ moe_status moe_router_bwd(const float* d_logits, const void* w_r, int32_t T, int
   hipError_t e = moe::launch_router_bwd(d_logits, w_r, T, H, E, dtype, dx, ws,
                                         as_stream(stream), moe::active_timer());
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_router_bwd");
+}
+
+namespace {
+
+// The merged export needs only the weight shapes: T and k are not read.
+moe_status check_merge_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_ERR_INVALID_ARG, "null shape");
+  if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_INVALID_ARG, "E must be in [1, 1024]");
+  if (s->H < 1 || s->I < 1) return fail(MOE_ERR_INVALID_ARG, "H and I must be >= 1");
+  if (s->r < 1) return fail(MOE_ERR_INVALID_ARG, "r must be >= 1");
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype " + std::to_string(s->dtype));
+  if (s->H % 8 != 0 || s->I % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 8");
+  if (s->r > 64) return fail(MOE_ERR_UNSUPPORTED, "r > 64 is not supported");
+  if (int64_t(s->E) * std::max(2 * int64_t(s->I), int64_t(s->H)) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_INVALID_ARG, "E * max(2I, H) must be < 2^31");
+  return MOE_OK;
+}
+
+moe::ExpertDims merge_dims_of(const moe_shape* s) {
+  moe::ExpertDims d{};
+  d.N = 0;
+  d.H = s->H;
+  d.I = s->I;
+  d.E = s->E;
+  d.r = s->r;
+  d.dtype = s->dtype;
+  d.scale = s->lora_scale;
+  return d;
+}
+
+}  // namespace
+
+moe_status moe_merge_workspace_bytes(const moe_shape* shape, size_t* ws_bytes) {
+  moe_status st = check_merge_shape(shape);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(ws_bytes);
+  *ws_bytes = moe::merge_ws_bytes(merge_dims_of(shape));
+  return MOE_OK;
+}
+
+moe_status moe_merge_lora(const moe_shape* shape, const moe_weights* weights, void* w_gu_merged,
+                          void* w_d_merged, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_merge_shape(shape);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(weights);
+  CHECK_PTR(weights->w_gu);
+  CHECK_PTR(weights->a_gu);
+  CHECK_PTR(weights->b_gu);
+  CHECK_PTR(weights->w_d);
+  CHECK_PTR(weights->a_d);
+  CHECK_PTR(weights->b_d);
+  CHECK_PTR(ws);
+  if (!w_gu_merged && !w_d_merged)
+    return fail(MOE_ERR_INVALID_ARG, "no output: w_gu_merged and w_d_merged are both NULL");
+  const void* lora[4] = {weights->a_gu, weights->b_gu, weights->a_d, weights->b_d};
+  for (const void* q : lora)
+    if (q == w_gu_merged || q == w_d_merged)
+      return fail(MOE_ERR_INVALID_ARG, "a merged output aliases a LoRA parameter");
+  if (w_gu_merged && (w_gu_merged == w_d_merged || w_gu_merged == weights->w_d))
+    return fail(MOE_ERR_INVALID_ARG, "w_gu_merged aliases the down projection");
+  if (w_d_merged && w_d_merged == weights->w_gu)
+    return fail(MOE_ERR_INVALID_ARG, "w_d_merged aliases the gate_up projection");
+  const moe::ExpertDims d = merge_dims_of(shape);
+  const size_t need = moe::merge_ws_bytes(d);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "merge workspace needs " + std::to_string(need) + " bytes");
+  hipError_t e = moe::launch_merge(d, *weights, w_gu_merged, w_d_merged, ws, as_stream(stream),
+                                   moe::active_timer());
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_merge_lora");
 }
 
 moe_status moe_accumulate(int32_t dtype, int64_t n, const void* src, void* dst, void* stream) {

@@ -46,8 +46,9 @@ namespace moe {
 namespace {
 
 enum Mode { GROUP_M = 0, GROUP_K = 1 };
-// EPI_STORE_F32: float32 output (router logits); EPI_ADD: out += result (bf16
-// read-modify-write, the sum formed in float32, one rounding).
+// EPI_STORE_F32: float32 output (router logits); EPI_ADD: out = src + result
+// with src = aux when given (merged export: W + s B A) else out itself (an
+// accumulate); the sum formed in float32, one rounding.
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2, EPI_STORE_F32 = 3, EPI_ADD = 4 };
 
 struct Opnd {
@@ -141,10 +142,11 @@ __device__ __forceinline__ void epi_store(const GemmArgs& p, int e, int64_t row0
     if (EPI == EPI_STORE || EPI == EPI_STORE_F32 || EPI == EPI_ADD) {
       float o[4];
       T* rp = static_cast<T*>(p.out) + row * p.ld_out;
+      const T* sp = EPI == EPI_ADD && p.aux ? static_cast<const T*>(p.aux) + row * p.ld_aux : rp;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         o[j] = v[j] * p.scale;
-        if (EPI == EPI_ADD && n_col + j < p.N) o[j] += to_f32<T>(rp[n_col + j]);
+        if (EPI == EPI_ADD && n_col + j < p.N) o[j] += to_f32<T>(sp[n_col + j]);
       }
       store4<T>(rp, n_col, p.N, (p.ld_out & 3) == 0, o);
     } else if (EPI == EPI_SWIGLU_BWD) {
@@ -875,6 +877,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
                        (p.out_estride & 7) == 0;
   const bool out_vec4 = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0 && (p.ld_out & 3) == 0 &&
                         (p.out_estride & 3) == 0;
+  const bool aux_vec = p.aux == nullptr ||
+                       ((reinterpret_cast<uintptr_t>(p.aux) & 15) == 0 && (p.ld_aux & 7) == 0);
 #pragma unroll
   for (int mi = 0; mi < MF; ++mi) {
     if (mi) wave_lds_sync();  // previous slab fully read
@@ -955,10 +959,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
                            ? static_cast<bf16_t*>(p.out) + (row0 + m_local) * p.ld_out
                            : static_cast<bf16_t*>(p.out) + static_cast<int64_t>(e) * p.out_estride +
                                  static_cast<int64_t>(m0 + m_local) * p.ld_out;
-          if (out_vec && col + 8 <= p.N) {
+          // EPI_ADD source row: aux (merged export) or the output row itself
+          const bf16_t* sp = EPI == EPI_ADD && p.aux
+                                 ? static_cast<const bf16_t*>(p.aux) + (row0 + m_local) * p.ld_aux
+                                 : rp;
+          if (out_vec && col + 8 <= p.N && (EPI != EPI_ADD || aux_vec)) {
             if (EPI == EPI_ADD) {
               float o[8];
-              load8(rp + col, o);
+              load8(sp + col, o);
 #pragma unroll
               for (int j = 0; j < 8; ++j) v[j] += o[j];
             }
@@ -967,7 +975,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
 #pragma unroll
             for (int j = 0; j < 8; ++j)
               if (col + j < p.N)
-                rp[col + j] = f32_to_bf16(EPI == EPI_ADD ? v[j] + bf16_to_f32(rp[col + j]) : v[j]);
+                rp[col + j] = f32_to_bf16(EPI == EPI_ADD ? v[j] + bf16_to_f32(sp[col + j]) : v[j]);
           }
         }
       }
@@ -1795,6 +1803,87 @@ hipError_t launch_router_bwd(const float* d_logits, const void* w_r, int T, int 
   a.ntn = ceil_div(H, 64);
   return launch(gemm_f32<GROUP_M, EPI_ADD, false>,
                 static_cast<int>(tile_cap(T, 1, R.L.small.bm)) * a.ntn, a, s);
+}
+
+// ----------------------------------------------------------------- merged export
+// W'[e] = W[e] + s B[e] A[e] for both stacked projections, as grouped GEMMs
+// whose "tokens" are the output rows of each expert's weight (2I for gate_up,
+// H for down; K = r) and whose epilogue adds the base weight read from aux.
+namespace {
+
+__global__ void uniform_offsets_kernel(int32_t* off, int E, int rows) {
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) off[e] = e * rows;
+}
+
+struct MergeWs {
+  int32_t* offsets;
+  WsLayout L;
+  size_t bytes;
+};
+
+MergeWs merge_ws(void* ws, const ExpertDims& d) {
+  MergeWs M;
+  char* p = static_cast<char*>(ws);
+  M.offsets = reinterpret_cast<int32_t*>(p);
+  size_t off = align_up(static_cast<size_t>(d.E + 1) * 4);
+  M.L = tile_ws(p ? p + off : nullptr, d);
+  M.bytes = off + align_up(M.L.bytes);
+  return M;
+}
+
+// rows of one expert's output, dims of the workspace-sizing view
+ExpertDims merge_dims(const ExpertDims& d, int rows) {
+  ExpertDims m = d;
+  m.N = d.E * rows;
+  return m;
+}
+
+hipError_t merge_one(const ExpertDims& d, int rows, int cols, const void* w, const void* a,
+                     const void* b, void* out, void* ws, hipStream_t s) {
+  const ExpertDims m = merge_dims(d, rows);
+  const MergeWs M = merge_ws(ws, m);
+  hipLaunchKernelGGL(uniform_offsets_kernel, dim3(1), dim3(256), 0, s, M.offsets, d.E, rows);
+  MOE_TRY(build_tiles(M.L, M.offsets, d.E, s));
+  GemmArgs g{};
+  g.a[1] = none();
+  g.b[1] = none();
+  g.E = d.E;
+  g.offsets = M.offsets;
+  g.tiles = M.L.small.tiles;
+  g.ntiles = M.L.small.ntiles;
+  g.a[0] = opnd(b, 0, d.r, 1, d.r % 8 == 0);                               // B rows: [rows, r]
+  g.b[0] = opnd(a, static_cast<int64_t>(d.r) * cols, cols, 0, true);      // A[e]: [K = r][N = cols]
+  g.K[0] = d.r;
+  g.K[1] = 0;
+  g.N = cols;
+  g.out = out;
+  g.ld_out = cols;
+  g.aux = w;
+  g.ld_aux = cols;
+  g.scale = d.scale;
+  const int grid_m = static_cast<int>(tile_cap(m.N, d.E, M.L.small.bm));
+  if (d.dtype == MOE_BF16) {
+    g.ntn = ceil_div(cols, 256);
+    return launch(gemm_bf16<128, 256, 64, 128, 32, 3, 2, GROUP_M, EPI_ADD, false, true, false>,
+                  grid_m * g.ntn, g, s);
+  }
+  g.ntn = ceil_div(cols, 64);
+  return launch(gemm_f32<GROUP_M, EPI_ADD, false>, grid_m * g.ntn, g, s);
+}
+
+}  // namespace
+
+size_t merge_ws_bytes(const ExpertDims& d) {
+  return std::max(merge_ws(nullptr, merge_dims(d, 2 * d.I)).bytes,
+                  merge_ws(nullptr, merge_dims(d, d.H)).bytes);
+}
+
+hipError_t launch_merge(const ExpertDims& d, const moe_weights& w, void* w_gu_out, void* w_d_out,
+                        void* ws, hipStream_t s, KernelTimer* tm) {
+  TimedScope ts(tm, MOE_K_MERGE, s);
+  if (w_gu_out) MOE_TRY(merge_one(d, 2 * d.I, d.H, w.w_gu, w.a_gu, w.b_gu, w_gu_out, ws, s));
+  if (w_d_out) MOE_TRY(merge_one(d, d.H, d.I, w.w_d, w.a_d, w.b_d, w_d_out, ws, s));
+  return hipSuccess;
 }
 
 hipError_t launch_accumulate(int dtype, int64_t n, const void* src, void* dst, hipStream_t s,

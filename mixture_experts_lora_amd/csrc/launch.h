@@ -87,6 +87,11 @@ hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, cons
                                         const moe_lora_grads& gr, const moe_base_grads* base,
                                         void* ws, hipStream_t s, KernelTimer* tm);
 
+// ---- merged export W + s B A (per expert, both projections; either output may be NULL)
+size_t merge_ws_bytes(const ExpertDims& d);
+hipError_t launch_merge(const ExpertDims& d, const moe_weights& w, void* w_gu_out, void* w_d_out,
+                        void* ws, hipStream_t s, KernelTimer* tm);
+
 // ---- router projection and element-wise accumulate
 size_t router_ws_bytes(int T, int E, int dtype);
 hipError_t launch_router_fwd(const void* x, const void* w_r, int T, int H, int E, int dtype,

@@ -6,6 +6,6 @@ package. It shares no code with the HIP library and imports nothing from it.
 from . import moe_oracle, accounting  # noqa: F401
 from .moe_oracle import (ROUTERS, route, route_backward, permute, gather_rows,  # noqa: F401
                          expert_forward, expert_backward, combine, combine_backward,
-                         layer_forward, layer_backward, merged_forward,
+                         layer_forward, layer_backward, merged_forward, merge_lora,
                          layer_forward_backward, router_logits, router_input_grad,
                          layer_with_router_and_shared)

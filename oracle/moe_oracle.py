@@ -337,6 +337,19 @@ def layer_backward(dY, cache, base_grads=False):
     return out
 
 
+def merge_lora(weights, s=1.0, dtype=np.float32):
+    """Merged export: every expert's adapter folded into its base weight,
+    W' = W + s B A for gate_up ([2I, H]) and down ([H, I]), as a model saved in
+    merged 16-bit form carries them (winningdata.io hands-on page, section
+    "4. Salvando o modelo"). Returns {"w_gu": [E, 2I, H], "w_d": [E, H, I]}."""
+    out = {}
+    for name, a, b in (("w_gu", "a_gu", "b_gu"), ("w_d", "a_d", "b_d")):
+        W = np.asarray(weights[name], dtype)
+        A, B = np.asarray(weights[a], dtype), np.asarray(weights[b], dtype)
+        out[name] = np.stack([W[e] + dtype(s) * (B[e] @ A[e]) for e in range(W.shape[0])])
+    return out
+
+
 def merged_forward(x, logits, weights, k, router, s=1.0, dtype=np.float32):
     """The PEFT-merge order the [moe] page contrasts with ("Faster LoRA MoE
     training"): form W' = W + s B A for every expert, then run the plain MoE.
@@ -349,14 +362,12 @@ def merged_forward(x, logits, weights, k, router, s=1.0, dtype=np.float32):
     ids, w = route(logits, k, router, dtype)
     counts, offsets, sorted_pair, inv_pos = permute(ids, E)
     y_perm = np.zeros((T * k, H), dtype=dtype)
+    merged = merge_lora(weights, s, dtype)
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if lo == hi:
             continue
-        W1 = np.asarray(weights["w_gu"][e], dtype) + dtype(s) * (
-            np.asarray(weights["b_gu"][e], dtype) @ np.asarray(weights["a_gu"][e], dtype))
-        W2 = np.asarray(weights["w_d"][e], dtype) + dtype(s) * (
-            np.asarray(weights["b_d"][e], dtype) @ np.asarray(weights["a_d"][e], dtype))
+        W1, W2 = merged["w_gu"][e], merged["w_d"][e]
         X_e = x[sorted_pair[lo:hi] // k]
         h = X_e @ W1.T
         I = W1.shape[0] // 2

@@ -186,6 +186,34 @@ def test_router_and_accumulate_validate(lib):
     assert lib.moe_accumulate(1, 16, fake, fake, None) == 1
 
 
+def test_merge_validates(lib):
+    """Merged export: shape, outputs, aliasing and workspace checked on the host."""
+    P = ctypes.c_void_p
+    from mixture_experts_lora_amd._lib import MoeShape, MoeWeights
+    sh = MoeShape(0, 2880, 2880, 32, 0, 16, 1, 1.0)      # T and k are not read
+    n = ctypes.c_size_t()
+    assert lib.moe_merge_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)) == 0
+    need = n.value
+    assert 0 < need < (1 << 20)
+    w = MoeWeights(*(0x10000 + i * 0x1000 for i in range(6)))   # w_gu a_gu b_gu w_d a_d b_d
+    ws = P(0x90000)
+    args = (ctypes.byref(sh), ctypes.byref(w))
+    assert lib.moe_merge_lora(*args, None, None, ws, need, None) == 1          # nothing to do
+    assert lib.moe_merge_lora(*args, P(0x80000), None, ws, need - 1, None) == 3
+    assert lib.moe_merge_lora(*args, P(0x11000), None, ws, need, None) == 1    # a_gu
+    assert lib.moe_merge_lora(*args, None, P(0x15000), ws, need, None) == 1    # b_d
+    assert lib.moe_merge_lora(*args, P(0x13000), None, ws, need, None) == 1    # w_d
+    assert lib.moe_merge_lora(*args, P(0x80000), P(0x80000), ws, need, None) == 1
+    assert lib.moe_merge_lora(*args, None, P(0x10000), ws, need, None) == 1    # w_gu
+    assert lib.moe_merge_lora(*args, P(0x80000), None, None, need, None) == 1
+    bad = MoeShape(0, 2882, 2880, 32, 0, 16, 1, 1.0)
+    assert lib.moe_merge_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == 2
+    bad = MoeShape(0, 2880, 2880, 32, 0, 65, 1, 1.0)
+    assert lib.moe_merge_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == 2
+    bad = MoeShape(0, 2880, 2880, 0, 0, 16, 1, 1.0)
+    assert lib.moe_merge_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == 1
+
+
 def test_aliasing_rejected(lib):
     P = ctypes.c_void_p
     fake = P(0x10000)

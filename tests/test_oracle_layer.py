@@ -49,6 +49,22 @@ def test_split_equals_merged(router, s):
     assert np.abs(Y - Ym).max() <= 1e-12 * np.abs(Y).max()
 
 
+def test_merge_of_zero_b_is_the_base_weight_and_rank_one_is_an_outer_product():
+    d = rand_layer(T=4, H=24, I=12, E=3, k=2, r=1, router="softmax_topk", seed=6)
+    m0 = oracle.merge_lora({**d, "b_gu": 0 * d["b_gu"], "b_d": 0 * d["b_d"]}, 1.7, np.float64)
+    np.testing.assert_array_equal(m0["w_gu"], d["w_gu"])
+    np.testing.assert_array_equal(m0["w_d"], d["w_d"])
+    m = oracle.merge_lora(d, 1.7, np.float64)
+    for e in range(3):
+        np.testing.assert_allclose(
+            m["w_gu"][e], d["w_gu"][e] + 1.7 * np.outer(d["b_gu"][e][:, 0], d["a_gu"][e][0]),
+            rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(
+            m["w_d"][e], d["w_d"][e] + 1.7 * np.outer(d["b_d"][e][:, 0], d["a_d"][e][0]),
+            rtol=1e-14, atol=1e-15)
+    assert m["w_gu"].shape == d["w_gu"].shape and m["w_d"].shape == d["w_d"].shape
+
+
 def test_split_equals_merged_on_tiny_config():
     cfg = LayerConfig("t", T=256, H=256, I=128, E=8, k=2, r=8, dtype="f32", router="softmax_topk")
     d = {n: to_numpy(v) for n, v in make_inputs(cfg, 3).items()}

@@ -65,6 +65,10 @@ MUTATIONS = [
      "return np.asarray(dlogits, dtype) @ np.asarray(w_r, dtype) * 0.5"),
     ("shared_output_dropped", 'Y = Y + f["y"]', "Y = Y"),
     ("shared_dx_dropped", 'g["dx"] = g["dx"] + b["dx"]', 'g["dx"] = g["dx"]'),
+    ("merge_scale_dropped", "out[name] = np.stack([W[e] + dtype(s) * (B[e] @ A[e])",
+     "out[name] = np.stack([W[e] + (B[e] @ A[e])"),
+    ("merge_base_dropped", "out[name] = np.stack([W[e] + dtype(s) * (B[e] @ A[e])",
+     "out[name] = np.stack([dtype(s) * (B[e] @ A[e])"),
 ]
 
 # Runs the pin tests with the oracle package taken from argv[1].
