@@ -13,7 +13,7 @@ value    = algorithmic TFLOP/s of the step, F = 12 N H I + 6 N r (2H + 3I)
            formed), over the mean step time of the timed region.
 roofline = the dominant GEMM kernel's algorithmic FLOPs per launch over its
            mean launch time, timed live with HIP events on the launch stream
-           by the library's kernel timer, against the dense bf16 MFMA peak.
+           by the library's kernel timer, against the dense bf16 (= fp16) MFMA peak.
 cpu_baseline = the CPU oracle (NumPy float32 per-expert loop) on a bounded
            sample of the same workload, on the host's cores.
 hbm      = the memory-bound kernels' algorithmic bytes per launch over their
@@ -57,7 +57,7 @@ def kernel_flops(name, cfg):
 def kernel_bytes(name, cfg):
     """Algorithmic HBM bytes of one launch of a memory-bound kernel (each tensor once)."""
     T, H, E, k, N = cfg.T, cfg.H, cfg.E, cfg.k, cfg.N
-    es = 2 if cfg.dtype == "bf16" else 4
+    es = 4 if cfg.dtype == "f32" else 2
     return {
         "route": T * E * 4 + T * k * 8,                        # logits in; ids, weights out
         "permute": N * 4 * 3 + (2 * E + 1) * 4,                # ids in; sorted_pair, inv_pos, counts
@@ -112,12 +112,12 @@ def traffic_for(kernel, workload):
 
 
 def classify_gemm(kernel_name):
-    """Map a profiler kernel name of the bf16 grouped GEMM to the step it runs."""
+    """Map a profiler kernel name of the 16-bit grouped GEMM to the step it runs."""
     import re
-    m = re.search(r"gemm_bf16<([^>]*)>", kernel_name)
+    m = re.search(r"gemm16<([^>]*)>", kernel_name)
     if not m:
         return None
-    a = [x.strip() for x in m.group(1).split(",")]
+    a = [x.strip() for x in m.group(1).split(",")][1:]     # drop the F16 flag
     bm, bn, mode, epi, b_kc = int(a[0]), int(a[1]), int(a[7]), int(a[8]), a[11] == "true"
     if mode != 0 or bn < 128 or epi > 2:
         return None  # LoRA side products, weight gradients, router projection
@@ -252,7 +252,7 @@ def bench_merge(mel, cfg, args):
         torch.cuda.synchronize()
     ms = a.elapsed_time(b) / args.steps
     kms, n = kt.read("merge")
-    es = 2 if cfg.dtype == "bf16" else 4
+    es = 4 if cfg.dtype == "f32" else 2
     base = cfg.E * 3 * cfg.I * cfg.H * es                  # W_gu [E, 2I, H] + W_d [E, H, I]
     lora = sum(w[n].numel() for n in ("a_gu", "b_gu", "a_d", "b_d")) * es
     nbytes = 2 * base + lora
@@ -391,8 +391,8 @@ def main():
 
     F = step_flops(cfg, args.full_ft, shared_I, args.block)
     tflops = F / (ms / 1e3) / 1e12
-    bf16 = cfg.dtype == "bf16"
-    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    half = cfg.dtype in ("bf16", "f16")      # dense bf16 and fp16 MFMA peaks are equal
+    peak = PEAK_BF16_TFLOPS if half else PEAK_F32_TFLOPS
     dom = max((k for k in GEMM_KERNELS if k in kms), key=lambda k: kms[k]["ms_per_step"])
     # FLOPs of the dominant kernel per step (block mode: its routed and shared
     # launches together) over its summed launch time per step
@@ -420,7 +420,7 @@ def main():
         "ms_median": round(step_ms[len(step_ms) // 2], 4), "ms_min": round(step_ms[0], 4),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
+        "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}-shaped MoE-LoRA "
                                + ("block (router projection, routed experts"
                                   + (f", shared expert of width {shared_I})" if shared_I else ")")

@@ -35,8 +35,13 @@
  *    token, r LoRA rank, N = T * k routed rows.
  *  - dtype (moe_shape.dtype) is the element type of x, the weights, the LoRA
  *    parameters, the saved activations, Y, dY, dX and the LoRA gradients:
- *    MOE_F32 (float) or MOE_BF16 (bfloat16). Router logits, combine weights
- *    and their gradients are always float32; indices are int32.
+ *    MOE_F32 (float), MOE_BF16 (bfloat16) or MOE_F16 (IEEE half, for parts
+ *    whose grouped GEMM runs in float16: the faster-moe page's
+ *    acknowledgements section credits float16 grouped_mm support for T4
+ *    and A100). The 16-bit types share every kernel: only the MFMA
+ *    instruction and the rounding of stored values differ. Products
+ *    accumulate in float32. Router logits, combine weights and their
+ *    gradients are always float32; indices are int32.
  *  - Outputs are fully overwritten (gradients are not accumulated into).
  *  - Arguments are checked before anything is enqueued. Errors:
  *      MOE_ERR_INVALID_ARG   a NULL pointer that is not optional, T < 1,
@@ -68,7 +73,7 @@ typedef enum {
   MOE_ERR_HIP = 4
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
 
 /* Router modes (how combine weights follow from the logits of the k chosen
  * experts; the choice itself is always the k largest logits, ties to the

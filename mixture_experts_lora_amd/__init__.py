@@ -34,8 +34,8 @@ __all__ = [
     "library_path",
 ]
 
-_TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
-_ABI_DTYPES = {"f32": _lib.MOE_F32, "bf16": _lib.MOE_BF16}
+_TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+_ABI_DTYPES = {"f32": _lib.MOE_F32, "bf16": _lib.MOE_BF16, "f16": _lib.MOE_F16}
 
 
 def library_path() -> str:
@@ -50,7 +50,7 @@ class Shape:
     E: int
     k: int
     r: int
-    dtype: str = "bf16"       # "bf16" or "f32"
+    dtype: str = "bf16"       # "bf16", "f16" or "f32"
     lora_scale: float = 1.0
 
     @property
@@ -281,7 +281,7 @@ def _dtype_of(t, name):
     for key, dt in _TORCH_DTYPES.items():
         if t.dtype == dt:
             return key, dt
-    raise ValueError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+    raise ValueError(f"{name} must be float32, bfloat16 or float16, got {t.dtype}")
 
 
 def moe_router_workspace_bytes(T: int, H: int, E: int, dtype: str) -> int:

@@ -8,7 +8,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_lora.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_F16 = 0, 1, 2
 ROUTER_IDS = {"softmax_topk": 0, "softmax_topk_renorm": 1, "topk_softmax": 2,
               "sigmoid_topk_renorm": 3}
 KERNEL_IDS = {"route": 0, "permute": 1, "gather": 2, "gate_up_fwd": 3, "down_fwd": 4,

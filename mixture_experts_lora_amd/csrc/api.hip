@@ -47,7 +47,7 @@ moe_status check_shape(const moe_shape* s) {
   if (st != MOE_OK) return st;
   if (s->H < 1 || s->I < 1) return fail(MOE_ERR_INVALID_ARG, "H and I must be >= 1");
   if (s->r < 1) return fail(MOE_ERR_INVALID_ARG, "r must be >= 1");
-  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16)
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_F16)
     return fail(MOE_ERR_INVALID_ARG, "unknown dtype " + std::to_string(s->dtype));
   if (s->H % 8 != 0 || s->I % 8 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 8");
@@ -220,7 +220,7 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, const vo
                                      static_cast<int32_t*>(ws), s, tm);
   if (e != hipSuccess) return hip_fail(e, "moe_permute");
   if (x_perm) {
-    const int64_t row_bytes = int64_t(d.H) * (d.dtype == MOE_BF16 ? 2 : 4);
+    const int64_t row_bytes = int64_t(d.H) * (d.dtype == MOE_F32 ? 4 : 2);
     e = moe::launch_gather(x, sorted_pair, offsets, d.E, shape->k, d.N, row_bytes, x_perm, s, tm);
     if (e != hipSuccess) return hip_fail(e, "moe_permute(gather)");
   }
@@ -417,7 +417,8 @@ namespace {
 moe_status check_router_dims(int32_t T, int32_t H, int32_t E, int32_t dtype) {
   if (T < 1 || H < 1 || E < 1 || E > 1024)
     return fail(MOE_ERR_INVALID_ARG, "need T >= 1, H >= 1, 1 <= E <= 1024");
-  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_F16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (H % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "H must be a multiple of 8");
   return MOE_OK;
 }
@@ -477,7 +478,7 @@ moe_status check_merge_shape(const moe_shape* s) {
   if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_INVALID_ARG, "E must be in [1, 1024]");
   if (s->H < 1 || s->I < 1) return fail(MOE_ERR_INVALID_ARG, "H and I must be >= 1");
   if (s->r < 1) return fail(MOE_ERR_INVALID_ARG, "r must be >= 1");
-  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16)
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_F16)
     return fail(MOE_ERR_INVALID_ARG, "unknown dtype " + std::to_string(s->dtype));
   if (s->H % 8 != 0 || s->I % 8 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 8");
@@ -541,7 +542,8 @@ moe_status moe_merge_lora(const moe_shape* shape, const moe_weights* weights, vo
 }
 
 moe_status moe_accumulate(int32_t dtype, int64_t n, const void* src, void* dst, void* stream) {
-  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_F16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (n < 0) return fail(MOE_ERR_INVALID_ARG, "n < 0");
   if (n == 0) return MOE_OK;
   CHECK_PTR(src);

@@ -38,6 +38,26 @@ template <> struct Pack<bf16_t> {
     return make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
+template <> struct Pack<f16_t> {
+  static constexpr int n = 8;
+  __device__ static void unpack(const uint4& r, float (&v)[8]) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = static_cast<float>(__builtin_bit_cast(f16_t, static_cast<uint16_t>(w[i])));
+      v[2 * i + 1] = static_cast<float>(__builtin_bit_cast(f16_t, static_cast<uint16_t>(w[i] >> 16)));
+    }
+  }
+  __device__ static uint4 pack(const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<f16_t>(v[2 * i]))) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<f16_t>(v[2 * i + 1])))
+              << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
 template <> struct Pack<float> {
   static constexpr int n = 4;
   __device__ static void unpack(const uint4& r, float (&v)[4]) {
@@ -121,13 +141,17 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
 
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos, const float* w,
                           int T, int k, int H, void* y, hipStream_t s, KernelTimer* tm) {
-  const int esz = dtype == MOE_BF16 ? 2 : 4;
+  const int esz = dtype == MOE_F32 ? 4 : 2;
   const int64_t cpr = static_cast<int64_t>(H) * esz / 16;
   const int64_t total = static_cast<int64_t>(T) * cpr;
   dim3 grid(static_cast<unsigned>((total + 255) / 256));
   TimedScope scope(tm, w ? MOE_K_COMBINE : MOE_K_UNPERMUTE, s);
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint4*>(y_perm), inv_pos, w, T, k, cpr,
+                       static_cast<uint4*>(y));
+  else if (dtype == MOE_F16)
+    hipLaunchKernelGGL(combine_kernel<f16_t>, grid, dim3(256), 0, s,
                        static_cast<const uint4*>(y_perm), inv_pos, w, T, k, cpr,
                        static_cast<uint4*>(y));
   else
@@ -140,11 +164,15 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos,
 hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_exp,
                               const int32_t* inv_pos, const float* w, int T, int k, int H,
                               void* g, float* dw, hipStream_t s, KernelTimer* tm) {
-  const int esz = dtype == MOE_BF16 ? 2 : 4;
+  const int esz = dtype == MOE_F32 ? 4 : 2;
   const int64_t cpr = static_cast<int64_t>(H) * esz / 16;
   TimedScope scope(tm, MOE_K_COMBINE_BWD, s);
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(T), dim3(256), 0, s,
+                       static_cast<const uint4*>(dy), static_cast<const uint4*>(y_exp), inv_pos,
+                       w, k, cpr, static_cast<uint4*>(g), dw);
+  else if (dtype == MOE_F16)
+    hipLaunchKernelGGL(combine_bwd_kernel<f16_t>, dim3(T), dim3(256), 0, s,
                        static_cast<const uint4*>(dy), static_cast<const uint4*>(y_exp), inv_pos,
                        w, k, cpr, static_cast<uint4*>(g), dw);
   else

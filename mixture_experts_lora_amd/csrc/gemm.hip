@@ -78,6 +78,7 @@ struct GemmArgs {
   int64_t ld_aux;
   int I;  // gate width for SwiGLU epilogues / paired weight rows
   float scale;
+  int dtype;  // host side only: MOE_BF16 or MOE_F16 picks the 16-bit kernel
 };
 
 // Spread `total` logical tiles over the 8 XCDs so that each XCD works on a
@@ -467,25 +468,54 @@ __device__ __forceinline__ void read8_interleaved(const char* slab, int r, int s
   }
 }
 
-// Eight consecutive bf16 as one 16-byte global access (16-byte aligned).
+// ---- the two 16-bit storage formats: bfloat16 and IEEE half, both held as
+// raw 16-bit words (the tiles, DMA and LDS layouts do not care which); F16
+// selects the MFMA instruction and the conversions of the epilogue.
+template <bool F16>
+__device__ __forceinline__ float h16_to_f32(uint16_t v) {
+  if constexpr (F16) return static_cast<float>(__builtin_bit_cast(_Float16, v));
+  else return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+template <bool F16>
+__device__ __forceinline__ uint16_t f32_to_h16(float f) {  // round to nearest even
+  if constexpr (F16) return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+  else return f32_to_bf16(f);
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// acc += A B^T on a 32 x 32 tile, k = 16 (bfloat16 or half operands, float32 accumulate)
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight consecutive 16-bit values as one 16-byte global access (16-byte aligned).
 // Epilogue traffic is streamed once: non-temporal loads and stores keep it
 // from evicting the operand tiles the other blocks are reading from L2.
+template <bool F16>
 __device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
   const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   const uint32_t w[4] = {r[0], r[1], r[2], r[3]};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    v[2 * j] = __uint_as_float(w[j] << 16);
-    v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    v[2 * j] = h16_to_f32<F16>(static_cast<uint16_t>(w[j] & 0xffffu));
+    v[2 * j + 1] = h16_to_f32<F16>(static_cast<uint16_t>(w[j] >> 16));
   }
 }
 
+template <bool F16>
 __device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
   uint32_t w[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    w[j] = static_cast<uint32_t>(f32_to_bf16(v[2 * j])) |
-           (static_cast<uint32_t>(f32_to_bf16(v[2 * j + 1])) << 16);
+    w[j] = static_cast<uint32_t>(f32_to_h16<F16>(v[2 * j])) |
+           (static_cast<uint32_t>(f32_to_h16<F16>(v[2 * j + 1])) << 16);
   u32x4 q;
   q[0] = w[0];
   q[1] = w[1];
@@ -498,9 +528,9 @@ __device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
 // before its lanes read what other lanes wrote.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int BM, int BN, int WM, int WN, int BK, int NST, int MINB, int MODE, int EPI,
-          bool PAIRED, bool A_KC, bool B_KC, int VST = 0>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(GemmArgs p) {
+template <bool F16, int BM, int BN, int WM, int WN, int BK, int NST, int MINB, int MODE, int EPI,
+          bool PAIRED, bool A_KC, bool B_KC, int VST>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmArgs p) {
   constexpr int WAVES_N = BN / WN, MF = WM / 32, NF = WN / 32;
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, ST = A_BYTES + B_BYTES;
@@ -777,8 +807,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
         for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
           for (int ni = 0; ni < NF; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][ni], af[cur][mi],
-                                                                  acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
       }
     };
     for (int it = 0; it < nk; it += NRB) {
@@ -853,8 +882,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
         for (int mi = 0; mi < MF; ++mi)
   #pragma unroll
           for (int ni = 0; ni < NF; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][ni], af[cur][mi],
-                                                                  acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
       }
     }
 
@@ -909,9 +937,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
           for (int j = 0; j < 8; ++j) a[j] = swiglu(g[j], u[j]);
           const int64_t row = row0 + m_local;
           bf16_t* hr = static_cast<bf16_t*>(p.out) + row * p.ld_out;
-          store8(hr + f, g);
-          store8(hr + p.I + f, u);
-          store8(static_cast<bf16_t*>(p.out2) + row * p.ld_out2 + f, a);
+          store8<F16>(hr + f, g);
+          store8<F16>(hr + p.I + f, u);
+          store8<F16>(static_cast<bf16_t*>(p.out2) + row * p.ld_out2 + f, a);
         }
       }
     } else {
@@ -929,13 +957,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
           const int64_t row = row0 + m_local;
           const bf16_t* hr = static_cast<const bf16_t*>(p.aux) + row * p.ld_aux;
           float g[8], u[8], dg[8], du[8];
-          load8(hr + col, g);
-          load8(hr + p.I + col, u);
+          load8<F16>(hr + col, g);
+          load8<F16>(hr + p.I + col, u);
 #pragma unroll
           for (int j = 0; j < 8; ++j) swiglu_bwd(g[j], u[j], v[j], dg[j], du[j]);
           bf16_t* dr = static_cast<bf16_t*>(p.out) + row * p.ld_out;
-          store8(dr + col, dg);
-          store8(dr + p.I + col, du);
+          store8<F16>(dr + col, dg);
+          store8<F16>(dr + p.I + col, du);
         } else if (EPI == EPI_STORE_F32) {
           // GROUP_M: router logits; GROUP_K: split-K partial weight gradients
           float* rp = MODE == GROUP_M
@@ -966,16 +994,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_bf16(Ge
           if (out_vec && col + 8 <= p.N && (EPI != EPI_ADD || aux_vec)) {
             if (EPI == EPI_ADD) {
               float o[8];
-              load8(sp + col, o);
+              load8<F16>(sp + col, o);
 #pragma unroll
               for (int j = 0; j < 8; ++j) v[j] += o[j];
             }
-            store8(rp + col, v);
+            store8<F16>(rp + col, v);
           } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
               if (col + j < p.N)
-                rp[col + j] = f32_to_bf16(EPI == EPI_ADD ? v[j] + bf16_to_f32(sp[col + j]) : v[j]);
+                rp[col + j] = f32_to_h16<F16>(EPI == EPI_ADD ? v[j] + h16_to_f32<F16>(sp[col + j]) : v[j]);
           }
         }
       }
@@ -1171,11 +1199,11 @@ struct WsLayout {
 };
 
 int big_variant();
-inline int small_rows(int dtype) { return dtype == MOE_BF16 ? 128 : 64; }
+inline int small_rows(int dtype) { return dtype != MOE_F32 ? 128 : 64; }
 // 256-row tiles for the register-staged variants, whose LoRA segment (K = r)
 // must come in 16-byte pieces.
 inline int big_rows(const ExpertDims& d) {
-  if (d.dtype != MOE_BF16) return 64;
+  if (d.dtype == MOE_F32) return 64;
   return big_variant() >= 4 && d.r % 8 == 0 ? 256 : 128;
 }
 
@@ -1211,6 +1239,11 @@ hipError_t launch(K kern, int grid, const GemmArgs& a, hipStream_t s, int thread
   return hipGetLastError();
 }
 
+// The 16-bit GEMM instantiation for a layer dtype (MOE_BF16 or MOE_F16); the
+// arguments are the tile parameters of gemm16 after F16, VST last.
+#define GEMM16(dtype, ...) \
+  ((dtype) == MOE_F16 ? gemm16<true, __VA_ARGS__> : gemm16<false, __VA_ARGS__>)
+
 // Tile variants of the four expert GEMMs, chosen by measurement on MI355X
 // (variant 5 is the default; MOE_LORA_GEMM_VARIANT overrides it for tuning
 // runs):
@@ -1241,23 +1274,23 @@ hipError_t launch_big(int grid, const GemmArgs& a, hipStream_t s, int bm) {
     // 256-row tiles go to a buffer->LDS kernel with element-wise fills.
     const bool all_vec = a.a[0].vec && a.b[0].vec && (a.K[1] == 0 || (a.a[1].vec && a.b[1].vec));
     if (!all_vec)
-      return launch(gemm_bf16<256, 256, 128, 128, 32, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
+      return launch(GEMM16(a.dtype, 256, 256, 128, 128, 32, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
     switch (big_variant()) {
       case 4:
-        return launch(gemm_bf16<256, 256, 64, 128, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 1>, grid, a, s, 512);
+        return launch(GEMM16(a.dtype, 256, 256, 64, 128, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 1), grid, a, s, 512);
       default:
-        return launch(gemm_bf16<256, 256, 128, 64, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 1>, grid, a, s, 512);
+        return launch(GEMM16(a.dtype, 256, 256, 128, 64, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 1), grid, a, s, 512);
     }
   }
   switch (big_variant()) {
     case 0:
-      return launch(gemm_bf16<128, 256, 64, 128, 64, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
+      return launch(GEMM16(a.dtype, 128, 256, 64, 128, 64, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
     case 2:
-      return launch(gemm_bf16<128, 256, 64, 128, 32, 4, 1, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
+      return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 4, 1, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
     case 3:
-      return launch(gemm_bf16<128, 256, 64, 128, 32, 6, 1, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
+      return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 6, 1, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
     default:
-      return launch(gemm_bf16<128, 256, 64, 128, 32, 3, 2, MODE, EPI, PAIRED, A_KC, B_KC>, grid, a, s);
+      return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 3, 2, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
   }
 }
 
@@ -1276,6 +1309,7 @@ GemmArgs base_args(const ExpertDims& d, const int32_t* offsets, const TileList& 
   a.ntiles = t.ntiles;
   a.I = d.I;
   a.scale = 1.0f;
+  a.dtype = d.dtype;
   return a;
 }
 
@@ -1294,19 +1328,19 @@ hipError_t side_product(const ExpertDims& d, const int32_t* offsets, const WsLay
   a.out = out;
   a.ld_out = d.r;
   a.scale = d.scale;
-  if (d.dtype == MOE_BF16) {
+  if (d.dtype != MOE_F32) {
     a.ntn = 1;
     if (l_kcontig) {
       if (d.r <= 32)
-        return launch(gemm_bf16<128, 32, 32, 32, 64, 3, 2, GROUP_M, EPI_STORE, false, true, true>,
+        return launch(GEMM16(a.dtype, 128, 32, 32, 32, 64, 3, 2, GROUP_M, EPI_STORE, false, true, true, 0),
                       gm_grid(d, t, 1), a, s);
-      return launch(gemm_bf16<128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE, false, true, true>,
+      return launch(GEMM16(a.dtype, 128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE, false, true, true, 0),
                     gm_grid(d, t, 1), a, s);
     }
     if (d.r <= 32)
-      return launch(gemm_bf16<128, 32, 32, 32, 64, 3, 2, GROUP_M, EPI_STORE, false, true, false>,
+      return launch(GEMM16(a.dtype, 128, 32, 32, 32, 64, 3, 2, GROUP_M, EPI_STORE, false, true, false, 0),
                     gm_grid(d, t, 1), a, s);
-    return launch(gemm_bf16<128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE, false, true, false>,
+    return launch(GEMM16(a.dtype, 128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE, false, true, false, 0),
                   gm_grid(d, t, 1), a, s);
   }
   a.ntn = ceil_div(d.r, 64);
@@ -1324,7 +1358,7 @@ hipError_t side_product(const ExpertDims& d, const int32_t* offsets, const WsLay
 
 // Tiles per expert of the kernel weight_grad picks for [P, Q].
 int wgrad_tiles(const ExpertDims& d, int P, int Q) {
-  if (d.dtype != MOE_BF16) return ceil_div(P, 64) * ceil_div(Q, 64);
+  if (d.dtype == MOE_F32) return ceil_div(P, 64) * ceil_div(Q, 64);
   if (Q <= 64 && P > 64) return ceil_div(P, 256);
   if (P >= 256 && Q >= 256) return ceil_div(P, 128) * ceil_div(Q, 256);
   return (P <= 32 ? 1 : ceil_div(P, 64)) * ceil_div(Q, 256);
@@ -1384,31 +1418,31 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
 template <int EPI>
 hipError_t weight_grad_launch(const ExpertDims& d, GemmArgs& a, int E, int P, int Q,
                               hipStream_t s) {
-  if (d.dtype == MOE_BF16) {
+  if (d.dtype != MOE_F32) {
     if (Q <= 64 && P > 64) {  // [big, r]
       a.ntn = 1;
       a.ntm = ceil_div(P, 256);
       if (Q <= 32)
-        return launch(gemm_bf16<256, 32, 64, 32, 32, 3, 2, GROUP_K, EPI, false, false, false>,
+        return launch(GEMM16(a.dtype, 256, 32, 64, 32, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
                       E * a.ntm, a, s);
-      return launch(gemm_bf16<256, 64, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false>,
+      return launch(GEMM16(a.dtype, 256, 64, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
                     E * a.ntm, a, s);
     }
     if (P >= 256 && Q >= 256) {  // [big, big]: full fine-tuning weight gradients
       a.ntm = ceil_div(P, 128);
       a.ntn = ceil_div(Q, 256);
-      return launch(gemm_bf16<128, 256, 64, 128, 32, 3, 2, GROUP_K, EPI, false, false, false>,
+      return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
                     E * a.ntm * a.ntn, a, s);
     }
     // [r, big] (or both small)
     a.ntn = ceil_div(Q, 256);
     if (P <= 32) {
       a.ntm = 1;
-      return launch(gemm_bf16<32, 256, 32, 64, 32, 3, 2, GROUP_K, EPI, false, false, false>,
+      return launch(GEMM16(a.dtype, 32, 256, 32, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
                     E * a.ntn, a, s);
     }
     a.ntm = ceil_div(P, 64);
-    return launch(gemm_bf16<64, 256, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false>,
+    return launch(GEMM16(a.dtype, 64, 256, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
                   E * a.ntm * a.ntn, a, s);
   }
   a.ntm = ceil_div(P, 64);
@@ -1425,6 +1459,7 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
   a.M = P;
   a.N = Q;
   a.scale = 1.0f;
+  a.dtype = d.dtype;
   a.out_estride = static_cast<int64_t>(P) * Q;
   a.ld_out = Q;
   a.a[0] = opnd(Lm, 0, P, 0, P % 8 == 0);
@@ -1451,6 +1486,9 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
   if (d.dtype == MOE_BF16)
     hipLaunchKernelGGL(reduce_splits_kernel<bf16_t>, grid, dim3(256), 0, s, part,
                        static_cast<bf16_t*>(out), S, PQ, total);
+  else if (d.dtype == MOE_F16)
+    hipLaunchKernelGGL(reduce_splits_kernel<f16_t>, grid, dim3(256), 0, s, part,
+                       static_cast<f16_t*>(out), S, PQ, total);
   else
     hipLaunchKernelGGL(reduce_splits_kernel<float>, grid, dim3(256), 0, s, part,
                        static_cast<float*>(out), S, PQ, total);
@@ -1470,7 +1508,7 @@ size_t experts_fwd_ws_bytes(const ExpertDims& d) {
 }
 
 size_t experts_bwd_ws_bytes(const ExpertDims& d) {
-  const size_t esz = d.dtype == MOE_BF16 ? 2 : 4;
+  const size_t esz = d.dtype == MOE_F32 ? 4 : 2;
   size_t b = tile_ws(nullptr, d).bytes;
   b += align_up(static_cast<size_t>(d.N) * d.r * esz) * 2;        // G B_d, dH B_gu
   b += align_up(static_cast<size_t>(d.N) * 2 * d.I * esz);         // dH
@@ -1498,7 +1536,7 @@ hipError_t launch_gate_up(const ExpertDims& d, const WsLayout& L, const void* x_
   a.out2 = act;
   a.ld_out2 = I;
   TimedScope ts(tm, MOE_K_GATE_UP_FWD, s);
-  if (d.dtype == MOE_BF16) {
+  if (d.dtype != MOE_F32) {
     a.ntn = ceil_div(I, 128);
     return launch_big<GROUP_M, EPI_SWIGLU, true, true, true>(gm_grid(d, L.big, a.ntn), a, s,
                                                               L.big.bm);
@@ -1509,13 +1547,13 @@ hipError_t launch_gate_up(const ExpertDims& d, const WsLayout& L, const void* x_
 
 // Recompute mode: h [N, 2I] and act [N, I] live in scratch after `base_bytes`.
 inline size_t lean_extra_bytes(const ExpertDims& d) {
-  const size_t esz = d.dtype == MOE_BF16 ? 2 : 4;
+  const size_t esz = d.dtype == MOE_F32 ? 4 : 2;
   return align_up(static_cast<size_t>(d.N) * 2 * d.I * esz) +
          align_up(static_cast<size_t>(d.N) * d.I * esz);
 }
 
 inline moe_saved lean_saved(const ExpertDims& d, const moe_saved& sv, void* ws, size_t base_bytes) {
-  const size_t esz = d.dtype == MOE_BF16 ? 2 : 4;
+  const size_t esz = d.dtype == MOE_F32 ? 4 : 2;
   moe_saved out = sv;
   char* p = static_cast<char*>(ws) + align_up(base_bytes);
   out.h = p;
@@ -1554,7 +1592,7 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
     a.out = sv.y_exp;
     a.ld_out = H;
     TimedScope ts(tm, MOE_K_DOWN_FWD, s);
-    if (d.dtype == MOE_BF16) {
+    if (d.dtype != MOE_F32) {
       a.ntn = ceil_div(H, 256);
       MOE_TRY((launch_big<GROUP_M, EPI_STORE, false, true, true>( gm_grid(d, L.big, a.ntn),
                      a, s, L.big.bm)));
@@ -1573,7 +1611,7 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
                               KernelTimer* tm) {
   const WsLayout L = tile_ws(ws, d);
   const int H = d.H, I = d.I, r = d.r;
-  const size_t esz = d.dtype == MOE_BF16 ? 2 : 4;
+  const size_t esz = d.dtype == MOE_F32 ? 4 : 2;
   char* p = static_cast<char*>(ws) + L.bytes;
   void* gb = p;
   p += align_up(static_cast<size_t>(d.N) * r * esz);
@@ -1602,7 +1640,7 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     a.aux = sv.h;
     a.ld_aux = 2 * I;
     TimedScope ts(tm, MOE_K_DOWN_BWD, s);
-    if (d.dtype == MOE_BF16) {
+    if (d.dtype != MOE_F32) {
       a.ntn = ceil_div(I, 256);
       MOE_TRY((launch_big<GROUP_M, EPI_SWIGLU_BWD, false, true, false>(
                      gm_grid(d, L.big, a.ntn), a, s, L.big.bm)));
@@ -1637,7 +1675,7 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     a.out = dx_perm;
     a.ld_out = H;
     TimedScope ts(tm, MOE_K_GATE_UP_BWD, s);
-    if (d.dtype == MOE_BF16) {
+    if (d.dtype != MOE_F32) {
       a.ntn = ceil_div(H, 256);
       MOE_TRY((launch_big<GROUP_M, EPI_STORE, false, true, false>( gm_grid(d, L.big, a.ntn),
                      a, s, L.big.bm)));
@@ -1699,17 +1737,36 @@ __global__ void range_offsets_kernel(int32_t* off, int T) {
   }
 }
 
-__global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ src,
-                                                        bf16_t* __restrict__ dst, int64_t n) {
+template <typename Elem>
+__global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ src,
+                                                   Elem* __restrict__ dst, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = f32_to_bf16(src[i]);
+  if (i < n) dst[i] = from_f32<Elem>(src[i]);
 }
 
+// dst += src; with vec, each thread takes 16 bytes (both pointers 16-byte aligned).
 template <typename Elem>
 __global__ __launch_bounds__(256) void accumulate_kernel(const Elem* __restrict__ src,
-                                                         Elem* __restrict__ dst, int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = from_f32<Elem>(to_f32<Elem>(dst[i]) + to_f32<Elem>(src[i]));
+                                                         Elem* __restrict__ dst, int64_t n,
+                                                         bool vec) {
+  constexpr int V = 16 / sizeof(Elem);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (vec) {
+    const int64_t i = t * V;
+    if (i + V <= n) {
+      Elem a[V], b[V];
+      *reinterpret_cast<uint4*>(a) = *reinterpret_cast<const uint4*>(src + i);
+      *reinterpret_cast<uint4*>(b) = *reinterpret_cast<const uint4*>(dst + i);
+#pragma unroll
+      for (int j = 0; j < V; ++j) b[j] = from_f32<Elem>(to_f32<Elem>(b[j]) + to_f32<Elem>(a[j]));
+      *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(b);
+    } else {
+      for (int64_t j = i; j < n; ++j)
+        dst[j] = from_f32<Elem>(to_f32<Elem>(dst[j]) + to_f32<Elem>(src[j]));
+    }
+  } else if (t < n) {
+    dst[t] = from_f32<Elem>(to_f32<Elem>(dst[t]) + to_f32<Elem>(src[t]));
+  }
 }
 
 struct RouterWs {
@@ -1732,13 +1789,14 @@ RouterWs router_ws(void* ws, int T, int E, int dtype) {
   R.L = tile_ws(p ? p + off : nullptr, d);
   off += align_up(R.L.bytes);
   R.dl16 = reinterpret_cast<bf16_t*>(p ? p + off : nullptr);
-  off += dtype == MOE_BF16 ? align_up(static_cast<size_t>(T) * E * 2) : 0;
+  off += dtype != MOE_F32 ? align_up(static_cast<size_t>(T) * E * 2) : 0;
   R.bytes = off;
   return R;
 }
 
-GemmArgs router_args(const RouterWs& R, int T) {
+GemmArgs router_args(const RouterWs& R, int dtype) {
   GemmArgs a{};
+  a.dtype = dtype;
   a.a[1] = none();
   a.b[1] = none();
   a.E = 1;
@@ -1760,16 +1818,16 @@ hipError_t launch_router_fwd(const void* x, const void* w_r, int T, int H, int E
   TimedScope ts(tm, MOE_K_ROUTER_FWD, s);
   hipLaunchKernelGGL(range_offsets_kernel, dim3(1), dim3(64), 0, s, R.offsets, T);
   MOE_TRY(build_tiles(R.L, R.offsets, 1, s));
-  GemmArgs a = router_args(R, T);
+  GemmArgs a = router_args(R, dtype);
   a.a[0] = opnd(x, 0, H, 1, true);
   a.b[0] = opnd(w_r, 0, H, 1, true);
   a.K[0] = H;
   a.N = E;
   a.out = logits;
   a.ld_out = E;
-  if (dtype == MOE_BF16) {
+  if (dtype != MOE_F32) {
     a.ntn = ceil_div(E, 64);
-    return launch(gemm_bf16<128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE_F32, false, true, true>,
+    return launch(GEMM16(a.dtype, 128, 64, 32, 64, 64, 3, 2, GROUP_M, EPI_STORE_F32, false, true, true, 0),
                   static_cast<int>(tile_cap(T, 1, R.L.small.bm)) * a.ntn, a, s);
   }
   a.ntn = ceil_div(E, 64);
@@ -1783,19 +1841,23 @@ hipError_t launch_router_bwd(const float* d_logits, const void* w_r, int T, int 
   TimedScope ts(tm, MOE_K_ROUTER_BWD, s);
   hipLaunchKernelGGL(range_offsets_kernel, dim3(1), dim3(64), 0, s, R.offsets, T);
   MOE_TRY(build_tiles(R.L, R.offsets, 1, s));
-  GemmArgs a = router_args(R, T);
+  GemmArgs a = router_args(R, dtype);
   a.K[0] = E;
   a.N = H;
   a.out = dx;
   a.ld_out = H;
-  if (dtype == MOE_BF16) {
+  if (dtype != MOE_F32) {
     const int64_t n = static_cast<int64_t>(T) * E;
-    hipLaunchKernelGGL(cast_bf16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                       0, s, d_logits, R.dl16, n);
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+    if (dtype == MOE_F16)
+      hipLaunchKernelGGL(cast_kernel<f16_t>, grid, dim3(256), 0, s, d_logits,
+                         reinterpret_cast<f16_t*>(R.dl16), n);
+    else
+      hipLaunchKernelGGL(cast_kernel<bf16_t>, grid, dim3(256), 0, s, d_logits, R.dl16, n);
     a.a[0] = opnd(R.dl16, 0, E, 1, true);
     a.b[0] = opnd(w_r, 0, H, 0, true);  // [K = E][N = H]
     a.ntn = ceil_div(H, 256);
-    return launch(gemm_bf16<128, 256, 64, 128, 32, 3, 2, GROUP_M, EPI_ADD, false, true, false>,
+    return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 3, 2, GROUP_M, EPI_ADD, false, true, false, 0),
                   static_cast<int>(tile_cap(T, 1, R.L.small.bm)) * a.ntn, a, s);
   }
   a.a[0] = opnd(d_logits, 0, E, 1, true);
@@ -1845,6 +1907,7 @@ hipError_t merge_one(const ExpertDims& d, int rows, int cols, const void* w, con
   hipLaunchKernelGGL(uniform_offsets_kernel, dim3(1), dim3(256), 0, s, M.offsets, d.E, rows);
   MOE_TRY(build_tiles(M.L, M.offsets, d.E, s));
   GemmArgs g{};
+  g.dtype = d.dtype;
   g.a[1] = none();
   g.b[1] = none();
   g.E = d.E;
@@ -1862,9 +1925,9 @@ hipError_t merge_one(const ExpertDims& d, int rows, int cols, const void* w, con
   g.ld_aux = cols;
   g.scale = d.scale;
   const int grid_m = static_cast<int>(tile_cap(m.N, d.E, M.L.small.bm));
-  if (d.dtype == MOE_BF16) {
+  if (d.dtype != MOE_F32) {
     g.ntn = ceil_div(cols, 256);
-    return launch(gemm_bf16<128, 256, 64, 128, 32, 3, 2, GROUP_M, EPI_ADD, false, true, false>,
+    return launch(GEMM16(g.dtype, 128, 256, 64, 128, 32, 3, 2, GROUP_M, EPI_ADD, false, true, false, 0),
                   grid_m * g.ntn, g, s);
   }
   g.ntn = ceil_div(cols, 64);
@@ -1891,12 +1954,18 @@ hipError_t launch_accumulate(int dtype, int64_t n, const void* src, void* dst, h
   if (n <= 0) return hipSuccess;
   TimedScope ts(tm, MOE_K_ACCUMULATE, s);
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(accumulate_kernel<bf16_t>, grid, dim3(256), 0, s,
-                       static_cast<const bf16_t*>(src), static_cast<bf16_t*>(dst), n);
-  else
-    hipLaunchKernelGGL(accumulate_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(src), static_cast<float*>(dst), n);
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+  auto go = [&](auto tag) {
+    using Elem = decltype(tag);
+    constexpr int V = 16 / sizeof(Elem);
+    const int64_t threads = vec ? (n + V - 1) / V : n;
+    hipLaunchKernelGGL(accumulate_kernel<Elem>, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                       dim3(256), 0, s, static_cast<const Elem*>(src), static_cast<Elem*>(dst), n,
+                       vec);
+  };
+  if (dtype == MOE_BF16) go(bf16_t{});
+  else if (dtype == MOE_F16) go(f16_t{});
+  else go(float{});
   return hipGetLastError();
 }
 

@@ -207,7 +207,7 @@ class MoELoRAFunction(torch.autograd.Function):
         T, H = x.shape
         E, r = logits.shape[1], a_gu.shape[1]
         I = w_gu.shape[1] // 2
-        dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}[x.dtype]
+        dtype = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[x.dtype]
         shape = Shape(T, H, I, E, k, r, dtype, lora_scale)
         full = bool(ctx.needs_input_grad[2] or ctx.needs_input_grad[5])
         layer = MoELoRALayer(shape, router, device=x.device, full_ft=full)

@@ -51,12 +51,14 @@ def ws(lib, sh):
 def test_workspace_never_holds_a_merged_delta(lib):
     from workloads import CONFIGS
     for cfg in CONFIGS.values():
-        sh = shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.r, 1 if cfg.dtype == "bf16" else 0)
+        sh = shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.r,
+                   {"f32": 0, "bf16": 1, "f16": 2}[cfg.dtype])
         st, f, b, p = ws(lib, sh)
         assert st == 0
-        esz = 2 if cfg.dtype == "bf16" else 4
+        esz = 4 if cfg.dtype == "f32" else 2
         delta = cfg.E * 2 * cfg.I * cfg.H * esz   # one materialised W + B A for gate_up
-        # forward scratch is a tile list only; backward holds dH [N, 2I] and two [N, r]
+        # forward scratch is a tile list only; backward holds dH [N, 2I] and two
+        # [N, r] (these layers have experts enough for no split-K partials)
         assert f < 1 << 20
         assert b <= cfg.N * (2 * cfg.I + 2 * cfg.r) * esz + (1 << 20)
         if cfg.T * cfg.k < cfg.E * cfg.H:            # the regime the pages' memory model favours
@@ -182,7 +184,7 @@ def test_router_and_accumulate_validate(lib):
     assert lib.moe_router_bwd(*args, fake, P(0x40000), need_bf16, None) == 1  # dx is d_logits
     assert lib.moe_accumulate(1, 0, None, None, None) == 0                 # empty: nothing to do
     assert lib.moe_accumulate(1, -1, fake, P(0x20000), None) == 1
-    assert lib.moe_accumulate(2, 16, fake, P(0x20000), None) == 1
+    assert lib.moe_accumulate(3, 16, fake, P(0x20000), None) == 1            # no such dtype
     assert lib.moe_accumulate(1, 16, fake, fake, None) == 1
 
 

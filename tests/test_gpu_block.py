@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 ROUTER_SHAPES = [  # (T, H, E, dtype)
     (300, 584, 6, "bf16"), (129, 256, 8, "bf16"), (1, 64, 3, "bf16"), (640, 512, 64, "bf16"),
     (8192, 2880, 32, "bf16"), (16384, 2048, 128, "bf16"), (333, 200, 5, "f32"),
-    (256, 256, 8, "f32"), (70, 136, 130, "f32"),
+    (256, 256, 8, "f32"), (70, 136, 130, "f32"), (300, 584, 6, "f16"), (8192, 2880, 32, "f16"),
 ]
 
 
@@ -39,7 +39,7 @@ def _mel():
 def test_router_projection_and_its_input_gradient(T, H, E, dtype):
     mel = _mel()
     say(f"[router] T={T} H={H} E={E} {dtype}")
-    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     g = torch.Generator(device="cuda")
     g.manual_seed(T * 7919 + H * 31 + E)
     x = torch.randn(T, H, device="cuda", generator=g).to(tdt)
@@ -57,18 +57,18 @@ def test_router_projection_and_its_input_gradient(T, H, E, dtype):
     torch.cuda.synchronize()
     xh, wh, dlh = to_numpy(x), to_numpy(w_r), to_numpy(dl)
     close("logits", to_numpy(logits), oracle.router_logits(xh, wh, np.float64), 1e-5)
-    # bf16 layers feed d_logits to the MFMA rounded to bf16 (relative 2^-9)
+    # 16-bit layers feed d_logits to the MFMA rounded to the layer dtype
     ref = oracle.router_input_grad(dlh, wh, np.float64)
-    close("dx (router term)", to_numpy(dx), ref, 1e-4 if dtype == "f32" else 1e-2)
+    close("dx (router term)", to_numpy(dx), ref, {"f32": 1e-4, "bf16": 1e-2, "f16": 2e-3}[dtype])
     close("dx (updated)", to_numpy(dx1), to_numpy(dx0) + ref, TOL[dtype])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("n", [1, 255, 256, 1000003])
 def test_accumulate_is_one_rounded_sum(dtype, n):
     mel = _mel()
     say(f"[accumulate] n={n} {dtype}")
-    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     g = torch.Generator(device="cuda")
     g.manual_seed(n)
     src = torch.randn(n, device="cuda", generator=g).to(tdt)
@@ -81,7 +81,7 @@ def test_accumulate_is_one_rounded_sum(dtype, n):
 
 BLOCK_CASES = [  # (parity config, shared expert width)
     ("tiny", 96), ("mini-bf16", 200), ("mini-renorm", 128), ("mini-f32", 72), ("mini-k1", None),
-    ("mini-T1", 64),
+    ("mini-T1", 64), ("mini-f16", 104),
 ]
 
 

@@ -24,7 +24,7 @@ SEED = 3407
 
 
 @pytest.mark.parametrize("name", ["gpt-oss-20b", "qwen3-30b-a3b", "deepseek-v3",
-                                  "gpt-oss-20b-long"])
+                                  "gpt-oss-20b-long", "gpt-oss-20b-f16"])
 def test_full_size_layer(name):
     import mixture_experts_lora_amd as mel
     cfg = CONFIGS[name]

@@ -4,7 +4,8 @@ Each merged element is one float32 sum of the base weight and the rank-r
 product, rounded once to the layer dtype, so against the float32 oracle the
 error is at most half an ulp of the dtype plus the float32 summation-order
 difference of the r-term product: checked element-wise at one ulp (2^-8 of
-the element for bf16, 1e-5 of the tensor's largest value for float32) and
+the element for bf16, 2^-11 for float16, 1e-5 of the tensor's largest value
+for float32) and
 normwise at the layer tolerance.
 """
 import numpy as np
@@ -29,8 +30,8 @@ def _check(name, got, ref, dtype):
     close(name, got, ref, TOL[dtype])
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
-    bound = (2.0 ** -8) * np.abs(ref) + 1e-6 * np.abs(ref).max() if dtype == "bf16" \
-        else 1e-5 * np.abs(ref).max()
+    ulp = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}.get(dtype)
+    bound = ulp * np.abs(ref) + 1e-6 * np.abs(ref).max() if ulp else 1e-5 * np.abs(ref).max()
     bad = np.abs(got - ref) > bound
     assert not bad.any(), f"{name}: {int(bad.sum())} elements beyond one ulp"
 
@@ -59,7 +60,7 @@ def test_merge_matches_oracle(name):
         _check(n, to_numpy(out[n]), ref[n], cfg.dtype)
 
 
-@pytest.mark.parametrize("name", ["mini-bf16", "mini-f32", "mini-r1"])
+@pytest.mark.parametrize("name", ["mini-bf16", "mini-f32", "mini-r1", "mini-f16"])
 def test_merge_in_place_and_one_projection(name):
     """Merging into the base weight itself equals the out-of-place merge bit for
     bit; a NULL output skips that projection."""
@@ -79,7 +80,7 @@ def test_merge_in_place_and_one_projection(name):
     assert torch.equal(w["w_d"], out["w_d"])
 
 
-@pytest.mark.parametrize("name", ["mini-bf16", "mini-renorm", "tiny"])
+@pytest.mark.parametrize("name", ["mini-bf16", "mini-renorm", "tiny", "mini-f16"])
 def test_merged_weights_reproduce_the_layer(name):
     """The exported weights with the adapters zeroed give the trained layer's
     output (split order with the adapters) up to the dtype's rounding."""

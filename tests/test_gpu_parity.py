@@ -72,7 +72,7 @@ def test_layer_matches_oracle(name, seed):
 
 
 @pytest.mark.parametrize("name", ["tiny", "mini-bf16", "mini-skew", "mini-f32", "mini-k1",
-                                  "mini-renorm"])
+                                  "mini-renorm", "mini-f16"])
 def test_full_fine_tuning_base_grads(name):
     """Full fine-tuning: dW_gu and dW_d against the oracle; every other output
     bit-identical to the LoRA-only backward."""
@@ -97,7 +97,8 @@ def test_full_fine_tuning_base_grads(name):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("name", ["tiny", "mini-bf16", "mini-skew", "mini-r1", "mini-f32"])
+@pytest.mark.parametrize("name", ["tiny", "mini-bf16", "mini-skew", "mini-r1", "mini-f32",
+                                  "mini-f16-skew"])
 @pytest.mark.parametrize("full_ft", [False, True])
 def test_recompute_mode_is_bit_identical(name, full_ft):
     """Activation-lean mode (h and act recomputed in the backward by the same

@@ -29,7 +29,7 @@ class LayerConfig:
     E: int
     k: int
     r: int
-    dtype: str            # "f32" or "bf16": x, weights, LoRA params, activations, outputs
+    dtype: str            # "f32", "bf16" or "f16": x, weights, LoRA params, activations, outputs
     router: str           # one of ROUTERS
     zipf_s: float = 0.0   # >0: add -zipf_s*ln(rank_e) to every token's logit of expert e
     n_dead: int = 0       # experts (lowest popularity ranks) whose logits get -30
@@ -69,6 +69,9 @@ CONFIGS = {
                                zipf_s=1.2, n_dead=8),
     "gpt-oss-20b-long": LayerConfig("gpt-oss-20b-long", T=65536, H=2880, I=2880, E=32, k=4,
                                     r=16, dtype="bf16", router="topk_softmax"),
+    # the gpt-oss layer in IEEE half (float16 MFMA)
+    "gpt-oss-20b-f16": LayerConfig("gpt-oss-20b-f16", T=8192, H=2880, I=2880, E=32, k=4, r=16,
+                                   dtype="f16", router="topk_softmax"),
 }
 
 # The layer the throughput figure is quoted on (fits one GPU).
@@ -106,6 +109,12 @@ PARITY_CONFIGS = {
                               dtype="bf16", router="sigmoid_topk_renorm", zipf_s=1.2, n_dead=1),
     "mini-f32-split": LayerConfig("mini-f32-split", T=1500, H=136, I=72, E=2, k=1, r=8,
                                   dtype="f32", router="softmax_topk"),
+    # IEEE half layers (the same kernels with the float16 MFMA)
+    "mini-f16": LayerConfig("mini-f16", T=300, H=584, I=200, E=6, k=3, r=16,
+                            dtype="f16", router="topk_softmax"),
+    "mini-f16-skew": LayerConfig("mini-f16-skew", T=1100, H=264, I=136, E=16, k=4, r=32,
+                                 dtype="f16", router="sigmoid_topk_renorm", zipf_s=1.2,
+                                 n_dead=4, lora_scale=2.0),
 }
 
 

@@ -11,7 +11,8 @@ Distributions (second argument of N(0, s) is the standard deviation, the usual
 
 LoRA B is drawn nonzero on purpose (a fresh adapter starts at B = 0, which
 would make every LoRA gradient but dB vanish). bf16 layers round each fp32
-draw to bfloat16 (round to nearest even, torch's conversion).
+draw to bfloat16 (round to nearest even, torch's conversion); f16 layers likewise
+round to IEEE half.
 
 Router logits are the frozen router projection x W_r^T, computed in float64
 from the (already rounded) x and W_r and rounded once to float32. Layers with
@@ -37,7 +38,7 @@ TENSOR_IDS = {"x": 0, "w_r": 1, "w_gu": 2, "w_d": 3, "a_gu": 4, "b_gu": 5,
               "shared_w_gu": 10, "shared_w_d": 11, "shared_a_gu": 12, "shared_b_gu": 13,
               "shared_a_d": 14, "shared_b_d": 15}
 
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def seed_for(seed: int, name: str, expert: int | None = None) -> int:
