@@ -394,12 +394,13 @@ def main():
     half = cfg.dtype in ("bf16", "f16")      # dense bf16 and fp16 MFMA peaks are equal
     peak = PEAK_BF16_TFLOPS if half else PEAK_F32_TFLOPS
     dom = max((k for k in GEMM_KERNELS if k in kms), key=lambda k: kms[k]["ms_per_step"])
-    # FLOPs of the dominant kernel per step (block mode: its routed and shared
-    # launches together) over its summed launch time per step
+    # FLOPs of the dominant kernel per step over its summed launch time per step.
+    # Every part (the routed layer; in block mode also the shared expert)
+    # launches each GEMM kernel equally often (twice for gate_up_fwd when the
+    # backward recomputes h; base_wgrad's figure is the mean of its two launches).
     parts = [c for c in block_parts(cfg, shared_I) if c is not None] if args.block else [cfg]
-    dom_flops_step = sum(kernel_flops(dom, c) * (2 if dom == "base_wgrad" else 1)
-                         for c in parts)
     dom_launches = kms[dom]["launches"] / args.steps
+    dom_flops_step = dom_launches / len(parts) * sum(kernel_flops(dom, c) for c in parts)
     dom_tf = dom_flops_step / (kms[dom]["ms_per_step"] / 1e3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(dom_tf / peak, 4),
