@@ -63,7 +63,12 @@ template <> struct Vec4<float> {
   }
 };
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// Logistic function for the SwiGLU epilogues: hardware exp2 and reciprocal
+// (each within 1 ulp) instead of an IEEE divide, about ten times fewer
+// instructions per element. exp(-z) overflowing to inf gives 0; underflow gives 1.
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // SwiGLU forward: act = g * sigmoid(g) * u.
 __device__ __forceinline__ float swiglu(float g, float u) { return g * sigmoidf_(g) * u; }
