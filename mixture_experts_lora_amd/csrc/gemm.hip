@@ -769,9 +769,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
 #pragma unroll
       for (int ni = 0; ni < NF; ++ni) bf[0][ni] = read_frag<BN, BK, B_KC, NF>(smem + A_BYTES, FB, ni, fb_base[ni], 0);
     }
-    // one k tile; tile it+1 sits in register buffer BUF = (it + 1) % NRB
-    auto ktile = [&](int it, auto bufc) {
+    // one k tile; tile it+1 sits in register buffer BUF = (it + 1) % NRB.
+    // MFMA = false: the wave's rows are all past the tile's valid rows (the
+    // ragged last tile of an expert); it still loads, stores and meets every
+    // barrier, but issues no MFMAs.
+    auto ktile = [&](int it, auto bufc, auto mfmac) {
       constexpr int BUF = decltype(bufc)::value;
+      constexpr bool MFMA = decltype(mfmac)::value;
       const char* sa = smem + (it % NST) * ST;
       const char* sb = sa + A_BYTES;
 #pragma unroll
@@ -803,17 +807,25 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
           store_tile(it + 1, ra[BUF], rb[BUF]);
           if (it + 1 + NRB < nk) load_tile(it + 1 + NRB, ra[BUF], rb[BUF]);
         }
+        if constexpr (MFMA) {
 #pragma unroll
-        for (int mi = 0; mi < MF; ++mi)
+          for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
-          for (int ni = 0; ni < NF; ++ni)
-            acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
+            for (int ni = 0; ni < NF; ++ni)
+              acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
+        }
       }
     };
-    for (int it = 0; it < nk; it += NRB) {
-      ktile(it, std::integral_constant<int, 1 % NRB>());
-      if (NRB > 1 && it + 1 < nk) ktile(it + 1, std::integral_constant<int, 2 % NRB>());
-    }
+    // The wave-uniform choice is made once, outside the k loop, so the loop
+    // itself has no extra branch.
+    auto kloop = [&](auto mfmac) {
+      for (int it = 0; it < nk; it += NRB) {
+        ktile(it, std::integral_constant<int, 1 % NRB>(), mfmac);
+        if (NRB > 1 && it + 1 < nk) ktile(it + 1, std::integral_constant<int, 2 % NRB>(), mfmac);
+      }
+    };
+    if (MODE != GROUP_M || wm * WM < rows) kloop(std::true_type());
+    else kloop(std::false_type());
   } else {
   #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
