@@ -293,6 +293,9 @@ def main():
                          "experts, and a shared expert (width --shared-I)")
     ap.add_argument("--shared-I", type=int, default=None,
                     help="shared expert width in --block mode (default I; 0: none)")
+    ap.add_argument("--chunks", type=int, default=1,
+                    help="run the layer over its tokens in this many chunks sharing one set "
+                         "of workspaces (long contexts: lower peak memory)")
     ap.add_argument("--merge", action="store_true",
                     help="only time the merged export W + s B A of both projections")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
@@ -347,11 +350,15 @@ def main():
             sum(v.numel() * v.element_size() for v in layer.shared.saved.values())
             if layer.shared is not None else 0)
     else:
-        layer = mel.MoELoRALayer(shape, cfg.router, full_ft=args.full_ft,
-                                 recompute=args.recompute)
+        if args.chunks > 1:
+            layer = mel.MoELoRAChunkedLayer(shape, cfg.router, args.chunks, full_ft=args.full_ft,
+                                            recompute=args.recompute)
+        else:
+            layer = mel.MoELoRALayer(shape, cfg.router, full_ft=args.full_ft,
+                                     recompute=args.recompute)
         step = lambda: layer.step(inp["x"], inp["logits"], inp["dy"], weights)  # noqa: E731
         fwd = lambda: layer.forward(inp["x"], inp["logits"], weights)  # noqa: E731
-        bwd = lambda: layer.backward(inp["dy"], inp["logits"], weights)  # noqa: E731
+        bwd = lambda: layer.backward(inp["dy"], inp["logits"], weights, x=inp["x"])  # noqa: E731
         saved = layer.saved_bytes()
     for _ in range(args.warmup):
         step()
@@ -428,7 +435,8 @@ def main():
                                   if args.block else "expert layer")
                                + " fwd+bwd"
                                + (", full fine-tuning" if args.full_ft else "")
-                               + (", h and act recomputed in backward" if args.recompute else ""),
+                               + (", h and act recomputed in backward" if args.recompute else "")
+                               + (f", {args.chunks} token chunks" if args.chunks > 1 else ""),
                    "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "r": cfg.r,
                    "router": cfg.router, "lora_scale": cfg.lora_scale, "seed": args.seed},
         "tokens_per_s": round(cfg.T / (ms / 1e3), 1),

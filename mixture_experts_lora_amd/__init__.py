@@ -381,6 +381,8 @@ try:
 except RuntimeError:
     pass
 
-from .layer import MoELoRABlock, MoELoRALayer, MoELoRAFunction  # noqa: E402
+from .layer import (LayerScratch, MoELoRABlock, MoELoRAChunkedLayer, MoELoRAFunction,  # noqa: E402
+                    MoELoRALayer)
 
-__all__ += ["MoELoRABlock", "MoELoRALayer", "MoELoRAFunction"]
+__all__ += ["LayerScratch", "MoELoRABlock", "MoELoRAChunkedLayer", "MoELoRALayer",
+            "MoELoRAFunction"]

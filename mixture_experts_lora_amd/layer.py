@@ -11,6 +11,10 @@ so nothing is allocated inside a step) and issues, on torch's current stream:
 MoELoRAFunction wraps the same calls as a torch.autograd.Function whose
 gradients are dX, d logits and the four LoRA gradients (base weights frozen).
 
+MoELoRAChunkedLayer runs the layer over its tokens in chunks that share one
+set of workspaces (long contexts: the peak is one chunk's transients plus
+every chunk's saved activations).
+
 MoELoRABlock is the block a model sees: it starts from hidden states, makes the
 logits with the frozen router projection (moe_router_fwd), runs the routed
 layer, and adds an optional always-on shared expert (a dense LoRA SwiGLU MLP
@@ -32,58 +36,117 @@ WEIGHT_NAMES = ("w_gu", "a_gu", "b_gu", "w_d", "a_d", "b_d")
 GRAD_NAMES = ("da_gu", "db_gu", "da_d", "db_d")
 
 
+class LayerScratch:
+    """Buffers a layer needs only while one of its calls runs: the workspace
+    shared by forward and backward, the permute workspace, the permuted
+    gradient rows (G and dX_perm), d_topk_w and, in the activation-lean mode,
+    x_perm (the backward gathers it again). Several layers or chunks that run
+    one after another can share one LayerScratch; it is sized for the largest
+    shape passed in and handed out as views."""
+
+    def __init__(self, shapes, recompute: bool, device="cuda"):
+        shapes = list(shapes)
+        es = max(s.torch_dtype.itemsize for s in shapes)
+        ws = perm = rows = tk = 0
+        for sh in shapes:
+            f, b, pm = moe_workspace_bytes(sh)
+            if recompute:
+                f, b = moe_workspace_bytes_lean(sh)
+            ws, perm = max(ws, f, b), max(perm, pm)
+            rows, tk = max(rows, sh.N * sh.H), max(tk, sh.T * sh.k)
+        self.recompute = recompute
+        u8 = dict(device=device, dtype=torch.uint8)
+        self.ws = torch.empty(max(ws, 1), **u8)
+        self.ws_perm = torch.empty(max(perm, 1), **u8)
+        nrow = 3 if recompute else 2          # G, dX_perm (+ x_perm)
+        self.rows = torch.empty(max(nrow * rows * es, 1), **u8)
+        self.rows_each = rows * es
+        self.d_topk_w = torch.empty(max(tk, 1), device=device, dtype=torch.float32)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.ws, self.ws_perm, self.rows, self.d_topk_w))
+
+    def row_view(self, i: int, shape: Shape):
+        n = shape.N * shape.H * shape.torch_dtype.itemsize
+        b = self.rows[i * self.rows_each: i * self.rows_each + n]
+        return b.view(shape.torch_dtype).view(shape.N, shape.H)
+
+
 class MoELoRALayer:
     """full_ft=True also computes the base-weight gradients (full fine-tuning).
     recompute=True is the activation-lean mode: h and act are not kept between
     forward and backward (they live in the forward workspace and are recomputed
-    in the backward's)."""
+    in the backward's), and neither is x_perm (the backward gathers it again
+    from x, so backward() needs x).
+
+    scratch: a LayerScratch to share with other layers or chunks (one is made
+    when None). out: optional views {"y", "dx", "d_logits"} to write the
+    outputs into (a chunk writes its rows of the whole layer's outputs).
+    grads, base_grads: optional gradient buffers to write into."""
 
     def __init__(self, shape: Shape, router: str, device="cuda", full_ft: bool = False,
-                 recompute: bool = False):
+                 recompute: bool = False, scratch: LayerScratch | None = None,
+                 out: dict | None = None, grads: dict | None = None,
+                 base_grads: dict | None = None):
         self.shape, self.router, self.full_ft, self.recompute = shape, router, full_ft, recompute
         T, H, I, E, k, r, N = shape.T, shape.H, shape.I, shape.E, shape.k, shape.r, shape.N
         dt = shape.torch_dtype
         z = lambda *s, dtype=dt: torch.empty(s, device=device, dtype=dtype)  # noqa: E731
         i32, f32 = torch.int32, torch.float32
+        if scratch is None:
+            scratch = LayerScratch([shape], recompute, device)
+        assert scratch.recompute == recompute
+        self.scratch = scratch
         self.topk_ids, self.topk_w = z(T, k, dtype=i32), z(T, k, dtype=f32)
         self.counts, self.offsets = z(E, dtype=i32), z(E + 1, dtype=i32)
         self.sorted_pair, self.inv_pos = z(N, dtype=i32), z(N, dtype=i32)
-        self.x_perm = z(N, H)
+        self.x_perm = scratch.row_view(2, shape) if recompute else z(N, H)
         self.saved = {"u_gu": z(N, r), "u_d": z(N, r), "y_exp": z(N, H)}
         if not recompute:
             self.saved.update(h=z(N, 2 * I), act=z(N, I))
-        self.y = z(T, H)
-        self.dy_perm, self.d_topk_w, self.d_logits = z(N, H), z(T, k, dtype=f32), z(T, E, dtype=f32)
-        self.dx_perm, self.dx = z(N, H), z(T, H)
-        self.grads = {"da_gu": z(E, r, H), "db_gu": z(E, 2 * I, r), "da_d": z(E, r, I),
-                      "db_d": z(E, H, r)}
-        self.base_grads = ({"dw_gu": z(E, 2 * I, H), "dw_d": z(E, H, I)} if full_ft else None)
-        fwd, bwd, perm = moe_workspace_bytes(shape)
-        if recompute:
-            fwd, bwd = moe_workspace_bytes_lean(shape)
-        # one scratch buffer serves both calls: they run one after the other on
-        # the stream, and nothing in the forward's scratch is read by the backward
-        self.ws_fwd = self.ws_bwd = z(max(fwd, bwd, 1), dtype=torch.uint8)
-        self.ws_perm = z(max(perm, 1), dtype=torch.uint8)
+        out = out or {}
+        self.y = out["y"] if "y" in out else z(T, H)
+        self.dx = out["dx"] if "dx" in out else z(T, H)
+        self.d_logits = out["d_logits"] if "d_logits" in out else z(T, E, dtype=f32)
+        self.dy_perm, self.dx_perm = scratch.row_view(0, shape), scratch.row_view(1, shape)
+        self.d_topk_w = scratch.d_topk_w[:T * k].view(T, k)
+        self.grads = grads if grads is not None else {
+            "da_gu": z(E, r, H), "db_gu": z(E, 2 * I, r), "da_d": z(E, r, I), "db_d": z(E, H, r)}
+        self.base_grads = None
+        if full_ft:
+            self.base_grads = base_grads if base_grads is not None else {
+                "dw_gu": z(E, 2 * I, H), "dw_d": z(E, H, I)}
+        self.ws_fwd = self.ws_bwd = scratch.ws
+        self.ws_perm = scratch.ws_perm
 
     def saved_bytes(self) -> int:
-        """Bytes held from forward to backward: the saved activations and x_perm
-        (the routing results and indices aside)."""
-        t = list(self.saved.values()) + [self.x_perm]
+        """Bytes held from forward to backward: the saved activations and, unless
+        the backward gathers it again, x_perm (the routing results and indices
+        aside)."""
+        t = list(self.saved.values()) + ([] if self.recompute else [self.x_perm])
         return sum(v.numel() * v.element_size() for v in t)
+
+    def _permute(self, x, stream):
+        s = self.shape
+        moe_permute(s, self.topk_ids, x, self.counts, self.offsets, self.sorted_pair,
+                    self.inv_pos, self.x_perm, self.ws_perm, stream)
 
     def forward(self, x, logits, weights: dict, stream=None):
         s = self.shape
         moe_route(logits, s.k, self.router, self.topk_ids, self.topk_w, stream)
-        moe_permute(s, self.topk_ids, x, self.counts, self.offsets, self.sorted_pair,
-                    self.inv_pos, self.x_perm, self.ws_perm, stream)
+        self._permute(x, stream)
         fwd = moe_grouped_lora_fwd_lean if self.recompute else moe_grouped_lora_fwd
         fwd(s, self.x_perm, self.offsets, weights, self.saved, self.ws_fwd, stream)
         moe_unpermute_combine(s, self.saved["y_exp"], self.inv_pos, self.topk_w, self.y, stream)
         return self.y
 
-    def backward(self, dy, logits, weights: dict, stream=None):
+    def backward(self, dy, logits, weights: dict, stream=None, x=None):
         s = self.shape
+        if self.recompute:
+            if x is None:
+                raise ValueError("the activation-lean backward gathers x_perm again: pass x")
+            self._permute(x, stream)   # same routing, so the same permutation and rows
         moe_unpermute_combine_bwd(s, dy, self.saved["y_exp"], self.inv_pos, self.topk_w,
                                   self.dy_perm, self.d_topk_w, stream)
         moe_route_bwd(logits, self.topk_ids, self.d_topk_w, s.k, self.router, self.d_logits,
@@ -104,7 +167,74 @@ class MoELoRALayer:
     def step(self, x, logits, dy, weights: dict, stream=None):
         """One forward and backward pass."""
         self.forward(x, logits, weights, stream)
-        return self.backward(dy, logits, weights, stream)
+        return self.backward(dy, logits, weights, stream, x=x)
+
+
+class MoELoRAChunkedLayer:
+    """The layer over its T tokens in `chunks` consecutive chunks, for long
+    contexts: every output row depends only on its own token, so each chunk
+    runs the same calls on its rows (writing its rows of Y, dX and d logits,
+    which are bit-identical to the unchunked layer's), and only the weight
+    gradients, sums over all rows, are added up across chunks (float32 sum,
+    one rounding per chunk). Saved activations stay per chunk; the workspaces
+    and the permuted gradient rows are sized for one chunk and shared, which
+    is what lowers the peak."""
+
+    def __init__(self, shape: Shape, router: str, chunks: int, device="cuda",
+                 full_ft: bool = False, recompute: bool = False):
+        if chunks < 1 or chunks > shape.T:
+            raise ValueError(f"chunks must be in [1, T], got {chunks}")
+        self.shape, self.router, self.chunks = shape, router, chunks
+        self.full_ft, self.recompute = full_ft, recompute
+        T, H, E = shape.T, shape.H, shape.E
+        dt = shape.torch_dtype
+        bounds = [T * i // chunks for i in range(chunks + 1)]
+        self.bounds = list(zip(bounds[:-1], bounds[1:]))
+        shapes = [Shape(hi - lo, shape.H, shape.I, shape.E, shape.k, shape.r, shape.dtype,
+                        shape.lora_scale) for lo, hi in self.bounds]
+        self.scratch = LayerScratch(shapes, recompute, device)
+        self.y = torch.empty(T, H, device=device, dtype=dt)
+        self.dx = torch.empty(T, H, device=device, dtype=dt)
+        self.d_logits = torch.empty(T, E, device=device, dtype=torch.float32)
+        # chunk 0 writes the gradients; every other chunk writes into one
+        # shared spare set, which is then added in
+        self.parts = []
+        spare = None
+        for i, ((lo, hi), sh) in enumerate(zip(self.bounds, shapes)):
+            out = {"y": self.y[lo:hi], "dx": self.dx[lo:hi], "d_logits": self.d_logits[lo:hi]}
+            g = None if i < 2 else spare
+            part = MoELoRALayer(sh, router, device, full_ft, recompute, self.scratch, out,
+                                grads=None if g is None else g[0],
+                                base_grads=None if g is None else g[1])
+            if i == 1:
+                spare = (part.grads, part.base_grads)
+            self.parts.append(part)
+        self.grads = self.parts[0].grads
+        self.base_grads = self.parts[0].base_grads
+
+    def saved_bytes(self) -> int:
+        return sum(p.saved_bytes() for p in self.parts)
+
+    def forward(self, x, logits, weights: dict, stream=None):
+        for (lo, hi), p in zip(self.bounds, self.parts):
+            p.forward(x[lo:hi], logits[lo:hi], weights, stream)
+        return self.y
+
+    def backward(self, dy, logits, weights: dict, stream=None, x=None):
+        for i, ((lo, hi), p) in enumerate(zip(self.bounds, self.parts)):
+            p.backward(dy[lo:hi], logits[lo:hi], weights, stream,
+                       x=None if x is None else x[lo:hi])
+            if i > 0:
+                for n, g in p.grads.items():
+                    moe_accumulate(g, self.grads[n], stream)
+                if p.base_grads is not None:
+                    for n, g in p.base_grads.items():
+                        moe_accumulate(g, self.base_grads[n], stream)
+        return self.dx, self.d_logits, self.grads
+
+    def step(self, x, logits, dy, weights: dict, stream=None):
+        self.forward(x, logits, weights, stream)
+        return self.backward(dy, logits, weights, stream, x=x)
 
 
 def _one_expert(w: dict) -> dict:
@@ -173,7 +303,7 @@ class MoELoRABlock:
     def backward(self, dy, x, w_r, weights: dict, shared_weights: dict | None = None,
                  stream=None):
         """Returns (dx, d_logits, routed LoRA grads, shared LoRA grads or None)."""
-        dx, dl, g = self.routed.backward(dy, self.logits, weights, stream)
+        dx, dl, g = self.routed.backward(dy, self.logits, weights, stream, x=x)
         moe_router_bwd(dl, w_r, dx, self.ws_router, stream)
         if self.shared is None:
             return dx, dl, g, None
@@ -212,14 +342,15 @@ class MoELoRAFunction(torch.autograd.Function):
         full = bool(ctx.needs_input_grad[2] or ctx.needs_input_grad[5])
         layer = MoELoRALayer(shape, router, device=x.device, full_ft=full)
         weights = dict(zip(WEIGHT_NAMES, (w_gu, a_gu, b_gu, w_d, a_d, b_d)))
-        y = layer.forward(x.contiguous(), logits.contiguous(), weights).clone()
-        ctx.layer, ctx.weights, ctx.logits = layer, weights, logits.contiguous()
+        x = x.contiguous()
+        y = layer.forward(x, logits.contiguous(), weights).clone()
+        ctx.layer, ctx.weights, ctx.logits, ctx.x = layer, weights, logits.contiguous(), x
         return y
 
     @staticmethod
     def backward(ctx, dy):
         layer = ctx.layer
-        dx, dl, g = layer.backward(dy.contiguous(), ctx.logits, ctx.weights)
+        dx, dl, g = layer.backward(dy.contiguous(), ctx.logits, ctx.weights, x=ctx.x)
         bg = layer.base_grads
         dw_gu = bg["dw_gu"].clone() if bg is not None and ctx.needs_input_grad[2] else None
         dw_d = bg["dw_d"].clone() if bg is not None and ctx.needs_input_grad[5] else None

@@ -117,7 +117,8 @@ def test_full_size_full_fine_tuning(name):
 
 def test_full_size_recompute_long_context():
     """Activation-lean mode at the long-context size: bit-identical to the
-    saving mode, with h and act no longer held between forward and backward."""
+    saving mode, with h, act and x_perm no longer held between forward and
+    backward."""
     import mixture_experts_lora_amd as mel
     cfg = CONFIGS["gpt-oss-20b-long"]
     say(f"[fullsize recompute] {cfg.name} T={cfg.T}")
@@ -131,7 +132,42 @@ def test_full_size_recompute_long_context():
     torch.cuda.synchronize()
     saved_a, saved_b = a.saved_bytes(), b.saved_bytes()
     say(f"  saved bytes: {saved_a / 1e9:.2f} GB -> {saved_b / 1e9:.2f} GB")
-    assert saved_a - saved_b == cfg.N * 3 * cfg.I * 2
+    # h [N, 2I], act [N, I] and x_perm [N, H] (gathered again in the backward)
+    assert saved_a - saved_b == cfg.N * (3 * cfg.I + cfg.H) * 2
     for t1, t2 in [(a.y, b.y), (a.dx, b.dx), (a.d_logits, b.d_logits)] + \
             [(a.grads[n], b.grads[n]) for n in a.grads]:
         assert torch.equal(t1, t2)
+
+
+def test_full_size_chunked_long_context():
+    """Long context in 4 token chunks, activation-lean: Y, dX and d logits
+    bit-identical to the unchunked lean layer, gradients close to its, and a
+    lower peak allocation (one chunk's workspaces instead of the whole
+    layer's)."""
+    import mixture_experts_lora_amd as mel
+    cfg = CONFIGS["gpt-oss-20b-long"]
+    say("[fullsize chunked] gpt-oss-20b-long, 4 chunks, lean")
+    inp = gpu_inputs(cfg, SEED)
+    w = {n: inp[n] for n in WEIGHTS}
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    b = mel.MoELoRAChunkedLayer(mel.Shape.of(cfg), cfg.router, 4, recompute=True)
+    b.step(inp["x"], inp["logits"], inp["dy"], w)
+    torch.cuda.synchronize()
+    peak_chunked = torch.cuda.max_memory_allocated() - base
+    ys, dxs, dls = b.y.clone(), b.dx.clone(), b.d_logits.clone()
+    gs = {n: v.clone() for n, v in b.grads.items()}
+    del b
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    a = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, recompute=True)
+    a.step(inp["x"], inp["logits"], inp["dy"], w)
+    torch.cuda.synchronize()
+    peak_whole = torch.cuda.max_memory_allocated() - base
+    say(f"  peak above inputs: whole {peak_whole / 1e9:.2f} GB, 4 chunks {peak_chunked / 1e9:.2f} GB")
+    assert torch.equal(a.y, ys) and torch.equal(a.dx, dxs) and torch.equal(a.d_logits, dls)
+    for n, v in gs.items():
+        close(n, to_numpy(v), to_numpy(a.grads[n]), 1e-2)
+    assert peak_chunked < 0.6 * peak_whole

@@ -124,6 +124,61 @@ def test_recompute_mode_is_bit_identical(name, full_ft):
         assert torch.equal(t1, t2)
 
 
+@pytest.mark.parametrize("name,chunks", [("tiny", 3), ("mini-bf16", 2), ("mini-skew", 4),
+                                         ("mini-f32", 3), ("mini-T1", 1), ("mini-split", 5),
+                                         ("mini-f16", 2)])
+@pytest.mark.parametrize("recompute", [False, True])
+def test_chunked_layer(name, chunks, recompute):
+    """The layer in token chunks: Y, dX and d logits (per token) bit-identical
+    to the unchunked layer; the LoRA gradients, summed over chunks, against
+    the oracle."""
+    mel = _mel()
+    cfg = PARITY_CONFIGS[name]
+    say(f"[chunked] {name} chunks={chunks} recompute={recompute}")
+    inp = gpu_inputs(cfg, 9)
+    w = {n: inp[n] for n in WEIGHTS}
+    a = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, recompute=recompute)
+    b = mel.MoELoRAChunkedLayer(mel.Shape.of(cfg), cfg.router, chunks, recompute=recompute)
+    a.step(inp["x"], inp["logits"], inp["dy"], w)
+    b.step(inp["x"], inp["logits"], inp["dy"], w)
+    torch.cuda.synchronize()
+    for t1, t2 in [(a.y, b.y), (a.dx, b.dx), (a.d_logits, b.d_logits)]:
+        assert torch.equal(t1, t2)
+    h = {n: to_numpy(v) for n, v in inp.items()}
+    _, g, _ = oracle.layer_forward_backward(h["x"], h["logits"], h["dy"], h, cfg.k, cfg.router,
+                                            cfg.lora_scale)
+    for n in ("da_gu", "db_gu", "da_d", "db_d"):
+        close(n, to_numpy(b.grads[n]), g[n], TOL[cfg.dtype])
+    assert b.saved_bytes() == a.saved_bytes()
+
+
+def test_chunked_full_fine_tuning():
+    mel = _mel()
+    cfg = PARITY_CONFIGS["mini-skew"]
+    say("[chunked full-ft] mini-skew")
+    inp = gpu_inputs(cfg, 10)
+    b = mel.MoELoRAChunkedLayer(mel.Shape.of(cfg), cfg.router, 3, full_ft=True, recompute=True)
+    b.step(inp["x"], inp["logits"], inp["dy"], {n: inp[n] for n in WEIGHTS})
+    torch.cuda.synchronize()
+    h = {n: to_numpy(v) for n, v in inp.items()}
+    _, g, _ = oracle.layer_forward_backward(h["x"], h["logits"], h["dy"], h, cfg.k, cfg.router,
+                                            cfg.lora_scale, base_grads=True)
+    for n in ("dw_gu", "dw_d"):
+        close(n, to_numpy(b.base_grads[n]), g[n], TOL[cfg.dtype])
+
+
+def test_lean_backward_needs_x():
+    mel = _mel()
+    cfg = PARITY_CONFIGS["mini-bf16"]
+    inp = gpu_inputs(cfg, 11)
+    w = {n: inp[n] for n in WEIGHTS}
+    layer = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, recompute=True)
+    layer.forward(inp["x"], inp["logits"], w)
+    with pytest.raises(ValueError):
+        layer.backward(inp["dy"], inp["logits"], w)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("name", ["mini-bf16", "mini-skew", "tiny"])
 def test_layer_is_deterministic(name):
     """Atomic-free kernels: two runs give bit-identical outputs."""
