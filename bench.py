@@ -402,10 +402,15 @@ def main():
     peak = PEAK_BF16_TFLOPS if half else PEAK_F32_TFLOPS
     dom = max((k for k in GEMM_KERNELS if k in kms), key=lambda k: kms[k]["ms_per_step"])
     # FLOPs of the dominant kernel per step over its summed launch time per step.
-    # Every part (the routed layer; in block mode also the shared expert)
-    # launches each GEMM kernel equally often (twice for gate_up_fwd when the
+    # Every part (the routed layer, or each token chunk; in block mode also the
+    # shared expert) launches each GEMM kernel equally often (twice for gate_up_fwd when the
     # backward recomputes h; base_wgrad's figure is the mean of its two launches).
-    parts = [c for c in block_parts(cfg, shared_I) if c is not None] if args.block else [cfg]
+    if args.block:
+        parts = [c for c in block_parts(cfg, shared_I) if c is not None]
+    elif args.chunks > 1:
+        parts = [cfg.with_(T=hi - lo) for lo, hi in layer.bounds]
+    else:
+        parts = [cfg]
     dom_launches = kms[dom]["launches"] / args.steps
     dom_flops_step = dom_launches / len(parts) * sum(kernel_flops(dom, c) for c in parts)
     dom_tf = dom_flops_step / (kms[dom]["ms_per_step"] / 1e3) / 1e12
