@@ -115,6 +115,9 @@ PARITY_CONFIGS = {
     "mini-f16-skew": LayerConfig("mini-f16-skew", T=1100, H=264, I=136, E=16, k=4, r=32,
                                  dtype="f16", router="sigmoid_topk_renorm", zipf_s=1.2,
                                  n_dead=4, lora_scale=2.0),
+    # the largest expert count and top-k the library accepts: about two rows per expert
+    "max-E-k": LayerConfig("max-E-k", T=64, H=64, I=32, E=1024, k=32, r=8,
+                           dtype="bf16", router="softmax_topk"),
 }
 
 
