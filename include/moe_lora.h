@@ -279,7 +279,7 @@ moe_status moe_merge_lora(const moe_shape *shape, const moe_weights *weights, vo
 
 /* dst[i] += src[i] for i < n, elements of `dtype`, sum in float32, one
  * rounding (adds a shared expert's output to the routed output, and its input
- * gradient to dx). src and dst may not alias.  */
+ * gradient to dx). src and dst may not overlap (MOE_ERR_INVALID_ARG).  */
 moe_status moe_accumulate(int32_t dtype, int64_t n, const void *src, void *dst, void *stream);
 
 const char *moe_status_str(moe_status status);

@@ -548,7 +548,11 @@ moe_status moe_accumulate(int32_t dtype, int64_t n, const void* src, void* dst, 
   if (n == 0) return MOE_OK;
   CHECK_PTR(src);
   CHECK_PTR(dst);
-  if (src == dst) return fail(MOE_ERR_INVALID_ARG, "src and dst alias");
+  {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t bytes = static_cast<uintptr_t>(n) * (dtype == MOE_F32 ? 4 : 2);
+    if (a < b + bytes && b < a + bytes) return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
+  }
   hipError_t e = moe::launch_accumulate(dtype, n, src, dst, as_stream(stream), moe::active_timer());
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_accumulate");
 }

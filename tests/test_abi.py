@@ -186,6 +186,8 @@ def test_router_and_accumulate_validate(lib):
     assert lib.moe_accumulate(1, -1, fake, P(0x20000), None) == 1
     assert lib.moe_accumulate(3, 16, fake, P(0x20000), None) == 1            # no such dtype
     assert lib.moe_accumulate(1, 16, fake, fake, None) == 1
+    assert lib.moe_accumulate(1, 16, fake, P(0x10000 + 30), None) == 1   # partial overlap
+    assert lib.moe_accumulate(0, 16, P(0x10000 + 60), fake, None) == 1    # f32: 64 bytes
 
 
 def test_merge_validates(lib):
