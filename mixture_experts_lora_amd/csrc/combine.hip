@@ -83,14 +83,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   float acc[n];
 #pragma unroll
   for (int i = 0; i < n; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int pos = inv_pos[t * k + j];
-    if (pos < 0) continue;
-    const float wj = w ? w[t * k + j] : 1.0f;
-    float v[n];
-    Pack<Elem>::unpack(yp[static_cast<int64_t>(pos) * cpr + c], v);
+  // slots in groups of four: the group's row loads are all issued before
+  // any is summed (several loads in flight per thread), and the sum still
+  // runs in slot order
+  constexpr int G = 4;
+  for (int j0 = 0; j0 < k; j0 += G) {
+    int pos[G];
+    float wj[G];
+    uint4 raw[G];
 #pragma unroll
-    for (int i = 0; i < n; ++i) acc[i] += wj * v[i];
+    for (int u = 0; u < G; ++u) {
+      const int j = j0 + u;
+      pos[u] = j < k ? inv_pos[t * k + j] : -1;
+      wj[u] = j < k && w ? w[t * k + j] : 1.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (pos[u] >= 0) raw[u] = yp[static_cast<int64_t>(pos[u]) * cpr + c];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      if (pos[u] < 0) continue;
+      float v[n];
+      Pack<Elem>::unpack(raw[u], v);
+#pragma unroll
+      for (int i = 0; i < n; ++i) acc[i] += wj[u] * v[i];
+    }
   }
   y[t * cpr + c] = Pack<Elem>::pack(acc);
 }
