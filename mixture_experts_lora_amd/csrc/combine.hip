@@ -11,6 +11,8 @@
 // experts closes the MoE block whose per-expert loop the faster-moe page
 // (Unsloth, "Fine-tune MoE models 12x faster", section "What is
 // torch._grouped_mm?") shows.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -112,8 +114,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   y[t * cpr + c] = Pack<Elem>::pack(acc);
 }
 
-// One block per token; threads stride over the row's 16-byte chunks.
-template <typename Elem>
+// One block per token; threads stride over the row's 16-byte chunks. Each
+// thread loads its chunks of dY once and serves every slot from them, keeping
+// one partial dot product per slot (KMAX >= k slots, unrolled), so the slots'
+// row loads are in flight together; the block reduces all slots at the end in
+// the same order as slot by slot (per-thread chunk order, wave tree, waves in
+// order), which leaves dw bit-identical.
+template <typename Elem, int KMAX>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dy,
                                                           const uint4* __restrict__ yexp,
                                                           const int32_t* __restrict__ inv_pos,
@@ -121,36 +128,50 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
                                                           int64_t cpr, uint4* __restrict__ g,
                                                           float* __restrict__ dw) {
   constexpr int n = Pack<Elem>::n;
-  __shared__ float red[256 / kWave];
+  constexpr int NWV = 256 / kWave;
+  __shared__ float red[KMAX][NWV];
   const int64_t t = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  for (int j = 0; j < k; ++j) {
-    const int pos = inv_pos[t * k + j];
-    const float wj = w[t * k + j];
-    float part = 0.f;
-    if (pos >= 0) {
-      for (int64_t c = threadIdx.x; c < cpr; c += blockDim.x) {
-        float d[n], y[n], o[n];
-        Pack<Elem>::unpack(dy[t * cpr + c], d);
-        Pack<Elem>::unpack(yexp[static_cast<int64_t>(pos) * cpr + c], y);
+  int pos[KMAX];
+  float wj[KMAX], part[KMAX];
 #pragma unroll
-        for (int i = 0; i < n; ++i) {
-          part += d[i] * y[i];
-          o[i] = wj * d[i];
-        }
-        g[static_cast<int64_t>(pos) * cpr + c] = Pack<Elem>::pack(o);
+  for (int j = 0; j < KMAX; ++j) {
+    pos[j] = j < k ? inv_pos[t * k + j] : -1;
+    wj[j] = j < k ? w[t * k + j] : 0.f;
+    part[j] = 0.f;
+  }
+  for (int64_t c = threadIdx.x; c < cpr; c += blockDim.x) {
+    float d[n];
+    Pack<Elem>::unpack(dy[t * cpr + c], d);
+    uint4 raw[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (pos[j] >= 0) raw[j] = yexp[static_cast<int64_t>(pos[j]) * cpr + c];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (pos[j] < 0) continue;
+      float y[n], o[n];
+      Pack<Elem>::unpack(raw[j], y);
+#pragma unroll
+      for (int i = 0; i < n; ++i) {
+        part[j] += d[i] * y[i];
+        o[i] = wj[j] * d[i];
       }
+      g[static_cast<int64_t>(pos[j]) * cpr + c] = Pack<Elem>::pack(o);
     }
-    part = wave_sum(part);
-    if (lane == 0) red[wave] = part;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float s = 0.f;
+  }
 #pragma unroll
-      for (int i = 0; i < 256 / kWave; ++i) s += red[i];
-      dw[t * k + j] = s;
-    }
-    __syncthreads();
+  for (int j = 0; j < KMAX; ++j) {
+    if (j >= k) break;
+    const float v = wave_sum(part[j]);
+    if (lane == 0) red[j][wave] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < k) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) s += red[threadIdx.x][i];
+    dw[t * k + threadIdx.x] = s;
   }
 }
 
@@ -184,18 +205,20 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_exp,
   const int esz = dtype == MOE_F32 ? 4 : 2;
   const int64_t cpr = static_cast<int64_t>(H) * esz / 16;
   TimedScope scope(tm, MOE_K_COMBINE_BWD, s);
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(T), dim3(256), 0, s,
-                       static_cast<const uint4*>(dy), static_cast<const uint4*>(y_exp), inv_pos,
-                       w, k, cpr, static_cast<uint4*>(g), dw);
-  else if (dtype == MOE_F16)
-    hipLaunchKernelGGL(combine_bwd_kernel<f16_t>, dim3(T), dim3(256), 0, s,
-                       static_cast<const uint4*>(dy), static_cast<const uint4*>(y_exp), inv_pos,
-                       w, k, cpr, static_cast<uint4*>(g), dw);
-  else
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(T), dim3(256), 0, s,
-                       static_cast<const uint4*>(dy), static_cast<const uint4*>(y_exp), inv_pos,
-                       w, k, cpr, static_cast<uint4*>(g), dw);
+  auto go = [&](auto tag, auto kmax) {
+    using Elem = decltype(tag);
+    hipLaunchKernelGGL((combine_bwd_kernel<Elem, decltype(kmax)::value>), dim3(T), dim3(256), 0,
+                       s, static_cast<const uint4*>(dy), static_cast<const uint4*>(y_exp),
+                       inv_pos, w, k, cpr, static_cast<uint4*>(g), dw);
+  };
+  auto by_k = [&](auto tag) {
+    if (k <= 4) go(tag, std::integral_constant<int, 4>());
+    else if (k <= 8) go(tag, std::integral_constant<int, 8>());
+    else go(tag, std::integral_constant<int, 32>());
+  };
+  if (dtype == MOE_BF16) by_k(bf16_t{});
+  else if (dtype == MOE_F16) by_k(f16_t{});
+  else by_k(float{});
   return hipGetLastError();
 }
 
