@@ -499,14 +499,18 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // Epilogue traffic is streamed once: non-temporal loads and stores keep it
 // from evicting the operand tiles the other blocks are reading from L2.
 template <bool F16>
-__device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
-  const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+__device__ __forceinline__ void unpack8(const u32x4& r, float (&v)[8]) {
   const uint32_t w[4] = {r[0], r[1], r[2], r[3]};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     v[2 * j] = h16_to_f32<F16>(static_cast<uint16_t>(w[j] & 0xffffu));
     v[2 * j + 1] = h16_to_f32<F16>(static_cast<uint16_t>(w[j] >> 16));
   }
+}
+
+template <bool F16>
+__device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
+  unpack8<F16>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)), v);
 }
 
 template <bool F16>
@@ -919,8 +923,32 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
                         (p.out_estride & 3) == 0;
   const bool aux_vec = p.aux == nullptr ||
                        ((reinterpret_cast<uintptr_t>(p.aux) & 15) == 0 && (p.ld_aux & 7) == 0);
+  // SwiGLU backward: the h segments a slab needs are loaded while the previous
+  // slab is finished, so one load latency per tile is exposed rather than one
+  // per slab (the epilogue reads h [rows, 2I] and writes dH of the same size).
+  // (wave tiles up to 64 wide: two slabs of h take 64 VGPRs; wider ones load per slab)
+  constexpr bool HPRE = MODE == GROUP_M && EPI == EPI_SWIGLU_BWD && !PAIRED && WN <= 64;
+  constexpr int HSEGS = WN / 8, HRPP = 64 / HSEGS, HPASS = 32 / HRPP;
+  u32x4 hpre[2][HPASS][2];
+  auto hfetch = [&](int mi, u32x4 (&hb)[HPASS][2]) {
+    const int mb = wm * WM + mi * 32;
+#pragma unroll
+    for (int pass = 0; pass < HPASS; ++pass) {
+      const int m_local = mb + pass * HRPP + lane / HSEGS;
+      const int col = n0 + wn * WN + 8 * (lane % HSEGS);
+      if (m_local < rows && col < p.N) {  // N = I, a multiple of 8
+        const bf16_t* hr = static_cast<const bf16_t*>(p.aux) + (row0 + m_local) * p.ld_aux;
+        hb[pass][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(hr + col));
+        hb[pass][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(hr + p.I + col));
+      }
+    }
+  };
+  if constexpr (HPRE) hfetch(0, hpre[0]);
 #pragma unroll
   for (int mi = 0; mi < MF; ++mi) {
+    if constexpr (HPRE) {
+      if (mi + 1 < MF) hfetch(mi + 1, hpre[(mi + 1) & 1]);
+    }
     if (mi) wave_lds_sync();  // previous slab fully read
 #pragma unroll
     for (int ni = 0; ni < NF; ++ni)
@@ -967,10 +995,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
         if (MODE == GROUP_M && EPI == EPI_SWIGLU_BWD) {
           if (col >= p.N) continue;  // N = I, a multiple of 8
           const int64_t row = row0 + m_local;
-          const bf16_t* hr = static_cast<const bf16_t*>(p.aux) + row * p.ld_aux;
           float g[8], u[8], dg[8], du[8];
-          load8<F16>(hr + col, g);
-          load8<F16>(hr + p.I + col, u);
+          if constexpr (HPRE) {
+            unpack8<F16>(hpre[mi & 1][pass][0], g);
+            unpack8<F16>(hpre[mi & 1][pass][1], u);
+          } else {
+            const bf16_t* hr = static_cast<const bf16_t*>(p.aux) + row * p.ld_aux;
+            load8<F16>(hr + col, g);
+            load8<F16>(hr + p.I + col, u);
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j) swiglu_bwd(g[j], u[j], v[j], dg[j], du[j]);
           bf16_t* dr = static_cast<bf16_t*>(p.out) + row * p.ld_out;
