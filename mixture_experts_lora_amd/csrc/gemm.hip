@@ -24,15 +24,17 @@
 //  - GROUP_K: the reduction runs over an expert's rows (the LoRA weight
 //    gradients), one block per (expert, M tile, N tile), so no atomics and
 //    bit-identical results run to run.
-// Operands are staged through LDS with k contiguous. Operands stored with k
-// contiguous (activations; forward weights) are copied as 16-byte chunks;
-// operands stored with the output dimension contiguous (backward weights,
-// and both operands of the weight gradients) are transposed in registers in
-// 4x8 blocks on their way into LDS. bf16 products use the gfx950
-// v_mfma_f32_32x32x16_bf16 instruction with float32 accumulation; the
-// weight tile is the MFMA A operand so that each lane ends up holding four
-// consecutive output columns of one row (8-byte stores). float32 layers use a
-// plain FMA kernel with the same tiling logic.
+//  - GROUP_KV: GROUP_K for dB = D^T U that also forms, from the D rows it
+//    already holds in LDS, float32 partials of the side product D B over its
+//    feature tile (summed over tiles by a second kernel), so that D is read
+//    once for both.
+// Operands are staged through LDS in 16-byte chunks, in the layout they have
+// in memory (k-contiguous or output-contiguous, XOR-swizzled); fragments of
+// output-contiguous tiles are read with the gfx950 transpose read. 16-bit
+// products use v_mfma_f32_32x32x16_bf16 (or _f16) with float32 accumulation;
+// the weight fragment is the MFMA A operand so that each lane ends up holding
+// consecutive output columns of one row. float32 layers use a plain FMA
+// kernel with the same tiling logic.
 #include <stdlib.h>
 
 #include <algorithm>
@@ -45,7 +47,7 @@ namespace moe {
 
 namespace {
 
-enum Mode { GROUP_M = 0, GROUP_K = 1 };
+enum Mode { GROUP_M = 0, GROUP_K = 1, GROUP_KV = 2 };
 // EPI_STORE_F32: float32 output (router logits); EPI_ADD: out = src + result
 // with src = aux when given (merged export: W + s B A) else out itself (an
 // accumulate); the sum formed in float32, one rounding.
@@ -79,6 +81,13 @@ struct GemmArgs {
   int I;  // gate width for SwiGLU epilogues / paired weight rows
   float scale;
   int dtype;  // host side only: MOE_BF16 or MOE_F16 picks the 16-bit kernel
+  // GROUP_KV: B of the side product (per expert [M, N] row-major, expert e of
+  // the launch uses B[e / vsplit]) and its float32 partials vp[M tile][row][N]
+  const void* vb;
+  int64_t vb_estride;
+  float* vp;
+  int64_t vp_tstride;  // elements between M tiles of vp
+  int vsplit;
 };
 
 // Spread `total` logical tiles over the 8 XCDs so that each XCD works on a
@@ -545,7 +554,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
   static_assert(GA::TI >= 1 && GB::TI >= 1, "tile smaller than one DMA instruction");
   static_assert(VST || (NST >= 3 && NST <= 6 && (NST - 2) * (GA::MINW + GB::MINW) <= 63),
                 "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) char smem[NST * ST];
+  // GROUP_KV: + the block's [BM][32] tile of the side-product B
+  constexpr int VB_BYTES = MODE == GROUP_KV ? BM * 32 * 2 : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * ST + VB_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a wave-uniform (scalar) value, so that everything derived
@@ -689,6 +700,35 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
     for (int j = 0; j < NF; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // GROUP_KV: this block's feature rows of the expert's side-product B, as
+  // MFMA fragments over the whole tile (k = feature, n = column of B; lane l
+  // holds column l%32 and features 8(l/32)..+7 of each 16-feature step). The
+  // [BM][32] tile goes through LDS in 16-byte pieces (zero-padded past M and
+  // N; rows of B are 16-byte aligned, N a multiple of 8) and is read back
+  // with transpose reads, like any output-contiguous operand.
+  static_assert(MODE != GROUP_KV || (BM == 256 && BN == 32 && BK == 32 && !A_KC && VST == 0),
+                "side-product partials assume 256 x 32 tiles, 32 rows per k tile");
+  constexpr int VKS = MODE == GROUP_KV ? BM / 16 : 1;
+  bf16x8 vbf[VKS];
+  if constexpr (MODE == GROUP_KV) {
+    const bf16_t* bm = static_cast<const bf16_t*>(p.vb) +
+                       static_cast<int64_t>(e / p.vsplit) * p.vb_estride;
+    char* vt = smem + NST * ST;
+    for (int i = tid; i < BM * 4; i += NW * 64) {  // piece i: feature i/4, columns 8 (i%4)..
+      const int f = i >> 2, c = i & 3;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (m0 + f < p.M && c * 8 < p.N)
+        v = *reinterpret_cast<const u32x4*>(bm + static_cast<int64_t>(m0 + f) * p.N + c * 8);
+      *reinterpret_cast<u32x4*>(vt + f * 64 + c * 16) = v;
+    }
+    __syncthreads();
+    FragAddr<32, BM, false, 1> FV;
+    const int zero[1] = {0};
+    frag_addr<32, BM, false, 1>(FV, zero, lane);
+#pragma unroll
+    for (int kk = 0; kk < VKS; ++kk) vbf[kk] = read_frag<32, BM, false, 1>(vt, FV, 0, 0, kk);
+  }
 
   if constexpr (VST > 0) {
     // ---- Register-staged main loop: every wave loads its share of a k tile
@@ -957,6 +997,37 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
   #pragma unroll
           for (int ni = 0; ni < NF; ++ni)
             acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
+      }
+      if constexpr (MODE == GROUP_KV) {
+        // The A stage holds rows it*BK.. of the expert's D as [BK rows][BM
+        // features] (output-contiguous layout). One wave per k tile, in turn,
+        // multiplies those 32 rows by B over the tile's features and stores
+        // the float32 partial; the stage stays valid until the next barrier.
+        if (wave == it % NW) {
+          f32x16 av;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) av[v] = 0.f;
+          const int kr = lane & 31, hb = lane >> 5;
+#pragma unroll
+          for (int kk = 0; kk < VKS; ++kk) {
+            const int chunk = 2 * kk + hb;  // 8 features 16 kk + 8 hb ..
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                sa + kr * BM * 2 + ((chunk ^ nswz<BM>(kr)) << 4));
+            av = mfma32<F16>(vbf[kk], a, av);
+          }
+          // lane holds row kr and columns 8 q + 4 hb + (0..3) for q = 0..3
+          const int rowl = it * BK + kr;
+          if (rowl < krows) {
+            float* vr = p.vp + static_cast<int64_t>(m0 / BM) * p.vp_tstride +
+                        (row0 + rowl) * static_cast<int64_t>(p.N);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int j = 8 * q + 4 * hb;
+              if (j < p.N)
+                *reinterpret_cast<f32x4*>(vr + j) = f32x4{av[4 * q], av[4 * q + 1], av[4 * q + 2], av[4 * q + 3]};
+            }
+          }
+        }
       }
     }
 
@@ -1527,6 +1598,12 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
 template <int EPI>
 hipError_t weight_grad_launch(const ExpertDims& d, GemmArgs& a, int E, int P, int Q,
                               hipStream_t s) {
+  if (a.vp) {  // [big, r <= 32] with side-product partials (checked by the caller)
+    a.ntn = 1;
+    a.ntm = ceil_div(P, 256);
+    return launch(GEMM16(a.dtype, 256, 32, 64, 32, 32, 3, 2, GROUP_KV, EPI, false, false, false, 0),
+                  E * a.ntm, a, s);
+  }
   if (d.dtype != MOE_F32) {
     if (Q <= 64 && P > 64) {  // [big, r]
       a.ntn = 1;
@@ -1559,10 +1636,55 @@ hipError_t weight_grad_launch(const ExpertDims& d, GemmArgs& a, int E, int P, in
   return launch(gemm_f32<GROUP_K, EPI_STORE, false>, E * a.ntm * a.ntn, a, s);
 }
 
+#define MOE_TRY_WG(x)                   \
+  do {                                  \
+    hipError_t err_ = (x);              \
+    if (err_ != hipSuccess) return err_; \
+  } while (0)
+
+// Side product fused into a LoRA B gradient (see GROUP_KV): alongside
+// dB = D^T U it forms V = scale * D Bm with Bm per expert [P, Q].
+struct SideOut {
+  const void* bm = nullptr;   // [E][P][Q]
+  void* out = nullptr;        // V [N, Q] in the layer dtype
+  float* part = nullptr;      // ceil(P / 256) x N x Q float32 partials
+};
+
+// The fused path covers 16-bit layers, Q = r <= 32 with rows of 16 bytes.
+inline bool side_fusable(const ExpertDims& d, int P, int Q) {
+  return d.dtype != MOE_F32 && Q <= 32 && Q % 8 == 0 && P % 8 == 0 && P > 64;
+}
+
+inline size_t side_part_bytes(const ExpertDims& d) {
+  const int P = std::max(d.H, 2 * d.I);
+  return static_cast<size_t>(ceil_div(P, 256)) * d.N * d.r * 4;
+}
+
+// V[i] = scale * sum over tiles t (in order) of part[t][i]
+template <typename Elem>
+__global__ __launch_bounds__(256) void side_sum_kernel(const float* __restrict__ part, int tiles,
+                                                       int64_t tstride, float scale,
+                                                       Elem* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= tstride) return;
+  float acc = 0.f;
+  for (int t = 0; t < tiles; ++t) acc += part[t * tstride + i];
+  out[i] = from_f32<Elem>(acc * scale);
+}
+
 // split_ws: at least wgrad_split_bytes(d, P, Q) bytes (unused when that is 0).
+// side (optional, side_fusable only): also form V = scale D Bm.
 hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* Lm, int P,
-                       const void* Rm, int Q, void* out, hipStream_t s, void* split_ws) {
+                       const void* Rm, int Q, void* out, hipStream_t s, void* split_ws,
+                       const SideOut* side = nullptr) {
   GemmArgs a{};
+  a.vsplit = 1;
+  if (side) {
+    a.vb = side->bm;
+    a.vb_estride = static_cast<int64_t>(P) * Q;
+    a.vp = side->part;
+    a.vp_tstride = d.N * Q;
+  }
   a.a[1] = none();
   a.b[1] = none();
   a.M = P;
@@ -1574,13 +1696,28 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
   a.a[0] = opnd(Lm, 0, P, 0, P % 8 == 0);
   a.b[0] = opnd(Rm, 0, Q, 0, Q % 8 == 0);
   const int S = wgrad_splits(d, P, Q);
+  auto side_sum = [&]() -> hipError_t {
+    if (!side) return hipSuccess;
+    const int tiles = ceil_div(P, 256);
+    const int64_t n = d.N * Q;
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+    if (d.dtype == MOE_BF16)
+      hipLaunchKernelGGL(side_sum_kernel<bf16_t>, grid, dim3(256), 0, s, side->part, tiles, n,
+                         d.scale, static_cast<bf16_t*>(side->out));
+    else
+      hipLaunchKernelGGL(side_sum_kernel<f16_t>, grid, dim3(256), 0, s, side->part, tiles, n,
+                         d.scale, static_cast<f16_t*>(side->out));
+    return hipGetLastError();
+  };
   if (S <= 1) {
     a.E = d.E;
     a.offsets = offsets;
     a.out = out;
-    return weight_grad_launch<EPI_STORE>(d, a, d.E, P, Q, s);
+    MOE_TRY_WG(weight_grad_launch<EPI_STORE>(d, a, d.E, P, Q, s));
+    return side_sum();
   }
   const int G = d.E * S;
+  a.vsplit = S;
   int32_t* voff = static_cast<int32_t*>(split_ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(split_ws) +
                                          align_up(static_cast<size_t>(G + 1) * 4));
@@ -1601,7 +1738,8 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
   else
     hipLaunchKernelGGL(reduce_splits_kernel<float>, grid, dim3(256), 0, s, part,
                        static_cast<float*>(out), S, PQ, total);
-  return hipGetLastError();
+  MOE_TRY_WG(hipGetLastError());
+  return side_sum();
 }
 
 #define MOE_TRY(x)                      \
@@ -1622,6 +1760,7 @@ size_t experts_bwd_ws_bytes(const ExpertDims& d) {
   b += align_up(static_cast<size_t>(d.N) * d.r * esz) * 2;        // G B_d, dH B_gu
   b += align_up(static_cast<size_t>(d.N) * 2 * d.I * esz);         // dH
   b += align_up(lora_wgrad_split_bytes(d));                         // split-K partials
+  if (d.dtype != MOE_F32) b += align_up(side_part_bytes(d));        // fused side products
   return b;
 }
 
@@ -1729,9 +1868,23 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
   void* dh = p;
   p += align_up(static_cast<size_t>(d.N) * 2 * I * esz);
   void* split = p;
+  p += align_up(lora_wgrad_split_bytes(d));
+  float* vpart = reinterpret_cast<float*>(p);
+  // The side products G B_d and dH B_gu read the same matrices as the
+  // gradients dB_d = G^T u_d and dB_gu = dH^T u_gu; where the shapes allow,
+  // one kernel reads each matrix once for both.
+  const bool fuse_d = side_fusable(d, H, r) && aligned16(w.b_d);
+  const bool fuse_gu = side_fusable(d, 2 * I, r) && aligned16(w.b_gu);
 
   MOE_TRY(build_tiles(L, offsets, d.E, s));
-  {  // gb = s G B_d      (B_d[e] is [H, r]: K = H rows, r contiguous)
+  if (fuse_d) {  // dB_d = G^T u_d [H, r] and gb = s G B_d in one pass over G
+    TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
+    SideOut so;
+    so.bm = w.b_d;
+    so.out = gb;
+    so.part = vpart;
+    MOE_TRY(weight_grad(d, offsets, g, H, sv.u_d, r, gr.db_d, s, split, &so));
+  } else {  // gb = s G B_d      (B_d[e] is [H, r]: K = H rows, r contiguous)
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
     MOE_TRY(side_product(d, offsets, L, g, H, w.b_d, static_cast<int64_t>(H) * r, 0, gb, s));
   }
@@ -1758,16 +1911,23 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
       MOE_TRY(launch(gemm_f32<GROUP_M, EPI_SWIGLU_BWD, false>, gm_grid(d, L.big, a.ntn), a, s));
     }
   }
-  {  // dB_d = G^T u_d  [H, r] ;  dA_d = gb^T act  [r, I]
+  {  // dB_d = G^T u_d  [H, r] (unless fused above) ;  dA_d = gb^T act  [r, I]
     TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
-    MOE_TRY(weight_grad(d, offsets, g, H, sv.u_d, r, gr.db_d, s, split));
+    if (!fuse_d) MOE_TRY(weight_grad(d, offsets, g, H, sv.u_d, r, gr.db_d, s, split));
     MOE_TRY(weight_grad(d, offsets, gb, r, sv.act, I, gr.da_d, s, split));
   }
   if (base) {  // full fine-tuning: dW_d = G^T act  [H, I]
     TimedScope ts(tm, MOE_K_BASE_WGRAD, s);
     MOE_TRY(weight_grad(d, offsets, g, H, sv.act, I, base->dw_d, s, nullptr));
   }
-  {  // dhb = s dH B_gu   (B_gu[e] is [2I, r])
+  if (fuse_gu) {  // dB_gu = dH^T u_gu [2I, r] and dhb = s dH B_gu in one pass over dH
+    TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
+    SideOut so;
+    so.bm = w.b_gu;
+    so.out = dhb;
+    so.part = vpart;
+    MOE_TRY(weight_grad(d, offsets, dh, 2 * I, sv.u_gu, r, gr.db_gu, s, split, &so));
+  } else {  // dhb = s dH B_gu   (B_gu[e] is [2I, r])
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
     MOE_TRY(side_product(d, offsets, L, dh, 2 * I, w.b_gu, static_cast<int64_t>(2) * I * r, 0,
                          dhb, s));
@@ -1793,9 +1953,9 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
       MOE_TRY(launch(gemm_f32<GROUP_M, EPI_STORE, false>, gm_grid(d, L.big, a.ntn), a, s));
     }
   }
-  {  // dB_gu = dH^T u_gu  [2I, r] ;  dA_gu = dhb^T X  [r, H]
+  {  // dB_gu = dH^T u_gu  [2I, r] (unless fused above) ;  dA_gu = dhb^T X  [r, H]
     TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
-    MOE_TRY(weight_grad(d, offsets, dh, 2 * I, sv.u_gu, r, gr.db_gu, s, split));
+    if (!fuse_gu) MOE_TRY(weight_grad(d, offsets, dh, 2 * I, sv.u_gu, r, gr.db_gu, s, split));
     MOE_TRY(weight_grad(d, offsets, dhb, r, x_perm, H, gr.da_gu, s, split));
   }
   if (base) {  // full fine-tuning: dW_gu = dH^T X  [2I, H]
