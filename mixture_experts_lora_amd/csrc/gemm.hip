@@ -901,16 +901,24 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
           if (it + 1 + NRB < nk) load_tile(it + 1 + NRB, ra[BUF], rb[BUF]);
         }
         if constexpr (MFMA) {
-          // Output-contiguous weights (the backward GEMMs) read their
-          // fragments with twice the LDS instructions; the compiler's
-          // MFMA/LDS interleaving strategy measured 1-3% faster on those
-          // kernels and slightly slower on the forward ones.
+          // Instruction order within the k-step, by measurement: output-
+          // contiguous weights (the backward GEMMs, twice the LDS reads per
+          // fragment) take the compiler's MFMA/LDS interleaving strategy
+          // (1-3% faster there); k-contiguous ones (the forward GEMMs) place
+          // one LDS read after each MFMA (gate_up forward 1-2% faster).
           if constexpr (!B_KC) __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
           for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
             for (int ni = 0; ni < NF; ++ni)
               acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
+          if constexpr (B_KC) {
+#pragma unroll
+            for (int i = 0; i < MF * NF; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            }
+          }
         }
         if constexpr (FSB) next_frags(it, ks, 0);
       }
