@@ -776,19 +776,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
         }
       }
     };
-    // With two register buffers, the compiler's waits for a tile's loads must
-    // count the next tile's loads as still in flight. Its in-order load
-    // counter is exact only if the same loads are issued on every path, so:
-    // the plans are switched to the LoRA segment's once, when its first tile
-    // is loaded (tiles are loaded in order; the branch holds register moves
-    // only), and live = false issues the loads with every lane out of range
-    // (they return zeros and touch no memory) instead of skipping them.
+    // Branch-free issue (BF). With two register buffers the compiler's waits
+    // for a tile's loads must count the next tile's loads as still in
+    // flight, and its in-order load counter is exact only if every path
+    // issues the same loads; for the forward GEMMs a k-step without branches
+    // also lets the staging stores and loads interleave with its MFMAs
+    // (measured faster there, slower for the backward GEMMs). So: the plans
+    // switch to the LoRA segment's once, before its first tile is loaded
+    // (tiles are loaded in order), and live = false issues the loads with
+    // every lane out of range (they return zeros and touch no memory)
+    // instead of skipping them.
+    constexpr bool BF = NRB >= 2 || B_KC;
+    auto switch_plans = [&]() __attribute__((always_inline)) {
+      pa0 = pa1;
+      pb0 = pb1;
+    };
     auto load_tile = [&](int j, u32x4* a, u32x4* b, bool live = true) __attribute__((always_inline)) {
-      if constexpr (NRB >= 2) {
-        if (j == nk0) {
-          pa0 = pa1;
-          pb0 = pb1;
-        }
+      if constexpr (BF) {
         const int k0 = (j >= nk0 ? j - nk0 : j) * BK;
         vload(pa0, k0, a, GeoK<GA, A_KC>(), live);
         vload(pb0, k0, b, GeoK<GB, B_KC>(), live);
@@ -818,11 +822,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
     };
     bf16x8 af[NRB >= 2 ? 1 : 2][MF], bf[NRB >= 2 ? 1 : 2][NF];
     if (nk > 0) {
+      if (BF && nk0 == 0) switch_plans();
       load_tile(0, ra[0], rb[0]);
       store_tile(0, ra[0], rb[0]);
 #pragma unroll
-      for (int q = 1; q <= NRB; ++q)
+      for (int q = 1; q <= NRB; ++q) {
+        if (BF && q == nk0) switch_plans();
         if (q < nk) load_tile(q, ra[q % NRB], rb[q % NRB]);
+      }
       __syncthreads();
 #pragma unroll
       for (int mi = 0; mi < MF; ++mi) af[0][mi] = read_frag<BM, BK, A_KC, MF>(smem, FA, mi, fa_base[mi], 0);
@@ -864,6 +871,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
       constexpr bool MFMA = decltype(mfmac)::value;
       const char* sa = smem + (it % NST) * ST;
       const char* sb = sa + A_BYTES;
+      // the tile loaded in this k tile is it+1+NRB
+      if (BF && it + 1 + NRB == nk0) switch_plans();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int cur = FSB ? 0 : ks & 1;
@@ -890,9 +899,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
             bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(na + A_BYTES, FB, ni, fb_base[ni], 0);
         }
         // tile it+1's slot was last read in tile it-1, before the last barrier
-        if constexpr (NRB >= 2) {
+        if constexpr (BF) {
           if (ks == 1) {
-            if (it + 1 < nk) store_tile(it + 1, ra[BUF], rb[BUF]);
+            // past the last tile this stores the zeros of an out-of-range
+            // load into a slot nobody reads again
+            store_tile(it + 1, ra[BUF], rb[BUF]);
             const int jn = it + 1 + NRB;
             load_tile(min(jn, nk - 1), ra[BUF], rb[BUF], jn < nk);
           }
@@ -905,7 +916,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
           // contiguous weights (the backward GEMMs, twice the LDS reads per
           // fragment) take the compiler's MFMA/LDS interleaving strategy
           // (1-3% faster there); k-contiguous ones (the forward GEMMs) place
-          // one LDS read after each MFMA (gate_up forward 1-2% faster).
+          // one LDS read, and in the staging k-step also one LDS write and
+          // one buffer load, after each MFMA (1-3% faster).
           if constexpr (!B_KC) __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
           for (int mi = 0; mi < MF; ++mi)
@@ -913,10 +925,20 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
             for (int ni = 0; ni < NF; ++ni)
               acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
           if constexpr (B_KC) {
+            if (ks == 1) {  // also the staging stores and loads
 #pragma unroll
-            for (int i = 0; i < MF * NF; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+              for (int i = 0; i < MF * NF; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one buffer load
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+              }
+            } else {
+#pragma unroll
+              for (int i = 0; i < MF * NF; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+              }
             }
           }
         }
