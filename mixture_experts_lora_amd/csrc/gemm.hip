@@ -916,8 +916,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
           // contiguous weights (the backward GEMMs, twice the LDS reads per
           // fragment) take the compiler's MFMA/LDS interleaving strategy
           // (1-3% faster there); k-contiguous ones (the forward GEMMs) place
-          // one LDS read, and in the staging k-step also one LDS write and
-          // one buffer load, after each MFMA (1-3% faster).
+          // one LDS read after each MFMA, and in the staging k-step the stores
+          // and loads early, two of each after each of the first MFMAs (gate_up
+          // forward 2-4%, down forward 4-7% faster than the compiler's order).
           if constexpr (!B_KC) __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
           for (int mi = 0; mi < MF; ++mi)
@@ -925,13 +926,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
             for (int ni = 0; ni < NF; ++ni)
               acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
           if constexpr (B_KC) {
-            if (ks == 1) {  // also the staging stores and loads
+            if (ks == 1) {  // the staging stores and loads early in the k-step
 #pragma unroll
-              for (int i = 0; i < MF * NF; ++i) {
+              for (int i = 0; i < MF * NF / 2; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one buffer load
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // two LDS writes
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // two buffer loads
+              }
+#pragma unroll
+              for (int i = 0; i < MF * NF / 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
               }
             } else {
 #pragma unroll
