@@ -776,33 +776,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
         }
       }
     };
-    // Branch-free issue (BF). With two register buffers the compiler's waits
-    // for a tile's loads must count the next tile's loads as still in
-    // flight, and its in-order load counter is exact only if every path
-    // issues the same loads; for the forward GEMMs a k-step without branches
-    // also lets the staging stores and loads interleave with its MFMAs
-    // (measured faster there, slower for the backward GEMMs). So: the plans
-    // switch to the LoRA segment's once, before its first tile is loaded
-    // (tiles are loaded in order), and live = false issues the loads with
-    // every lane out of range (they return zeros and touch no memory)
+    // Branch-free issue. A k-step without branches lets the staging stores
+    // and loads interleave with its MFMAs, and with two register buffers the
+    // compiler's waits for a tile's loads count the next tile's loads as
+    // still in flight only if every path issues the same loads (its
+    // in-order load counter is otherwise merged conservatively). So: the
+    // plans switch to the LoRA segment's once, before its first tile is
+    // loaded (tiles are loaded in order), and live = false issues the loads
+    // with every lane out of range (they return zeros and touch no memory)
     // instead of skipping them.
-    constexpr bool BF = NRB >= 2 || B_KC;
     auto switch_plans = [&]() __attribute__((always_inline)) {
       pa0 = pa1;
       pb0 = pb1;
     };
     auto load_tile = [&](int j, u32x4* a, u32x4* b, bool live = true) __attribute__((always_inline)) {
-      if constexpr (BF) {
-        const int k0 = (j >= nk0 ? j - nk0 : j) * BK;
-        vload(pa0, k0, a, GeoK<GA, A_KC>(), live);
-        vload(pb0, k0, b, GeoK<GB, B_KC>(), live);
-      } else if (j < nk0) {
-        vload(pa0, j * BK, a, GeoK<GA, A_KC>(), true);
-        vload(pb0, j * BK, b, GeoK<GB, B_KC>(), true);
-      } else {
-        vload(pa1, (j - nk0) * BK, a, GeoK<GA, A_KC>(), true);
-        vload(pb1, (j - nk0) * BK, b, GeoK<GB, B_KC>(), true);
-      }
+      const int k0 = (j >= nk0 ? j - nk0 : j) * BK;
+      vload(pa0, k0, a, GeoK<GA, A_KC>(), live);
+      vload(pb0, k0, b, GeoK<GB, B_KC>(), live);
     };
     auto store_tile = [&](int j, const u32x4* a, const u32x4* b) __attribute__((always_inline)) {
       char* sa = smem + (j % NST) * ST;
@@ -822,12 +812,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
     };
     bf16x8 af[NRB >= 2 ? 1 : 2][MF], bf[NRB >= 2 ? 1 : 2][NF];
     if (nk > 0) {
-      if (BF && nk0 == 0) switch_plans();
+      if (nk0 == 0) switch_plans();
       load_tile(0, ra[0], rb[0]);
       store_tile(0, ra[0], rb[0]);
 #pragma unroll
       for (int q = 1; q <= NRB; ++q) {
-        if (BF && q == nk0) switch_plans();
+        if (q == nk0) switch_plans();
         if (q < nk) load_tile(q, ra[q % NRB], rb[q % NRB]);
       }
       __syncthreads();
@@ -872,7 +862,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
       const char* sa = smem + (it % NST) * ST;
       const char* sb = sa + A_BYTES;
       // the tile loaded in this k tile is it+1+NRB
-      if (BF && it + 1 + NRB == nk0) switch_plans();
+      if (it + 1 + NRB == nk0) switch_plans();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int cur = FSB ? 0 : ks & 1;
@@ -899,33 +889,25 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
             bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(na + A_BYTES, FB, ni, fb_base[ni], 0);
         }
         // tile it+1's slot was last read in tile it-1, before the last barrier
-        if constexpr (BF) {
-          if (ks == 1) {
-            // past the last tile this stores the zeros of an out-of-range
-            // load into a slot nobody reads again
-            store_tile(it + 1, ra[BUF], rb[BUF]);
-            const int jn = it + 1 + NRB;
-            load_tile(min(jn, nk - 1), ra[BUF], rb[BUF], jn < nk);
-          }
-        } else if (ks == 1 && it + 1 < nk) {
+        if (ks == 1) {
+          // past the last tile this stores the zeros of an out-of-range
+          // load into a slot nobody reads again
           store_tile(it + 1, ra[BUF], rb[BUF]);
-          if (it + 1 + NRB < nk) load_tile(it + 1 + NRB, ra[BUF], rb[BUF]);
+          const int jn = it + 1 + NRB;
+          load_tile(min(jn, nk - 1), ra[BUF], rb[BUF], jn < nk);
         }
         if constexpr (MFMA) {
-          // Instruction order within the k-step, by measurement: output-
-          // contiguous weights (the backward GEMMs, twice the LDS reads per
-          // fragment) take the compiler's MFMA/LDS interleaving strategy
-          // (1-3% faster there); k-contiguous ones (the forward GEMMs) place
-          // one LDS read after each MFMA, and in the staging k-step the stores
-          // and loads early, two of each after each of the first MFMAs (gate_up
-          // forward 2-4%, down forward 4-7% faster than the compiler's order).
-          if constexpr (!B_KC) __builtin_amdgcn_iglp_opt(0);
+          // Instruction order within the k-step, by measurement: one LDS read
+          // after each MFMA, and in the staging k-step the stores and loads
+          // early, two of each after each of the first four MFMAs (2-7% faster
+          // per GEMM than the compiler's own order or its MFMA/LDS
+          // interleaving strategy).
 #pragma unroll
           for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
             for (int ni = 0; ni < NF; ++ni)
               acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
-          if constexpr (B_KC) {
+          {
             if (ks == 1) {  // the staging stores and loads early in the k-step
 #pragma unroll
               for (int i = 0; i < MF * NF / 2; ++i) {
