@@ -364,9 +364,26 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, kernel timer live (HIP events on the launch stream)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # Per-kernel times, in a pass of their own: every launch bracketed by HIP
+    # events on its stream (about 50 event records per step, which would add
+    # ~2% to a timed step).
+    kpass = max(1, min(args.steps, 10))
     with mel.kernel_timer() as kt:
+        for _ in range(kpass):
+            step()
+        torch.cuda.synchronize()
+    kms = {}
+    for name in mel._lib.KERNEL_IDS:
+        tot, n = kt.read(name)
+        if n:
+            kms[name] = {"ms_per_step": round(tot / kpass, 4), "launches": round(n / kpass, 3),
+                         "ms_per_launch": round(tot / n, 4)}
+    dom = max((k for k in GEMM_KERNELS if k in kms), key=lambda k: kms[k]["ms_per_step"])
+
+    # timed region: K steps, the dominant kernel's launches timed live (HIP
+    # events on the launch stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    with mel.kernel_timer(only=[dom]) as kt:
         torch.cuda.synchronize()
         ev[0].record()
         for i in range(args.steps):
@@ -375,6 +392,7 @@ def main():
         torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
     step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    dom_tot, dom_n = kt.read(dom)
 
     # forward-only and backward-only, after the timed region
     def timed(fn, n=5):
@@ -388,20 +406,14 @@ def main():
         return a.elapsed_time(b) / n
     fwd_ms = timed(fwd)
     bwd_ms = timed(bwd)
-    kms = {}
-    for name in mel._lib.KERNEL_IDS:
-        tot, n = kt.read(name)
-        if n:
-            kms[name] = {"ms_per_step": round(tot / args.steps, 4), "launches": n,
-                         "ms_per_launch": round(tot / n, 4)}
     peak_bytes = torch.cuda.max_memory_allocated()
 
     F = step_flops(cfg, args.full_ft, shared_I, args.block)
     tflops = F / (ms / 1e3) / 1e12
     half = cfg.dtype in ("bf16", "f16")      # dense bf16 and fp16 MFMA peaks are equal
     peak = PEAK_BF16_TFLOPS if half else PEAK_F32_TFLOPS
-    dom = max((k for k in GEMM_KERNELS if k in kms), key=lambda k: kms[k]["ms_per_step"])
-    # FLOPs of the dominant kernel per step over its summed launch time per step.
+    # FLOPs of the dominant kernel per step over its summed launch time per
+    # step, both from the timed region.
     # Every part (the routed layer, or each token chunk; in block mode also the
     # shared expert) launches each GEMM kernel equally often (twice for gate_up_fwd when the
     # backward recomputes h; base_wgrad's figure is the mean of its two launches).
@@ -411,14 +423,14 @@ def main():
         parts = [cfg.with_(T=hi - lo) for lo, hi in layer.bounds]
     else:
         parts = [cfg]
-    dom_launches = kms[dom]["launches"] / args.steps
+    dom_launches = dom_n / args.steps
     dom_flops_step = dom_launches / len(parts) * sum(kernel_flops(dom, c) for c in parts)
-    dom_tf = dom_flops_step / (kms[dom]["ms_per_step"] / 1e3) / 1e12
+    dom_tf = dom_flops_step / (dom_tot / args.steps / 1e3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(dom_tf / peak, 4),
                 "traffic": None if args.block else traffic_for(dom, cfg.name),
                 "flops_per_launch": int(dom_flops_step / dom_launches),
-                "ms_per_launch": kms[dom]["ms_per_launch"]}
+                "ms_per_launch": round(dom_tot / dom_n, 4)}
     hbm = {}
     for name, kv in kms.items():
         nb = kernel_bytes(name, cfg)

@@ -301,6 +301,10 @@ typedef enum {
   MOE_K_ACCUMULATE = 16, MOE_K_MERGE = 17, MOE_K_COUNT = 18
 } moe_kernel_id;
 moe_status moe_kernel_timer_enable(int32_t on);
+/* Time only the kernels whose bit (1u << id) is set in mask (all, by default):
+ * a timed region can bracket just the kernel it reports with events, while the
+ * other kernels are timed in a pass of their own. */
+moe_status moe_kernel_timer_select(uint32_t mask);
 moe_status moe_kernel_timer_reset(void);
 moe_status moe_kernel_timer_read(int32_t kernel_id, double *total_ms, int32_t *launches);
 

@@ -349,16 +349,24 @@ class kernel_timer:
     with kernel_timer() as kt:
         ...launches...
     torch.cuda.synchronize(); kt.read("gate_up_fwd") -> (total_ms, launches)
+
+    only: names of the kernels to time (default: all of them).
     """
+
+    def __init__(self, only=None):
+        self.mask = 0xFFFFFFFF if only is None else sum(1 << _lib.KERNEL_IDS[n] for n in only)
 
     def __enter__(self):
         lib = _lib.load()
         check(lib.moe_kernel_timer_reset(), "moe_kernel_timer_reset")
+        check(lib.moe_kernel_timer_select(self.mask), "moe_kernel_timer_select")
         check(lib.moe_kernel_timer_enable(1), "moe_kernel_timer_enable")
         return self
 
     def __exit__(self, *exc):
-        check(_lib.load().moe_kernel_timer_enable(0), "moe_kernel_timer_enable")
+        lib = _lib.load()
+        check(lib.moe_kernel_timer_enable(0), "moe_kernel_timer_enable")
+        check(lib.moe_kernel_timer_select(0xFFFFFFFF), "moe_kernel_timer_select")
         return False
 
     @staticmethod

@@ -24,7 +24,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
            "moe_merge_workspace_bytes", "moe_merge_lora",
            "moe_status_str",
            "moe_last_error",
-           "moe_kernel_timer_enable", "moe_kernel_timer_reset", "moe_kernel_timer_read")
+           "moe_kernel_timer_enable", "moe_kernel_timer_select", "moe_kernel_timer_reset",
+           "moe_kernel_timer_read")
 
 
 class MoeShape(ctypes.Structure):
@@ -108,6 +109,7 @@ def load() -> ctypes.CDLL:
         "moe_status_str": (ctypes.c_char_p, [st]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_kernel_timer_enable": (st, [I32]),
+        "moe_kernel_timer_select": (st, [ctypes.c_uint32]),
         "moe_kernel_timer_reset": (st, []),
         "moe_kernel_timer_read": (st, [I32, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int32)]),
@@ -115,7 +117,12 @@ def load() -> ctypes.CDLL:
     # every export gets an explicit signature (sizes are 64-bit size_t)
     assert set(sig) == set(EXPORTS), sorted(set(EXPORTS) ^ set(sig))
     for name, (res, args) in sig.items():
-        fn = getattr(lib, name)
+        try:
+            fn = getattr(lib, name)
+        except AttributeError:
+            # an older build of the library: refuse it (and let the build module import)
+            raise RuntimeError(f"{LIB_PATH} lacks {name}: it is out of date, rebuild it with "
+                               "`python -m mixture_experts_lora_amd.build`") from None
         fn.restype = res
         fn.argtypes = args
     _lib = lib

@@ -81,6 +81,7 @@ struct TimerRec {
 struct TimerState {
   std::mutex mu;
   bool on = false;
+  uint32_t mask = 0xffffffffu;  // kernel ids timed while on
   std::vector<TimerRec> recs;
   std::vector<hipEvent_t> pool;
   std::vector<int> open;  // index into recs of the pending start, per id
@@ -112,6 +113,7 @@ KernelTimer* active_timer() { return timer().on ? &g_timer_handle : nullptr; }
 void KernelTimer::record_start(int id, hipStream_t s) {
   TimerState& t = timer();
   std::lock_guard<std::mutex> lk(t.mu);
+  if (!((t.mask >> id) & 1u)) return;
   if (t.open.size() < MOE_K_COUNT) t.open.assign(MOE_K_COUNT, -1);
   hipEvent_t a = t.get(), b = t.get();
   if (!a || !b) return;
@@ -561,6 +563,13 @@ moe_status moe_kernel_timer_enable(int32_t on) {
   TimerState& t = timer();
   std::lock_guard<std::mutex> lk(t.mu);
   t.on = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_kernel_timer_select(uint32_t mask) {
+  TimerState& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.mask = mask;
   return MOE_OK;
 }
 
