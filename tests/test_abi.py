@@ -242,3 +242,14 @@ def test_python_binding_checks_shapes_on_host():
         mel.moe_route(torch.zeros(4, 8), 2, "topk_softmax", torch.zeros(4, 2, dtype=torch.int32),
                       torch.zeros(4, 2))          # CPU tensors are refused before any call
 
+
+
+def test_kernel_timer_selection(lib):
+    """The timer can be restricted to chosen kernels (host-side state only)."""
+    import mixture_experts_lora_amd as mel
+    from mixture_experts_lora_amd import _lib
+    assert mel.kernel_timer(only=["gate_up_fwd"]).mask == 1 << _lib.KERNEL_IDS["gate_up_fwd"]
+    assert mel.kernel_timer(only=["route", "merge"]).mask == (1 << 0) | (1 << 17)
+    assert mel.kernel_timer().mask == 0xFFFFFFFF
+    assert lib.moe_kernel_timer_select(0) == 0
+    assert lib.moe_kernel_timer_select(0xFFFFFFFF) == 0
