@@ -72,16 +72,19 @@ template <> struct Pack<float> {
   }
 };
 
-// One thread per (token, 16-byte column chunk).
-template <typename Elem>
+// One thread per (token, 16-byte column chunk); the chunk index is split
+// with 32-bit unsigned arithmetic when the chunk count fits (Idx), a 64-bit
+// division costing about ten times the instructions.
+template <typename Elem, typename Idx>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ yp,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ w, int T, int k,
-                                                      int64_t cpr, uint4* __restrict__ y) {
+                                                      Idx cpr, uint4* __restrict__ y) {
   constexpr int n = Pack<Elem>::n;
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t t = g / cpr, c = g - t * cpr;
-  if (t >= T) return;
+  const Idx g = static_cast<Idx>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const Idx tt = g / cpr, c = g - tt * cpr;
+  if (tt >= static_cast<Idx>(T)) return;
+  const int64_t t = static_cast<int64_t>(tt);
   float acc[n];
 #pragma unroll
   for (int i = 0; i < n; ++i) acc[i] = 0.f;
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
       for (int i = 0; i < n; ++i) acc[i] += wj[u] * v[i];
     }
   }
-  y[t * cpr + c] = Pack<Elem>::pack(acc);
+  y[t * static_cast<int64_t>(cpr) + c] = Pack<Elem>::pack(acc);
 }
 
 // One block per token; threads stride over the row's 16-byte chunks. Each
@@ -184,18 +187,20 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos,
   const int64_t total = static_cast<int64_t>(T) * cpr;
   dim3 grid(static_cast<unsigned>((total + 255) / 256));
   TimedScope scope(tm, w ? MOE_K_COMBINE : MOE_K_UNPERMUTE, s);
+  auto go = [&](auto elem, auto idx) {
+    typedef decltype(elem) Elem;
+    typedef decltype(idx) Idx;
+    hipLaunchKernelGGL((combine_kernel<Elem, Idx>), grid, dim3(256), 0, s,
+                       static_cast<const uint4*>(y_perm), inv_pos, w, T, k,
+                       static_cast<Idx>(cpr), static_cast<uint4*>(y));
+  };
+  const bool small = total + 255 <= 0xffffffffLL;
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint4*>(y_perm), inv_pos, w, T, k, cpr,
-                       static_cast<uint4*>(y));
+    small ? go(bf16_t(), uint32_t()) : go(bf16_t(), uint64_t());
   else if (dtype == MOE_F16)
-    hipLaunchKernelGGL(combine_kernel<f16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint4*>(y_perm), inv_pos, w, T, k, cpr,
-                       static_cast<uint4*>(y));
+    small ? go(f16_t(), uint32_t()) : go(f16_t(), uint64_t());
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const uint4*>(y_perm), inv_pos, w, T, k, cpr,
-                       static_cast<uint4*>(y));
+    small ? go(float(), uint32_t()) : go(float(), uint64_t());
   return hipGetLastError();
 }
 

@@ -168,18 +168,22 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   }
 }
 
-// X_perm[pos] = x[sorted_pair[pos] / k]; one thread per 16-byte chunk.
+// X_perm[pos] = x[sorted_pair[pos] / k]; one thread per 16-byte chunk. The
+// chunk index is split into (row, chunk) with 32-bit unsigned arithmetic when
+// the chunk count fits (a 64-bit division costs about ten times as many
+// instructions, a large share of this kernel's issue).
+template <typename Idx>
 __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x,
                                                      const int32_t* __restrict__ sorted_pair,
                                                      const int32_t* __restrict__ offsets, int E,
-                                                     int k, int64_t chunks_per_row,
+                                                     int k, Idx chunks_per_row,
                                                      uint4* __restrict__ xp) {
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t rows = offsets[E];
-  const int64_t pos = g / chunks_per_row, c = g - pos * chunks_per_row;
+  const Idx g = static_cast<Idx>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const Idx rows = static_cast<Idx>(offsets[E]);
+  const Idx pos = g / chunks_per_row, c = g - pos * chunks_per_row;
   if (pos >= rows) return;
-  const int64_t t = sorted_pair[pos] / k;
-  xp[pos * chunks_per_row + c] = x[t * chunks_per_row + c];
+  const Idx t = static_cast<Idx>(sorted_pair[pos]) / static_cast<Idx>(k);
+  xp[static_cast<int64_t>(pos) * chunks_per_row + c] = x[static_cast<int64_t>(t) * chunks_per_row + c];
 }
 
 }  // namespace
@@ -208,10 +212,16 @@ hipError_t launch_gather(const void* x, const int32_t* sorted_pair, const int32_
                          hipStream_t s, KernelTimer* tm) {
   const int64_t cpr = row_bytes / 16;
   const int64_t total = N * cpr;
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
   TimedScope scope(tm, MOE_K_GATHER, s);
-  hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256),
-                     0, s, static_cast<const uint4*>(x), sorted_pair, offsets, E, k, cpr,
-                     static_cast<uint4*>(x_perm));
+  if (total + 255 <= 0xffffffffLL)
+    hipLaunchKernelGGL(gather_kernel<uint32_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint4*>(x), sorted_pair, offsets, E, k,
+                       static_cast<uint32_t>(cpr), static_cast<uint4*>(x_perm));
+  else
+    hipLaunchKernelGGL(gather_kernel<uint64_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint4*>(x), sorted_pair, offsets, E, k,
+                       static_cast<uint64_t>(cpr), static_cast<uint4*>(x_perm));
   return hipGetLastError();
 }
 
