@@ -91,12 +91,19 @@ def step_flops(cfg, full_ft, shared_I=None, block=False):
     return F
 
 
+# The sources the counted GEMM kernels are built from (their template, the
+# headers it includes, and the build flags); a change to any of them makes
+# the recorded traffic stale.
+TRAFFIC_SOURCES = ("mixture_experts_lora_amd/csrc/gemm.hip",
+                   "mixture_experts_lora_amd/csrc/device_common.h",
+                   "mixture_experts_lora_amd/csrc/launch.h",
+                   "mixture_experts_lora_amd/build.py")
+
+
 def source_hash():
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "mixture_experts_lora_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
 
