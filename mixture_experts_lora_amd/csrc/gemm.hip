@@ -835,9 +835,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
     // and the other wave of the SIMD covers that LDS latency. This frees the
     // registers of the second buffer.
     constexpr bool FSB = NRB >= 2;
-    auto next_frags = [&](int it, int ks, int dst) __attribute__((always_inline)) {
+    auto next_frags = [&](int it, int ks, int dst, int ns) __attribute__((always_inline)) {
       const char* sa = smem + (it % NST) * ST;
-      if (ks + 1 < KS) {
+      if (ks + 1 < ns) {
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi)
           af[dst][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
@@ -856,25 +856,40 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
           bf[dst][ni] = read_frag<BN, BK, B_KC, NF>(na + A_BYTES, FB, ni, fb_base[ni], 0);
       }
     };
-    auto ktile = [&](int it, auto bufc, auto mfmac) __attribute__((always_inline)) {
+    // k-steps of the last tile holding valid k (the rest of it is zeros)
+    const int klast = MODE == GROUP_M ? (nk1 > 0 ? p.K[1] - (nk1 - 1) * BK : p.K[0] - (nk0 - 1) * BK)
+                                      : krows - (nk0 - 1) * BK;
+    const int ns_last = (klast + 15) / 16;
+    // NS k-steps of the tile are multiplied; LAST: the last tile, which
+    // stages and loads nothing and leaves its k-step loop after the k-steps
+    // that hold valid k (a LoRA segment of rank 16 fills one of a 64-wide
+    // tile's four; the rest is zeros). One path with early exits, so the
+    // accumulators stay in place.
+    auto ktile = [&](int it, auto bufc, auto mfmac, auto nsc, auto lastc) __attribute__((always_inline)) {
       constexpr int BUF = decltype(bufc)::value;
       constexpr bool MFMA = decltype(mfmac)::value;
+      constexpr int NS = decltype(nsc)::value;
+      constexpr bool LAST = decltype(lastc)::value;
+      static_assert(NS >= 1 && NS <= KS && (LAST || NS == KS), "k-steps of a tile");
       const char* sa = smem + (it % NST) * ST;
       const char* sb = sa + A_BYTES;
       // the tile loaded in this k tile is it+1+NRB
       if (it + 1 + NRB == nk0) switch_plans();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 0; ks < NS; ++ks) {
+        if constexpr (LAST) {
+          if (ks >= ns_last) break;
+        }
         const int cur = FSB ? 0 : ks & 1;
         if constexpr (FSB) {
-        } else if (ks + 1 < KS) {
+        } else if (ks + 1 < NS) {
 #pragma unroll
           for (int mi = 0; mi < MF; ++mi)
             af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
 #pragma unroll
           for (int ni = 0; ni < NF; ++ni)
             bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], ks + 1);
-        } else if (it + 1 < nk) {
+        } else if (!LAST && it + 1 < nk) {
           // Before the last k-step's MFMAs: every wave has read all of tile
           // it (its slot may be refilled next) and has written tile it+1, so
           // one barrier covers both, and the first fragment reads of tile
@@ -889,7 +904,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
             bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(na + A_BYTES, FB, ni, fb_base[ni], 0);
         }
         // tile it+1's slot was last read in tile it-1, before the last barrier
-        if (ks == 1) {
+        if (!LAST && ks == 1) {
           // past the last tile this stores the zeros of an out-of-range
           // load into a slot nobody reads again
           store_tile(it + 1, ra[BUF], rb[BUF]);
@@ -908,7 +923,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
             for (int ni = 0; ni < NF; ++ni)
               acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
           {
-            if (ks == 1) {  // the staging stores and loads early in the k-step
+            if (!LAST && ks == 1) {  // the staging stores and loads early in the k-step
 #pragma unroll
               for (int i = 0; i < MF * NF / 2; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -929,23 +944,31 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
             }
           }
         }
-        if constexpr (FSB) next_frags(it, ks, 0);
+        if constexpr (FSB) next_frags(it, ks, 0, NS);
       }
     };
     // The wave-uniform choice is made once, outside the k loop, so the loop
     // itself has no extra branch.
     auto kloop = [&](auto mfmac) __attribute__((always_inline)) {
+      using Full = std::integral_constant<int, KS>;
+      using No = std::false_type;
+      const int nkf = nk - 1;  // full tiles before the last
       if constexpr (NRB >= 2) {
         // pairs of tiles, so that the buffer index is compile-time; the odd
-        // last tile is peeled rather than branched around inside the loop
+        // tile is peeled rather than branched around inside the loop
         int it = 0;
-        for (; it + 1 < nk; it += 2) {
-          ktile(it, std::integral_constant<int, 1>(), mfmac);
-          ktile(it + 1, std::integral_constant<int, 0>(), mfmac);
+        for (; it + 1 < nkf; it += 2) {
+          ktile(it, std::integral_constant<int, 1>(), mfmac, Full(), No());
+          ktile(it + 1, std::integral_constant<int, 0>(), mfmac, Full(), No());
         }
-        if (it < nk) ktile(it, std::integral_constant<int, 1>(), mfmac);
+        if (it < nkf) ktile(it, std::integral_constant<int, 1>(), mfmac, Full(), No());
       } else {
-        for (int it = 0; it < nk; ++it) ktile(it, std::integral_constant<int, 0>(), mfmac);
+        for (int it = 0; it < nkf; ++it) ktile(it, std::integral_constant<int, 0>(), mfmac, Full(), No());
+      }
+      if (nk > 0) {
+        using Yes = std::true_type;
+        using B0 = std::integral_constant<int, 0>;
+        ktile(nkf, B0(), mfmac, Full(), Yes());
       }
     };
     if (MODE != GROUP_M || wm * WM < rows) kloop(std::true_type());
