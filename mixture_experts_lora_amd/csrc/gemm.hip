@@ -811,14 +811,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
       }
     };
     bf16x8 af[NRB >= 2 ? 1 : 2][MF], bf[NRB >= 2 ? 1 : 2][NF];
+    // With one register buffer, tile 1 is loaded into a buffer of its own
+    // together with tile 0 (the accumulators hold nothing yet, so their
+    // registers are free), and the first k tile stores it from there: a
+    // block waits for one load latency before its first MFMA, not two.
+    constexpr bool T1 = NRB == 1;
+    u32x4 ta[T1 ? GA::NIW : 1], tb[T1 ? GB::NIW : 1];
     if (nk > 0) {
       if (nk0 == 0) switch_plans();
       load_tile(0, ra[0], rb[0]);
-      store_tile(0, ra[0], rb[0]);
+      if constexpr (T1) {
+        if (1 == nk0) switch_plans();
+        load_tile(1, ta, tb, 1 < nk);
+        store_tile(0, ra[0], rb[0]);
+      } else {
+        store_tile(0, ra[0], rb[0]);
 #pragma unroll
-      for (int q = 1; q <= NRB; ++q) {
-        if (q == nk0) switch_plans();
-        if (q < nk) load_tile(q, ra[q % NRB], rb[q % NRB]);
+        for (int q = 1; q <= NRB; ++q) {
+          if (q == nk0) switch_plans();
+          if (q < nk) load_tile(q, ra[q % NRB], rb[q % NRB]);
+        }
       }
       __syncthreads();
 #pragma unroll
@@ -865,7 +877,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
     // that hold valid k (a LoRA segment of rank 16 fills one of a 64-wide
     // tile's four; the rest is zeros). One path with early exits, so the
     // accumulators stay in place.
-    auto ktile = [&](int it, auto bufc, auto mfmac, auto nsc, auto lastc) __attribute__((always_inline)) {
+    auto ktile = [&](int it, auto bufc, auto mfmac, auto nsc, auto lastc,
+                     auto firstc) __attribute__((always_inline)) {
+      constexpr bool FIRST = decltype(firstc)::value;
+      static_assert(!FIRST || T1, "the first tile's own buffer exists with one register buffer");
       constexpr int BUF = decltype(bufc)::value;
       constexpr bool MFMA = decltype(mfmac)::value;
       constexpr int NS = decltype(nsc)::value;
@@ -907,7 +922,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
         if (!LAST && ks == 1) {
           // past the last tile this stores the zeros of an out-of-range
           // load into a slot nobody reads again
-          store_tile(it + 1, ra[BUF], rb[BUF]);
+          if constexpr (FIRST) store_tile(it + 1, ta, tb);
+          else store_tile(it + 1, ra[BUF], rb[BUF]);
           const int jn = it + 1 + NRB;
           load_tile(min(jn, nk - 1), ra[BUF], rb[BUF], jn < nk);
         }
@@ -958,17 +974,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
         // tile is peeled rather than branched around inside the loop
         int it = 0;
         for (; it + 1 < nkf; it += 2) {
-          ktile(it, std::integral_constant<int, 1>(), mfmac, Full(), No());
-          ktile(it + 1, std::integral_constant<int, 0>(), mfmac, Full(), No());
+          ktile(it, std::integral_constant<int, 1>(), mfmac, Full(), No(), No());
+          ktile(it + 1, std::integral_constant<int, 0>(), mfmac, Full(), No(), No());
         }
-        if (it < nkf) ktile(it, std::integral_constant<int, 1>(), mfmac, Full(), No());
+        if (it < nkf) ktile(it, std::integral_constant<int, 1>(), mfmac, Full(), No(), No());
       } else {
-        for (int it = 0; it < nkf; ++it) ktile(it, std::integral_constant<int, 0>(), mfmac, Full(), No());
+        using B0 = std::integral_constant<int, 0>;
+        if (nkf > 0) ktile(0, B0(), mfmac, Full(), No(), std::true_type());
+        for (int it = 1; it < nkf; ++it) ktile(it, B0(), mfmac, Full(), No(), No());
       }
       if (nk > 0) {
         using Yes = std::true_type;
         using B0 = std::integral_constant<int, 0>;
-        ktile(nkf, B0(), mfmac, Full(), Yes());
+        ktile(nkf, B0(), mfmac, Full(), Yes(), No());
       }
     };
     if (MODE != GROUP_M || wm * WM < rows) kloop(std::true_type());
