@@ -562,7 +562,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
   // wave index as a wave-uniform (scalar) value, so that everything derived
   // from it (DMA destinations, resources) stays in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  // The second and later rows of waves are rotated along N: when only the
+  // first column of waves holds valid columns (a narrow last N tile), its
+  // waves sit on different SIMDs (wave w runs on SIMD w % 4).
+  const int wm = wave / WAVES_N, wn = (wave % WAVES_N + wm) % WAVES_N;
 
   int e, n_tile, rows, m0 = 0, krows = 0;
   int64_t row0;
@@ -847,9 +850,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
     // and the other wave of the SIMD covers that LDS latency. This frees the
     // registers of the second buffer.
     constexpr bool FSB = NRB >= 2;
-    auto next_frags = [&](int it, int ks, int dst, int ns) __attribute__((always_inline)) {
+    auto next_frags = [&](int it, int ks, int dst, int ns, auto mfmac) __attribute__((always_inline)) {
+      constexpr bool RD = decltype(mfmac)::value;  // only waves that multiply read fragments
       const char* sa = smem + (it % NST) * ST;
-      if (ks + 1 < ns) {
+      if (!RD) {
+        if (ks + 1 >= ns && it + 1 < nk) barrier_lds();
+      } else if (ks + 1 < ns) {
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi)
           af[dst][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
@@ -898,25 +904,29 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
         const int cur = FSB ? 0 : ks & 1;
         if constexpr (FSB) {
         } else if (ks + 1 < NS) {
+          if constexpr (MFMA) {
 #pragma unroll
-          for (int mi = 0; mi < MF; ++mi)
-            af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
+            for (int mi = 0; mi < MF; ++mi)
+              af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
 #pragma unroll
-          for (int ni = 0; ni < NF; ++ni)
-            bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], ks + 1);
+            for (int ni = 0; ni < NF; ++ni)
+              bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], ks + 1);
+          }
         } else if (!LAST && it + 1 < nk) {
           // Before the last k-step's MFMAs: every wave has read all of tile
           // it (its slot may be refilled next) and has written tile it+1, so
           // one barrier covers both, and the first fragment reads of tile
           // it+1 overlap this k-step's MFMAs.
           barrier_lds();
-          const char* na = smem + ((it + 1) % NST) * ST;
+          if constexpr (MFMA) {
+            const char* na = smem + ((it + 1) % NST) * ST;
 #pragma unroll
-          for (int mi = 0; mi < MF; ++mi)
-            af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(na, FA, mi, fa_base[mi], 0);
+            for (int mi = 0; mi < MF; ++mi)
+              af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(na, FA, mi, fa_base[mi], 0);
 #pragma unroll
-          for (int ni = 0; ni < NF; ++ni)
-            bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(na + A_BYTES, FB, ni, fb_base[ni], 0);
+            for (int ni = 0; ni < NF; ++ni)
+              bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(na + A_BYTES, FB, ni, fb_base[ni], 0);
+          }
         }
         // tile it+1's slot was last read in tile it-1, before the last barrier
         if (!LAST && ks == 1) {
@@ -960,7 +970,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
             }
           }
         }
-        if constexpr (FSB) next_frags(it, ks, 0, NS);
+        if constexpr (FSB) next_frags(it, ks, 0, NS, mfmac);
       }
     };
     // The wave-uniform choice is made once, outside the k loop, so the loop
@@ -989,7 +999,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
         ktile(nkf, B0(), mfmac, Full(), Yes(), No());
       }
     };
-    if (MODE != GROUP_M || wm * WM < rows) kloop(std::true_type());
+    // Waves whose rows all lie past the tile's valid rows, or whose columns
+    // all lie past the valid columns, neither read fragments nor multiply.
+    const bool live = MODE != GROUP_M ||
+                      (wm * WM < rows && (PAIRED ? n_tile * (BN / 2) + wn * (WN / 2) < p.I
+                                                 : n0 + wn * WN < p.N));
+    if (live) kloop(std::true_type());
     else kloop(std::false_type());
   } else {
   #pragma unroll
