@@ -123,7 +123,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 // row loads are in flight together; the block reduces all slots at the end in
 // the same order as slot by slot (per-thread chunk order, wave tree, waves in
 // order), which leaves dw bit-identical.
-template <typename Elem, int KMAX>
+// NT: G is written with non-temporal stores (a G larger than the 256 MB
+// Infinity Cache; a smaller one stays cached for the kernels that read it next).
+template <typename Elem, int KMAX, bool NT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dy,
                                                           const uint4* __restrict__ yexp,
                                                           const int32_t* __restrict__ inv_pos,
@@ -160,7 +162,15 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
         part[j] += d[i] * y[i];
         o[i] = wj[j] * d[i];
       }
-      g[static_cast<int64_t>(pos[j]) * cpr + c] = Pack<Elem>::pack(o);
+      const uint4 q = Pack<Elem>::pack(o);
+      if constexpr (NT) {
+        typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+        v4u v;
+        __builtin_memcpy(&v, &q, sizeof(v));
+        __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(g) + static_cast<int64_t>(pos[j]) * cpr + c);
+      } else {
+        g[static_cast<int64_t>(pos[j]) * cpr + c] = q;
+      }
     }
   }
 #pragma unroll
@@ -210,11 +220,18 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_exp,
   const int esz = dtype == MOE_F32 ? 4 : 2;
   const int64_t cpr = static_cast<int64_t>(H) * esz / 16;
   TimedScope scope(tm, MOE_K_COMBINE_BWD, s);
+  const bool nt = static_cast<int64_t>(T) * k * H * esz > (int64_t{256} << 20);
   auto go = [&](auto tag, auto kmax) {
     using Elem = decltype(tag);
-    hipLaunchKernelGGL((combine_bwd_kernel<Elem, decltype(kmax)::value>), dim3(T), dim3(256), 0,
-                       s, static_cast<const uint4*>(dy), static_cast<const uint4*>(y_exp),
-                       inv_pos, w, k, cpr, static_cast<uint4*>(g), dw);
+    if (nt)
+      hipLaunchKernelGGL((combine_bwd_kernel<Elem, decltype(kmax)::value, true>), dim3(T), dim3(256),
+                         0, s, static_cast<const uint4*>(dy), static_cast<const uint4*>(y_exp),
+                         inv_pos, w, k, cpr, static_cast<uint4*>(g), dw);
+    else
+      hipLaunchKernelGGL((combine_bwd_kernel<Elem, decltype(kmax)::value, false>), dim3(T),
+                         dim3(256), 0, s, static_cast<const uint4*>(dy),
+                         static_cast<const uint4*>(y_exp), inv_pos, w, k, cpr,
+                         static_cast<uint4*>(g), dw);
   };
   auto by_k = [&](auto tag) {
     if (k <= 4) go(tag, std::integral_constant<int, 4>());
