@@ -46,7 +46,10 @@
  *  - Arguments are checked before anything is enqueued. Errors:
  *      MOE_ERR_INVALID_ARG   a NULL pointer that is not optional, T < 1,
  *                            k < 1, k > E, E < 1, E > 1024, H < 1, I < 1,
- *                            r < 1, N >= 2^31, unknown router or dtype
+ *                            r < 1, N >= 2^31, N * max(2I, H) bytes of
+ *                            `dtype` above 32 GiB (one activation tensor),
+ *                            2I * H bytes of `dtype` at or above 2 GiB (one
+ *                            expert's weight matrix), unknown router or dtype
  *      MOE_ERR_UNSUPPORTED   H or I not a multiple of 8, r > 64, k > 32
  *      MOE_ERR_WORKSPACE     workspace smaller than moe_workspace_bytes says
  *      MOE_ERR_HIP           a launch failed (moe_last_error() has the text)

@@ -52,9 +52,16 @@ moe_status check_shape(const moe_shape* s) {
   if (s->H % 8 != 0 || s->I % 8 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 8");
   if (s->r > 64) return fail(MOE_ERR_UNSUPPORTED, "r > 64 is not supported");
+  // Activation tensors up to 32 GiB each, so that their 16-byte chunk
+  // indices fit 32 bits in the element-wise kernels; one expert's weight
+  // matrix below 2 GiB, the reach of a 32-bit buffer offset in the GEMMs.
   const int64_t N = int64_t(s->T) * s->k;
-  if (N * (2 * int64_t(s->I)) >= (int64_t(1) << 40) || N * int64_t(s->H) >= (int64_t(1) << 40))
-    return fail(MOE_ERR_INVALID_ARG, "activation tensors too large");
+  const int64_t esz = s->dtype == MOE_F32 ? 4 : 2;
+  const int64_t wide = std::max(2 * int64_t(s->I), int64_t(s->H));
+  if (N * wide * esz > (int64_t(1) << 35))
+    return fail(MOE_ERR_INVALID_ARG, "activation tensors larger than 32 GiB");
+  if (2 * int64_t(s->I) * s->H * esz >= (int64_t(1) << 31))
+    return fail(MOE_ERR_INVALID_ARG, "one expert's weight matrix must be smaller than 2 GiB");
   return MOE_OK;
 }
 

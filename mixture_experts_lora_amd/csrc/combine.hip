@@ -73,13 +73,15 @@ template <> struct Pack<float> {
 };
 
 // One thread per (token, 16-byte column chunk); the chunk index is split
-// with 32-bit unsigned arithmetic when the chunk count fits (Idx), a 64-bit
-// division costing about ten times the instructions.
-template <typename Elem, typename Idx>
+// with 32-bit unsigned arithmetic (a 64-bit division costs about ten times
+// the instructions; the layer's shape limit keeps an activation tensor under
+// 32 GiB, so its chunk count fits).
+template <typename Elem>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ yp,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ w, int T, int k,
-                                                      Idx cpr, uint4* __restrict__ y) {
+                                                      uint32_t cpr, uint4* __restrict__ y) {
+  typedef uint32_t Idx;
   constexpr int n = Pack<Elem>::n;
   const Idx g = static_cast<Idx>(blockIdx.x) * blockDim.x + threadIdx.x;
   const Idx tt = g / cpr, c = g - tt * cpr;
@@ -197,20 +199,16 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos,
   const int64_t total = static_cast<int64_t>(T) * cpr;
   dim3 grid(static_cast<unsigned>((total + 255) / 256));
   TimedScope scope(tm, w ? MOE_K_COMBINE : MOE_K_UNPERMUTE, s);
-  auto go = [&](auto elem, auto idx) {
+  if (total + 255 > 0xffffffffLL) return hipErrorInvalidValue;  // excluded by the shape limit
+  auto go = [&](auto elem) {
     typedef decltype(elem) Elem;
-    typedef decltype(idx) Idx;
-    hipLaunchKernelGGL((combine_kernel<Elem, Idx>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((combine_kernel<Elem>), grid, dim3(256), 0, s,
                        static_cast<const uint4*>(y_perm), inv_pos, w, T, k,
-                       static_cast<Idx>(cpr), static_cast<uint4*>(y));
+                       static_cast<uint32_t>(cpr), static_cast<uint4*>(y));
   };
-  const bool small = total + 255 <= 0xffffffffLL;
-  if (dtype == MOE_BF16)
-    small ? go(bf16_t(), uint32_t()) : go(bf16_t(), uint64_t());
-  else if (dtype == MOE_F16)
-    small ? go(f16_t(), uint32_t()) : go(f16_t(), uint64_t());
-  else
-    small ? go(float(), uint32_t()) : go(float(), uint64_t());
+  if (dtype == MOE_BF16) go(bf16_t());
+  else if (dtype == MOE_F16) go(f16_t());
+  else go(float());
   return hipGetLastError();
 }
 

@@ -295,6 +295,7 @@ struct Geo {
 template <int ROWS, int BK, bool KC, int NW>
 struct Plan {
   const void* base;
+  int64_t bytes;  // extent of the operand from base
   int nrec;
   u32x4 rs;  // buffer resource over [base, base + nrec)
   uint32_t vo[Geo<ROWS, BK, KC, NW>::NIW];
@@ -313,6 +314,7 @@ __device__ __forceinline__ void make_plan(Plan<ROWS, BK, KC, NW>& P, const View<
   P.klim = v.klim;
   P.ld = v.ld;
   P.base = v.base;
+  P.bytes = bytes;
   P.nrec = clamp_records(bytes);
   P.rs = buffer_rsrc(v.base, P.nrec);
 #pragma unroll
@@ -334,16 +336,33 @@ __device__ __forceinline__ void make_plan(Plan<ROWS, BK, KC, NW>& P, const View<
   }
 }
 
+// Buffer resource and scalar offset of the tile at k0. A k-contiguous
+// operand keeps one resource (k0 is a small byte offset). An output-contiguous
+// one advances along its rows: its resource starts at row k0 (64-bit address
+// arithmetic) and covers the rest of the operand, so neither the 32-bit scalar
+// offset nor the 2^31-byte record count limits how many rows it spans (a
+// weight gradient runs over all of an expert's rows).
+template <int ROWS, int BK, bool KC, int NW>
+__device__ __forceinline__ u32x4 tile_rsrc(const Plan<ROWS, BK, KC, NW>& P, int k0,
+                                           uint32_t& soff) {
+  if (KC) {
+    soff = static_cast<uint32_t>(k0) * 2;
+    return P.rs;
+  }
+  soff = 0;
+  const int64_t adv = static_cast<int64_t>(k0) * P.ld * 2;
+  return buffer_rsrc(static_cast<const char*>(P.base) + adv, clamp_records(P.bytes - adv));
+}
+
 // Issue one tile: DMA when possible, else an element-wise fill.
 template <int ROWS, int BK, bool KC, int NW>
 __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC, NW>& P, int k0, char* lds, int wave,
                                      int lane) {
   typedef Geo<ROWS, BK, KC, NW> G;
   if (P.vec) {
-    const uint32_t soff = KC ? static_cast<uint32_t>(k0) * 2
-                             : static_cast<uint32_t>(static_cast<int64_t>(k0) * P.ld * 2);
+    uint32_t soff;
+    const u32x4 rs = tile_rsrc(P, k0, soff);
     const bool tail = KC && (k0 + BK > P.klim);  // n-contiguous tails hit the buffer bound
-    const u32x4 rs = P.rs;
 #pragma unroll
     for (int i = 0; i < G::NIW; ++i) {
       const int j = wave + NW * i;
@@ -383,15 +402,15 @@ __device__ __forceinline__ void fill_one(const Plan<ROWS, BK, KC, NW>& P, int k0
   typedef Geo<ROWS, BK, KC, NW> G;
   const int j = wave + NW * i;
   if (G::TI % NW != 0 && j >= G::TI) return;
-  const uint32_t soff = KC ? static_cast<uint32_t>(k0) * 2
-                           : static_cast<uint32_t>(static_cast<int64_t>(k0) * P.ld * 2);
+  uint32_t soff;
+  const u32x4 rs = tile_rsrc(P, k0, soff);
   uint32_t vo = P.vo[i];
   if (KC && k0 + BK > P.klim) {  // k tail of a k-contiguous operand: mask by lane
     const int r = G::RPI * j + lane / G::CPR;
     const int c = (lane % G::CPR) ^ kswz<BK>(r);
     if (k0 + c * 8 >= P.klim) vo = kOOB;
   }
-  dma16(lds + j * 1024, P.rs, vo, soff);
+  dma16(lds + j * 1024, rs, vo, soff);
 }
 
 // A fill geometry tagged with its operand's k-contiguity (for generic lambdas).
@@ -1450,13 +1469,12 @@ struct WsLayout {
   size_t bytes;
 };
 
-int big_variant();
 inline int small_rows(int dtype) { return dtype != MOE_F32 ? 128 : 64; }
-// 256-row tiles for the register-staged variants, whose LoRA segment (K = r)
+// 256-row tiles for the register-staged kernel, whose LoRA segment (K = r)
 // must come in 16-byte pieces.
 inline int big_rows(const ExpertDims& d) {
   if (d.dtype == MOE_F32) return 64;
-  return big_variant() >= 4 && d.r % 8 == 0 ? 256 : 128;
+  return d.r % 8 == 0 ? 256 : 128;
 }
 
 WsLayout tile_ws(void* ws, const ExpertDims& d) {
@@ -1496,60 +1514,28 @@ hipError_t launch(K kern, int grid, const GemmArgs& a, hipStream_t s, int thread
 #define GEMM16(dtype, ...) \
   ((dtype) == MOE_F16 ? gemm16<true, __VA_ARGS__> : gemm16<false, __VA_ARGS__>)
 
-// Tile variants of the four expert GEMMs, chosen by measurement on MI355X
-// (variant 5 is the default; MOE_LORA_GEMM_VARIANT overrides it for tuning
-// runs):
-//   0: 128 x 256, four waves, buffer->LDS DMA, BK 64, 3 LDS stages (144 KB), 1 block/CU
-//   1: 128 x 256, four waves, buffer->LDS DMA, BK 32, 3 LDS stages (72 KB), 2 blocks/CU
-//   2: 128 x 256, four waves, buffer->LDS DMA, BK 32, 4 LDS stages (96 KB), 1 block/CU
-//   3: 128 x 256, four waves, buffer->LDS DMA, BK 32, 6 LDS stages (144 KB), 1 block/CU
-//   4: 256 x 256, eight waves (64 x 128 each), BK 64, 2 LDS stages (128 KB),
-//      operands staged through VGPRs (one k tile in flight per wave)
-//   5: as 4 with eight waves of 128 x 64 each
-//   6: as 5 with two k tiles of loads in flight per wave (two register
-//      buffers, single-buffered MFMA fragments to make room): measured about
-//      1.5% faster on the gpt-oss-shaped forward GEMMs, even on Qwen3-shaped
-//      ones, and slower backward (the n-contiguous-weight kernels spill)
-// Measured: a wave issues buffer->LDS DMA at about a quarter of the rate it
-// issues buffer loads into VGPRs, so the register-staged kernels keep the
-// MFMAs fed with fewer bytes in flight; 256-row tiles also halve the L2
-// traffic per MFMA relative to 128 x 256.
-int big_variant() {
-  static int v = [] {
-    const char* e = getenv("MOE_LORA_GEMM_VARIANT");
-    return e ? atoi(e) : 5;
-  }();
-  return v;
-}
-
+// Tiles of the four expert GEMMs, chosen by measurement on MI355X:
+//  - 256 x 256, eight waves of 128 x 64, BK 64, two LDS slots (128 KB),
+//    operands staged through VGPRs (one k tile in flight per wave): the
+//    default. A wave issues buffer->LDS DMA at about a quarter of the rate it
+//    issues buffer loads into VGPRs, so register staging keeps the MFMAs fed
+//    with fewer bytes in flight; 256-row tiles also halve the L2 traffic per
+//    MFMA relative to 128 x 256.
+//  - 256 x 256 with buffer->LDS DMA fills (128 x 128 per wave, BK 32, three
+//    stages) when an operand cannot be read in 16-byte pieces (a pointer that
+//    is not 16-byte aligned): the DMA fill falls back to element-wise loads.
+//  - 128 x 256, four waves, buffer->LDS DMA, BK 32, three stages, two blocks
+//    per CU: ranks that are not a multiple of 8 (the LoRA segment, K = r,
+//    then takes element-wise fills).
 template <int MODE, int EPI, bool PAIRED, bool A_KC, bool B_KC>
 hipError_t launch_big(int grid, const GemmArgs& a, hipStream_t s, int bm) {
   if (bm == 256) {
-    // The register-staged kernels load every operand in 16-byte pieces; with
-    // an operand that cannot be (unaligned pointer or leading dimension) the
-    // 256-row tiles go to a buffer->LDS kernel with element-wise fills.
     const bool all_vec = a.a[0].vec && a.b[0].vec && (a.K[1] == 0 || (a.a[1].vec && a.b[1].vec));
     if (!all_vec)
       return launch(GEMM16(a.dtype, 256, 256, 128, 128, 32, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
-    switch (big_variant()) {
-      case 4:
-        return launch(GEMM16(a.dtype, 256, 256, 64, 128, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 1), grid, a, s, 512);
-      case 6:
-        return launch(GEMM16(a.dtype, 256, 256, 128, 64, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 2), grid, a, s, 512);
-      default:
-        return launch(GEMM16(a.dtype, 256, 256, 128, 64, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 1), grid, a, s, 512);
-    }
+    return launch(GEMM16(a.dtype, 256, 256, 128, 64, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 1), grid, a, s, 512);
   }
-  switch (big_variant()) {
-    case 0:
-      return launch(GEMM16(a.dtype, 128, 256, 64, 128, 64, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
-    case 2:
-      return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 4, 1, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
-    case 3:
-      return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 6, 1, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
-    default:
-      return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 3, 2, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
-  }
+  return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 3, 2, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
 }
 
 // M-tile grid bound for GROUP_M launches over a tile list (excess blocks exit at once).
@@ -1750,7 +1736,9 @@ __global__ __launch_bounds__(256) void side_sum_kernel(const float* __restrict__
   out[i] = from_f32<Elem>(acc * scale);
 }
 
-// split_ws: at least wgrad_split_bytes(d, P, Q) bytes (unused when that is 0).
+// split_ws: at least wgrad_split_bytes(d, P, Q) bytes (unused when that is 0),
+// or null: then the rows are never split (one workgroup per output tile runs
+// over all of an expert's rows), whatever wgrad_splits would choose.
 // side (optional, side_fusable only): also form V = scale D Bm.
 hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* Lm, int P,
                        const void* Rm, int Q, void* out, hipStream_t s, void* split_ws,
@@ -1773,7 +1761,7 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
   a.ld_out = Q;
   a.a[0] = opnd(Lm, 0, P, 0, P % 8 == 0);
   a.b[0] = opnd(Rm, 0, Q, 0, Q % 8 == 0);
-  const int S = wgrad_splits(d, P, Q);
+  const int S = split_ws ? wgrad_splits(d, P, Q) : 1;
   auto side_sum = [&]() -> hipError_t {
     if (!side) return hipSuccess;
     const int tiles = ceil_div(P, 256);

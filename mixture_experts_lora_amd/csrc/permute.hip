@@ -169,20 +169,22 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 }
 
 // X_perm[pos] = x[sorted_pair[pos] / k]; one thread per 16-byte chunk. The
-// chunk index is split into (row, chunk) with 32-bit unsigned arithmetic when
-// the chunk count fits (a 64-bit division costs about ten times as many
-// instructions, a large share of this kernel's issue).
+// chunk index is split into (row, chunk) with 32-bit unsigned arithmetic (a
+// 64-bit division costs about ten times as many instructions, a large share
+// of this kernel's issue; the layer's shape limit keeps X_perm under 32 GiB,
+// so its chunk count fits).
 // NT: non-temporal stores, for an X_perm larger than the 256 MB Infinity
 // Cache. One that fits is left in the cache for its next readers (the side
 // product and the gate_up GEMM); a larger one would only evict their operands
 // (Qwen3-shaped layer, 537 MB: side product -16%, layer step -1.6%; at
 // gpt-oss shape, 189 MB, the same stores slow the side product by 17%).
-template <typename Idx, bool NT>
+template <bool NT>
 __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x,
                                                      const int32_t* __restrict__ sorted_pair,
                                                      const int32_t* __restrict__ offsets, int E,
-                                                     int k, Idx chunks_per_row,
+                                                     int k, uint32_t chunks_per_row,
                                                      uint4* __restrict__ xp) {
+  typedef uint32_t Idx;
   const Idx g = static_cast<Idx>(blockIdx.x) * blockDim.x + threadIdx.x;
   const Idx rows = static_cast<Idx>(offsets[E]);
   const Idx pos = g / chunks_per_row, c = g - pos * chunks_per_row;
@@ -224,21 +226,15 @@ hipError_t launch_gather(const void* x, const int32_t* sorted_pair, const int32_
   const dim3 grid(static_cast<unsigned>((total + 255) / 256));
   TimedScope scope(tm, MOE_K_GATHER, s);
   const bool nt = N * row_bytes > (int64_t{256} << 20);
-  const bool narrow = total + 255 <= 0xffffffffLL;
+  if (total + 255 > 0xffffffffLL) return hipErrorInvalidValue;  // excluded by the shape limit
   const uint4* xs = static_cast<const uint4*>(x);
   uint4* xd = static_cast<uint4*>(x_perm);
-  if (narrow && !nt)
-    hipLaunchKernelGGL((gather_kernel<uint32_t, false>), grid, dim3(256), 0, s, xs, sorted_pair,
-                       offsets, E, k, static_cast<uint32_t>(cpr), xd);
-  else if (narrow)
-    hipLaunchKernelGGL((gather_kernel<uint32_t, true>), grid, dim3(256), 0, s, xs, sorted_pair,
-                       offsets, E, k, static_cast<uint32_t>(cpr), xd);
-  else if (!nt)
-    hipLaunchKernelGGL((gather_kernel<uint64_t, false>), grid, dim3(256), 0, s, xs, sorted_pair,
-                       offsets, E, k, static_cast<uint64_t>(cpr), xd);
+  if (!nt)
+    hipLaunchKernelGGL((gather_kernel<false>), grid, dim3(256), 0, s, xs, sorted_pair, offsets, E,
+                       k, static_cast<uint32_t>(cpr), xd);
   else
-    hipLaunchKernelGGL((gather_kernel<uint64_t, true>), grid, dim3(256), 0, s, xs, sorted_pair,
-                       offsets, E, k, static_cast<uint64_t>(cpr), xd);
+    hipLaunchKernelGGL((gather_kernel<true>), grid, dim3(256), 0, s, xs, sorted_pair, offsets, E,
+                       k, static_cast<uint32_t>(cpr), xd);
   return hipGetLastError();
 }
 

@@ -74,11 +74,29 @@ def test_workspace_never_holds_a_merged_delta(lib):
     (dict(T=0), 1), (dict(k=0), 1), (dict(k=9), 1), (dict(E=0), 1), (dict(E=2000, k=2), 1),
     (dict(H=100), 2), (dict(I=12), 2), (dict(r=65), 2), (dict(r=0), 1), (dict(dtype=7), 1),
     (dict(k=40, E=64), 2),
+    # one activation tensor above 32 GiB: N * 2I * 2 bytes = 2^25 * 2048 * 2 = 2^37
+    (dict(T=1 << 22, k=8, E=8, I=1024, H=1024), 1),
+    # one expert's weight matrix of 2 GiB (2I * H * 2 bytes = 2^31)
+    (dict(H=32768, I=16384), 1),
+    (dict(H=32768, I=16384, dtype=0), 1),
 ])
 def test_shape_validation(lib, kw, status):
     st, *_ = ws(lib, shape(**kw))
     assert st == status
     assert lib.moe_last_error()
+
+
+def test_shape_limits_at_the_edge(lib):
+    """The largest accepted sizes: a 32 GiB activation tensor and an expert
+    weight matrix just under 2 GiB."""
+    # N * 2I * 2 bytes = 2^22 * 2^12 * 2 = 2^35 exactly
+    st, *_ = ws(lib, shape(T=1 << 19, k=8, E=8, I=2048, H=1024))
+    assert st == 0
+    st, *_ = ws(lib, shape(T=1 << 19, k=8, E=8, I=2056, H=1024))
+    assert st == 1
+    # 2I * H * 2 bytes = 2^31 - 2^16
+    st, *_ = ws(lib, shape(T=8, H=32768 - 8, I=16384, k=2, E=8))
+    assert st == 0
 
 
 def test_null_pointers_rejected(lib):

@@ -61,7 +61,8 @@ def test_full_size_layer(name):
 
     nz = np.where(counts > 0)[0]
     experts = sorted({int(nz[np.argmax(counts[nz])]), int(nz[len(nz) // 2])})
-    wn = to_numpy(layer.topk_w)
+    # the experts' inputs come from the oracle's routing, never from the GPU's
+    wn = w
     for e in experts:
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         pairs = sp[lo:hi]
@@ -95,11 +96,14 @@ def test_full_size_full_fine_tuning(name):
     layer.step(inp["x"], inp["logits"], inp["dy"], {n: inp[n] for n in WEIGHTS})
     torch.cuda.synchronize()
     tol = TOL[cfg.dtype]
-    counts = to_numpy(layer.counts)
-    offsets = to_numpy(layer.offsets)
-    sp = to_numpy(layer.sorted_pair)
+    # routing and permutation from the oracle (and the GPU's checked against them)
+    ids, wn = oracle.route(to_numpy(inp["logits"]), cfg.k, cfg.router)
+    counts, offsets, sp, inv = oracle.permute(ids, cfg.E)
+    np.testing.assert_array_equal(to_numpy(layer.topk_ids), ids)
+    np.testing.assert_array_equal(to_numpy(layer.offsets), offsets)
+    np.testing.assert_array_equal(to_numpy(layer.sorted_pair), sp)
+    close("topk_w", to_numpy(layer.topk_w), wn, 1e-5)
     wts = {n: ExpertSlices(inp[n]) for n in WEIGHTS}
-    wn = to_numpy(layer.topk_w)
     nz = np.where(counts > 0)[0]
     for e in sorted({int(nz[0]), int(nz[-1])}):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
