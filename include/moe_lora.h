@@ -168,6 +168,24 @@ moe_status moe_permute(const moe_shape *shape, const int32_t *topk_ids, const vo
                        int32_t *inv_pos, void *x_perm, void *ws, size_t ws_bytes,
                        void *stream);
 
+/* moe_permute without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses
+ * that forbid hipMalloc). Same arguments, outputs and results as moe_permute;
+ * its per-chunk expert counts live in a library-owned device array of
+ * MOE_PERMUTE_NOALLOC_BYTES per GPU (its first call on a GPU looks up that
+ * GPU's copy; the array is held until the process ends). The GPU is the one
+ * current on the calling thread, and `stream` must belong to it.
+ *   Limit: E * ceil(T * k / 64) * 4 bytes <= MOE_PERMUTE_NOALLOC_BYTES, else
+ *   MOE_ERR_UNSUPPORTED (checked before anything is enqueued).
+ *   Calls on one GPU share the array: calls on one stream are ordered and
+ *   safe, calls that overlap in time on one GPU (different streams, or host
+ *   threads) race and give wrong results. Every call rewrites the part of the
+ *   array it uses before reading it. Allocates nothing.  */
+#define MOE_PERMUTE_NOALLOC_BYTES (4u << 20)
+moe_status moe_permute_noalloc(const moe_shape *shape, const int32_t *topk_ids, const void *x,
+                               int32_t *counts, int32_t *offsets, int32_t *sorted_pair,
+                               int32_t *inv_pos, void *x_perm, void *stream);
+
 /* Grouped expert forward with split LoRA and SwiGLU (faster-moe page, "Faster
  * LoRA MoE training" and "Implementation details"): fills every field of
  * `saved` for rows in permuted order. offsets is moe_permute's output.  */

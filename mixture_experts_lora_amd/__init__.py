@@ -26,6 +26,7 @@ from ._lib import MoeBaseGrads, MoeLoraGrads, MoeSaved, MoeShape, MoeWeights, RO
 
 __all__ = [
     "Shape", "moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
+    "moe_permute_noalloc",
     "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
     "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_workspace_bytes_lean",
     "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute", "moe_router_workspace_bytes",
@@ -147,6 +148,22 @@ def moe_permute(shape: Shape, topk_ids, x, counts, offsets, sorted_pair, inv_pos
         _ptr(inv_pos, (shape.N,), torch.int32, "inv_pos"),
         _ptr(x_perm, (shape.N, shape.H), dt, "x_perm", optional=True),
         wsp, wsb, _stream(stream)), "moe_permute")
+
+
+def moe_permute_noalloc(shape: Shape, topk_ids, x, counts, offsets, sorted_pair, inv_pos,
+                        x_perm, stream=None):
+    """moe_permute with its table in the library's own device array (no workspace)."""
+    dt = shape.torch_dtype
+    check(_lib.load().moe_permute_noalloc(
+        ctypes.byref(shape.c()),
+        _ptr(topk_ids, (shape.T, shape.k), torch.int32, "topk_ids"),
+        _ptr(x, (shape.T, shape.H), dt, "x", optional=x_perm is None),
+        _ptr(counts, (shape.E,), torch.int32, "counts"),
+        _ptr(offsets, (shape.E + 1,), torch.int32, "offsets"),
+        _ptr(sorted_pair, (shape.N,), torch.int32, "sorted_pair"),
+        _ptr(inv_pos, (shape.N,), torch.int32, "inv_pos"),
+        _ptr(x_perm, (shape.N, shape.H), dt, "x_perm", optional=True),
+        _stream(stream)), "moe_permute_noalloc")
 
 
 def _weights(shape: Shape, w: dict) -> MoeWeights:

@@ -21,7 +21,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
            "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_workspace_bytes_lean",
            "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute",
            "moe_router_workspace_bytes", "moe_router_fwd", "moe_router_bwd", "moe_accumulate",
-           "moe_merge_workspace_bytes", "moe_merge_lora",
+           "moe_merge_workspace_bytes", "moe_merge_lora", "moe_permute_noalloc",
            "moe_status_str",
            "moe_last_error",
            "moe_kernel_timer_enable", "moe_kernel_timer_select", "moe_kernel_timer_reset",
@@ -74,6 +74,7 @@ def load() -> ctypes.CDLL:
         "moe_route_bwd": (st, [P, P, P, I32, I32, I32, I32, P, P]),
         "moe_permute": (st, [ctypes.POINTER(MoeShape), P, P, P, P, P, P, P, P, ctypes.c_size_t,
                              P]),
+        "moe_permute_noalloc": (st, [ctypes.POINTER(MoeShape), P, P, P, P, P, P, P, P]),
         "moe_grouped_lora_fwd": (st, [ctypes.POINTER(MoeShape), P, P,
                                       ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeSaved), P,
                                       ctypes.c_size_t, P]),

@@ -236,6 +236,40 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, const vo
   return MOE_OK;
 }
 
+moe_status moe_permute_noalloc(const moe_shape* shape, const int32_t* topk_ids, const void* x,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                               int32_t* inv_pos, void* x_perm, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(topk_ids);
+  CHECK_PTR(counts);
+  CHECK_PTR(offsets);
+  CHECK_PTR(sorted_pair);
+  CHECK_PTR(inv_pos);
+  if (x_perm) CHECK_PTR(x);
+  if (x_perm && x_perm == x) return fail(MOE_ERR_INVALID_ARG, "x_perm aliases x");
+  const moe::ExpertDims d = dims_of(shape);
+  const size_t need = moe::permute_ws_bytes(d.N, d.E);
+  if (need > MOE_PERMUTE_NOALLOC_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_permute_noalloc: E * ceil(T*k/64) * 4 = " +
+                                         std::to_string(need) + " bytes exceeds its " +
+                                         std::to_string(MOE_PERMUTE_NOALLOC_BYTES) +
+                                         "-byte table; use moe_permute with a workspace");
+  int32_t* table = nullptr;
+  hipError_t e = moe::noalloc_permute_table(&table);
+  if (e != hipSuccess) return hip_fail(e, "moe_permute_noalloc(table lookup)");
+  hipStream_t s = as_stream(stream);
+  moe::KernelTimer* tm = moe::active_timer();
+  e = moe::launch_permute(topk_ids, d.N, d.E, counts, offsets, sorted_pair, inv_pos, table, s, tm);
+  if (e != hipSuccess) return hip_fail(e, "moe_permute_noalloc");
+  if (x_perm) {
+    const int64_t row_bytes = int64_t(d.H) * (d.dtype == MOE_F32 ? 4 : 2);
+    e = moe::launch_gather(x, sorted_pair, offsets, d.E, shape->k, d.N, row_bytes, x_perm, s, tm);
+    if (e != hipSuccess) return hip_fail(e, "moe_permute_noalloc(gather)");
+  }
+  return MOE_OK;
+}
+
 namespace {
 
 moe_status grouped_fwd(const char* name, bool lean, const moe_shape* shape, const void* x_perm,

@@ -39,6 +39,9 @@ hipError_t launch_route_bwd(const float* logits, const int32_t* ids, const float
 
 // ---- permutation
 size_t permute_ws_bytes(int64_t N, int E);
+// The current GPU's copy of the moe_permute_noalloc table
+// (MOE_PERMUTE_NOALLOC_BYTES), looked up on the first call on each GPU.
+hipError_t noalloc_permute_table(int32_t** table);
 hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* inv_pos,
                           int32_t* table, hipStream_t s, KernelTimer* tm);

@@ -18,6 +18,8 @@
 //
 // Pairs whose expert id lies outside [0, E) (a caller error) are dropped:
 // they get inv_pos = -1 and no row, and every access stays in bounds.
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -198,6 +200,34 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
 }
 
 }  // namespace
+
+// The histogram table of moe_permute_noalloc: a file-scope device array (one
+// copy per GPU the library runs on). In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current GPU, looked up once per GPU.
+static __device__ __align__(256) char scratch[MOE_PERMUTE_NOALLOC_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_permute_table(int32_t** table) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_noalloc_ptr[dev] = p;
+  }
+  *table = static_cast<int32_t*>(g_noalloc_ptr[dev]);
+  return hipSuccess;
+}
 
 size_t permute_ws_bytes(int64_t N, int E) {
   const int64_t nchunks = (N + kChunk - 1) / kChunk;

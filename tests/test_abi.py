@@ -123,6 +123,20 @@ def test_null_pointers_rejected(lib):
                                     None) == 1
 
 
+def test_noalloc_permute_rejects_tables_beyond_its_array(lib):
+    """moe_permute_noalloc's table (E * ceil(T k / 64) int32) must fit its
+    4 MiB device array; a larger one is refused before any GPU call."""
+    P = ctypes.c_void_p
+    fake = P(0x10000)
+    # E = 1024, N = 65600 pairs: 1024 * 1025 * 4 bytes > 4 MiB
+    sh = shape(T=65600, k=1, E=1024, H=64, I=32)
+    st = lib.moe_permute_noalloc(ctypes.byref(sh), fake, None, fake, fake, fake, fake, None, None)
+    assert st == 2
+    assert b"4194304" in lib.moe_last_error()
+    assert lib.moe_permute_noalloc(ctypes.byref(shape()), None, None, fake, fake, fake, fake,
+                                   None, None) == 1
+
+
 def test_short_workspace_rejected(lib):
     P = ctypes.c_void_p
     fake = P(0x10000)
