@@ -4,8 +4,9 @@
 
 One step is the whole hot path over one batch: route, permute + gather,
 grouped gate_up (+LoRA, SwiGLU) and down (+LoRA) GEMMs, combine, and the
-backward (combine, route, down and gate_up with SwiGLU', LoRA weight
-gradients, unpermute-sum). Inputs are seeded synthetic tensors already
+backward (the combine backward folded into the down backward: dY's rows
+gathered, dw from the down backward's epilogue; route, down and gate_up with
+SwiGLU', LoRA weight gradients, unpermute-sum). Inputs are seeded synthetic tensors already
 resident in HBM when timing starts. Prints one JSON line.
 
 value    = algorithmic TFLOP/s of the step, F = 12 N H I + 6 N r (2H + 3I)
@@ -64,12 +65,21 @@ def kernel_bytes(name, cfg):
         "gather": T * H * es + N * H * es + N * 4,            # x in, X_perm out, sorted_pair
         "combine": N * H * es + T * H * es + N * 8,           # Yexp in, Y out, inv_pos + weights
         "combine_bwd": T * H * es + 2 * N * H * es + N * 12,  # dY, Yexp in; G out; idx, w, dw
+        "dy_gather": T * H * es + N * H * es + N * 4,         # dY in, its permuted rows out
+        # routing weight per row, w u_d, and the dw partial sums of the down backward
+        "dw_sum": N * 12 + 2 * N * cfg.r * es + N * 4 * dw_slots(cfg) + N * 8,
         "route_bwd": 2 * T * E * 4 + T * k * 8,                # logits in, dlogits out; ids, dw
         "unpermute": N * H * es + T * H * es + N * 4,         # dX_perm in, dX out, inv_pos
         "router_fwd": T * H * es + E * H * es + T * E * 4,    # x, W_r in; logits out
         "router_bwd": T * E * 4 + E * H * es + 2 * T * H * es,  # dlogits, W_r in; dx in and out
         "accumulate": 3 * T * H * es,                          # src, dst in; dst out
     }.get(name)
+
+
+def dw_slots(cfg):
+    """dw partial sums per row that the down backward writes (one per 64-wide
+    wave column of its 256-wide column tiles; 64-wide tiles for float32)."""
+    return -(-cfg.I // 64) if cfg.dtype == "f32" else -(-cfg.I // 256) * 4
 
 
 def block_parts(cfg, shared_I):

@@ -264,6 +264,46 @@ moe_status moe_grouped_lora_bwd_recompute(const moe_shape *shape, const void *dy
                                           const moe_base_grads *base, void *ws, size_t ws_bytes,
                                           void *stream);
 
+/* The combine backward folded into the experts' backward, in one call: it
+ * replaces moe_unpermute_combine_bwd followed by moe_grouped_lora_bwd (or
+ * moe_grouped_full_bwd, or moe_grouped_lora_bwd_recompute with recompute != 0)
+ * and gives the same results, but never forms G = w dY and does not read
+ * y_exp, so y_exp [N, H] need not be kept from the forward (the combine's
+ * output Y is all the forward must leave). It uses, by the chain rule through
+ * the combine (the layer's output) and the split down projection (faster-moe
+ * page, "Faster LoRA MoE training": the same gradients with the products
+ * reordered),
+ *   dw[t, j] = <dY[t], y_exp[p]> = <dY[t] W_d + s (dY[t] B_d) A_d, act[p]>
+ * for p = inv_pos[t*k+j] and the pair's expert: the unweighted product of the
+ * down backward, already formed there, dotted with the SwiGLU output it
+ * recomputes from h; the weight w[t, j] is applied to that product before the
+ * SwiGLU derivative and to the LoRA operands (dB_d = dY^T (w u_d), dA_d from
+ * w s dY B_d).
+ *   dy          [T, H] dtype in
+ *   topk_w      [T, k] float32 in;  sorted_pair, inv_pos [N] int32 in (moe_route,
+ *               moe_permute outputs); offsets [E+1] as for moe_grouped_lora_bwd
+ *   saved       h, act (unless recompute), u_gu, u_d; y_exp is not read
+ *   recompute   0: saving-mode forward; else the lean forward's saved fields
+ *               (h and act recomputed in `ws`, as moe_grouped_lora_bwd_recompute)
+ *   dy_perm     [N, H] dtype scratch, written: dy's rows in permuted order
+ *               (unweighted; with base, scaled by w before dW_d is formed)
+ *   dx_perm, grads, base (NULL: LoRA only)  as moe_grouped_lora_bwd /
+ *               moe_grouped_full_bwd
+ *   d_topk_w    [T, k] float32 out (the routing-weight gradient moe_route_bwd takes)
+ *   ws          backward workspace: moe_workspace_bytes' bwd_ws, or
+ *               moe_workspace_bytes_lean's when recompute != 0
+ * Errors as moe_grouped_lora_bwd, plus a NULL dy, topk_w, sorted_pair,
+ * inv_pos or d_topk_w, and dy_perm aliasing dy, x_perm or dx_perm.  */
+moe_status moe_grouped_lora_combine_bwd(const moe_shape *shape, const void *dy,
+                                        const float *topk_w, const int32_t *sorted_pair,
+                                        const int32_t *inv_pos, const void *x_perm,
+                                        const int32_t *offsets, const moe_weights *weights,
+                                        const moe_saved *saved, int32_t recompute,
+                                        void *dy_perm, void *dx_perm,
+                                        const moe_lora_grads *grads, const moe_base_grads *base,
+                                        float *d_topk_w, void *ws, size_t ws_bytes,
+                                        void *stream);
+
 /* Router projection and its input gradient, for callers that start from
  * hidden states rather than logits. The pages keep the router frozen (faster-
  * moe page, "Implementation details"), so there is no router weight
@@ -319,7 +359,8 @@ typedef enum {
   MOE_K_DOWN_FWD = 4, MOE_K_COMBINE = 5, MOE_K_COMBINE_BWD = 6, MOE_K_ROUTE_BWD = 7,
   MOE_K_DOWN_BWD = 8, MOE_K_GATE_UP_BWD = 9, MOE_K_LORA_SIDE = 10, MOE_K_LORA_WGRAD = 11,
   MOE_K_UNPERMUTE = 12, MOE_K_BASE_WGRAD = 13, MOE_K_ROUTER_FWD = 14, MOE_K_ROUTER_BWD = 15,
-  MOE_K_ACCUMULATE = 16, MOE_K_MERGE = 17, MOE_K_COUNT = 18
+  MOE_K_ACCUMULATE = 16, MOE_K_MERGE = 17, MOE_K_DY_GATHER = 18, MOE_K_DW_SUM = 19,
+  MOE_K_COUNT = 20
 } moe_kernel_id;
 moe_status moe_kernel_timer_enable(int32_t on);
 /* Time only the kernels whose bit (1u << id) is set in mask (all, by default):

@@ -26,7 +26,7 @@ from ._lib import MoeBaseGrads, MoeLoraGrads, MoeSaved, MoeShape, MoeWeights, RO
 
 __all__ = [
     "Shape", "moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
-    "moe_permute_noalloc",
+    "moe_permute_noalloc", "moe_grouped_lora_combine_bwd",
     "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
     "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_workspace_bytes_lean",
     "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute", "moe_router_workspace_bytes",
@@ -292,6 +292,30 @@ def moe_grouped_lora_bwd_recompute(shape: Shape, dy_perm, x_perm, offsets, weigh
     check(_lib.load().moe_grouped_lora_bwd_recompute(
         *head, ctypes.byref(b) if b is not None else None, wsp, wsb, _stream(stream)),
         "moe_grouped_lora_bwd_recompute")
+
+
+def moe_grouped_lora_combine_bwd(shape: Shape, dy, topk_w, sorted_pair, inv_pos, x_perm,
+                                 offsets, weights: dict, saved: dict, dy_perm, dx_perm,
+                                 grads: dict, d_topk_w, ws, base_grads=None, recompute=False,
+                                 stream=None):
+    """The combine backward folded into the experts' backward (G = w dY never
+    formed, y_exp not read): writes dx_perm, the LoRA gradients (and
+    base_grads when given), d_topk_w, and dy's permuted rows into dy_perm."""
+    head, keep, wsp, wsb = _bwd_args(shape, dy_perm, x_perm, offsets, weights, saved, dx_perm,
+                                     grads, ws, lean=recompute)
+    shp, dyp, xp, off, w, sv, dxp, g = head
+    T, k, N, H, E, I, dt = shape.T, shape.k, shape.N, shape.H, shape.E, shape.I, shape.torch_dtype
+    b = None
+    if base_grads is not None:
+        b = MoeBaseGrads(_ptr(base_grads["dw_gu"], (E, 2 * I, H), dt, "dw_gu"),
+                         _ptr(base_grads["dw_d"], (E, H, I), dt, "dw_d"))
+    check(_lib.load().moe_grouped_lora_combine_bwd(
+        shp, _ptr(dy, (T, H), dt, "dy"), _ptr(topk_w, (T, k), torch.float32, "topk_w"),
+        _ptr(sorted_pair, (N,), torch.int32, "sorted_pair"),
+        _ptr(inv_pos, (N,), torch.int32, "inv_pos"), xp, off, w, sv, 1 if recompute else 0,
+        dyp, dxp, g, ctypes.byref(b) if b is not None else None,
+        _ptr(d_topk_w, (T, k), torch.float32, "d_topk_w"), wsp, wsb, _stream(stream)),
+        "moe_grouped_lora_combine_bwd")
 
 
 def _dtype_of(t, name):

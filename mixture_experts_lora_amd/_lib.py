@@ -14,7 +14,8 @@ ROUTER_IDS = {"softmax_topk": 0, "softmax_topk_renorm": 1, "topk_softmax": 2,
 KERNEL_IDS = {"route": 0, "permute": 1, "gather": 2, "gate_up_fwd": 3, "down_fwd": 4,
               "combine": 5, "combine_bwd": 6, "route_bwd": 7, "down_bwd": 8, "gate_up_bwd": 9,
               "lora_side": 10, "lora_wgrad": 11, "unpermute": 12, "base_wgrad": 13,
-              "router_fwd": 14, "router_bwd": 15, "accumulate": 16, "merge": 17}
+              "router_fwd": 14, "router_bwd": 15, "accumulate": 16, "merge": 17,
+              "dy_gather": 18, "dw_sum": 19}
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
            "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
@@ -22,6 +23,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
            "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute",
            "moe_router_workspace_bytes", "moe_router_fwd", "moe_router_bwd", "moe_accumulate",
            "moe_merge_workspace_bytes", "moe_merge_lora", "moe_permute_noalloc",
+           "moe_grouped_lora_combine_bwd",
            "moe_status_str",
            "moe_last_error",
            "moe_kernel_timer_enable", "moe_kernel_timer_select", "moe_kernel_timer_reset",
@@ -99,6 +101,12 @@ def load() -> ctypes.CDLL:
                                                 ctypes.POINTER(MoeLoraGrads),
                                                 ctypes.POINTER(MoeBaseGrads), P, ctypes.c_size_t,
                                                 P]),
+        "moe_grouped_lora_combine_bwd": (st, [ctypes.POINTER(MoeShape), P, P, P, P, P, P,
+                                              ctypes.POINTER(MoeWeights),
+                                              ctypes.POINTER(MoeSaved), I32, P, P,
+                                              ctypes.POINTER(MoeLoraGrads),
+                                              ctypes.POINTER(MoeBaseGrads), P, P,
+                                              ctypes.c_size_t, P]),
         "moe_router_workspace_bytes": (st, [I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]),
         "moe_router_fwd": (st, [P, P, I32, I32, I32, I32, P, P, ctypes.c_size_t, P]),
         "moe_router_bwd": (st, [P, P, I32, I32, I32, I32, P, P, ctypes.c_size_t, P]),

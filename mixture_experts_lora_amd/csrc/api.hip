@@ -362,11 +362,11 @@ moe_status moe_unpermute_combine_bwd(const moe_shape* shape, const void* dy,
 
 namespace {
 
-moe_status grouped_bwd(const char* name, bool lean, const moe_shape* shape,
-                       const void* dy_perm, const void* x_perm, const int32_t* offsets,
-                       const moe_weights* weights, const moe_saved* saved, void* dx_perm,
-                       const moe_lora_grads* grads, const moe_base_grads* base, void* ws,
-                       size_t ws_bytes, void* stream) {
+moe_status grouped_bwd_check(bool lean, const moe_shape* shape, const void* dy_perm,
+                             const void* x_perm, const int32_t* offsets,
+                             const moe_weights* weights, const moe_saved* saved, void* dx_perm,
+                             const moe_lora_grads* grads, const moe_base_grads* base, void* ws,
+                             size_t ws_bytes) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   CHECK_PTR(dy_perm);
@@ -414,6 +414,18 @@ moe_status grouped_bwd(const char* name, bool lean, const moe_shape* shape,
   const size_t need = lean ? moe::experts_bwd_lean_ws_bytes(d) : moe::experts_bwd_ws_bytes(d);
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "backward workspace needs " + std::to_string(need) + " bytes");
+  return MOE_OK;
+}
+
+moe_status grouped_bwd(const char* name, bool lean, const moe_shape* shape,
+                       const void* dy_perm, const void* x_perm, const int32_t* offsets,
+                       const moe_weights* weights, const moe_saved* saved, void* dx_perm,
+                       const moe_lora_grads* grads, const moe_base_grads* base, void* ws,
+                       size_t ws_bytes, void* stream) {
+  moe_status st = grouped_bwd_check(lean, shape, dy_perm, x_perm, offsets, weights, saved,
+                                    dx_perm, grads, base, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  const moe::ExpertDims d = dims_of(shape);
   hipError_t e =
       lean ? moe::launch_experts_bwd_recompute(d, dy_perm, x_perm, offsets, *weights, *saved,
                                                dx_perm, *grads, base, ws, as_stream(stream),
@@ -453,6 +465,49 @@ moe_status moe_grouped_lora_bwd_recompute(const moe_shape* shape, const void* dy
                                           size_t ws_bytes, void* stream) {
   return grouped_bwd("moe_grouped_lora_bwd_recompute", true, shape, dy_perm, x_perm, offsets,
                      weights, saved, dx_perm, grads, base, ws, ws_bytes, stream);
+}
+
+moe_status moe_grouped_lora_combine_bwd(const moe_shape* shape, const void* dy,
+                                        const float* topk_w, const int32_t* sorted_pair,
+                                        const int32_t* inv_pos, const void* x_perm,
+                                        const int32_t* offsets, const moe_weights* weights,
+                                        const moe_saved* saved, int32_t recompute,
+                                        void* dy_perm, void* dx_perm,
+                                        const moe_lora_grads* grads, const moe_base_grads* base,
+                                        float* d_topk_w, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(dy);
+  CHECK_PTR(topk_w);
+  CHECK_PTR(sorted_pair);
+  CHECK_PTR(inv_pos);
+  CHECK_PTR(d_topk_w);
+  const bool lean = recompute != 0;
+  if (dy_perm == dy || dy_perm == x_perm || dy_perm == dx_perm)
+    return fail(MOE_ERR_INVALID_ARG, "dy_perm aliases another tensor");
+  // the expert part: the same checks as the separate backward calls (dy_perm
+  // is written here, so it takes the place of the G input)
+  st = grouped_bwd_check(lean, shape, dy_perm, x_perm, offsets, weights, saved, dx_perm, grads,
+                         base, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  const moe::ExpertDims d = dims_of(shape);
+  moe::CombineBwd cb;
+  cb.dy = dy;
+  cb.topk_w = topk_w;
+  cb.sorted_pair = sorted_pair;
+  cb.inv_pos = inv_pos;
+  cb.T = shape->T;
+  cb.k = shape->k;
+  cb.d_topk_w = d_topk_w;
+  hipError_t e =
+      lean ? moe::launch_experts_bwd_recompute(d, dy_perm, x_perm, offsets, *weights, *saved,
+                                               dx_perm, *grads, base, ws, as_stream(stream),
+                                               moe::active_timer(), &cb)
+           : moe::launch_experts_bwd(d, dy_perm, x_perm, offsets, *weights, *saved, dx_perm,
+                                     *grads, base, ws, as_stream(stream), moe::active_timer(),
+                                     &cb);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_lora_combine_bwd");
 }
 
 namespace {

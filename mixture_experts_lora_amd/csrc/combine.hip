@@ -190,7 +190,63 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
   }
 }
 
+// Routing weight of each permuted row, and the row-weighted copy of u
+// ([N, r]): one thread per element of u.
+template <typename Elem>
+__global__ __launch_bounds__(256) void perm_weights_kernel(const float* __restrict__ w,
+                                                           const int32_t* __restrict__ sorted_pair,
+                                                           int64_t N, const Elem* __restrict__ u,
+                                                           int r, float* __restrict__ w_perm,
+                                                           Elem* __restrict__ wu) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= N * r) return;
+  const int64_t row = i / r;
+  const float wr = w[sorted_pair[row]];
+  wu[i] = from_f32<Elem>(wr * to_f32<Elem>(u[i]));
+  if (i - row * r == 0) w_perm[row] = wr;
+}
+
+// d_topk_w[p]: the down backward's per-slot partial sums of <dAct', act> for
+// pair p's row (contiguous per row), added in slot order (deterministic).
+__global__ __launch_bounds__(256) void dw_sum_kernel(const float* __restrict__ dwp, int slots,
+                                                     const int32_t* __restrict__ inv_pos,
+                                                     int64_t npairs, float* __restrict__ dw) {
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (p >= npairs) return;
+  const int32_t pos = inv_pos[p];
+  float acc = 0.f;
+  if (pos >= 0) {
+    const float* q = dwp + static_cast<int64_t>(pos) * slots;
+    for (int s = 0; s < slots; ++s) acc += q[s];
+  }
+  dw[p] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_perm_weights(int dtype, const float* w, const int32_t* sorted_pair, int64_t N,
+                               const void* u, int r, float* w_perm, void* wu, hipStream_t s) {
+  const int64_t total = N * r;
+  if (total <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  auto go = [&](auto tag) {
+    using Elem = decltype(tag);
+    hipLaunchKernelGGL(perm_weights_kernel<Elem>, grid, dim3(256), 0, s, w, sorted_pair, N,
+                       static_cast<const Elem*>(u), r, w_perm, static_cast<Elem*>(wu));
+  };
+  if (dtype == MOE_BF16) go(bf16_t{});
+  else if (dtype == MOE_F16) go(f16_t{});
+  else go(float{});
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_sum(const float* dwp, int slots, const int32_t* inv_pos, int64_t npairs,
+                         float* d_topk_w, hipStream_t s) {
+  if (npairs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dw_sum_kernel, dim3(static_cast<unsigned>((npairs + 255) / 256)), dim3(256),
+                     0, s, dwp, slots, inv_pos, npairs, d_topk_w);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos, const float* w,
                           int T, int k, int H, void* y, hipStream_t s, KernelTimer* tm) {

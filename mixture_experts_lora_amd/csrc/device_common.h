@@ -80,6 +80,15 @@ __device__ __forceinline__ void swiglu_bwd(float g, float u, float d, float& dg,
   du = d * g * s;
 }
 
+// SwiGLU backward that also returns the forward output g s u (one logistic
+// evaluation for both).
+__device__ __forceinline__ float swiglu_bwd_act(float g, float u, float d, float& dg, float& du) {
+  float s = sigmoidf_(g);
+  dg = d * u * s * (1.0f + g * (1.0f - s));
+  du = d * g * s;
+  return g * s * u;
+}
+
 // Wave-wide butterfly sum (every lane gets the total; fixed order, deterministic).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -88,6 +88,14 @@ struct GemmArgs {
   float* vp;
   int64_t vp_tstride;  // elements between M tiles of vp
   int vsplit;
+  // EPI_SWIGLU_BWD (GROUP_M), both optional: roww[row] scales the product
+  // before the SwiGLU derivative (dAct = w * acc); dwp receives, per output
+  // row, float32 partial sums of acc * act over each wave's column slice
+  // (at dwp[row * dwp_slots + n_tile * (BN / WN) + wave column]), act being
+  // SwiGLU(h) recomputed from the h the epilogue loads.
+  const float* roww;
+  float* dwp;
+  int dwp_slots;
 };
 
 // Spread `total` logical tiles over the 8 XCDs so that each XCD works on a
@@ -159,17 +167,6 @@ __device__ __forceinline__ void epi_store(const GemmArgs& p, int e, int64_t row0
         if (EPI == EPI_ADD && n_col + j < p.N) o[j] += to_f32<T>(sp[n_col + j]);
       }
       store4<T>(rp, n_col, p.N, (p.ld_out & 3) == 0, o);
-    } else if (EPI == EPI_SWIGLU_BWD) {
-      if (n_col >= p.N) return;  // N = I (multiple of 8)
-      const T* hr = static_cast<const T*>(p.aux) + row * p.ld_aux;
-      float g[4], uu[4], dg[4], du[4];
-      Vec4<T>::load(hr + n_col, g);
-      Vec4<T>::load(hr + p.I + n_col, uu);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) swiglu_bwd(g[j], uu[j], v[j], dg[j], du[j]);
-      T* dr = static_cast<T*>(p.out) + row * p.ld_out;
-      Vec4<T>::store(dr + n_col, dg);
-      Vec4<T>::store(dr + p.I + n_col, du);
     }
   } else {
     // GROUP_K: out[e][m][n], row = feature m (rows = valid M in this tile)
@@ -1217,25 +1214,39 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
         const int col = n0 + wn * WN + 8 * s;
         float v[8];
         read8_interleaved<WN>(slab, r, s, v);
-        if (m_local >= rows) continue;
         if (MODE == GROUP_M && EPI == EPI_SWIGLU_BWD) {
-          if (col >= p.N) continue;  // N = I, a multiple of 8
+          // every lane stays to the end: the dw partial is summed over the
+          // SEGS lanes that hold one row
           const int64_t row = row0 + m_local;
-          float g[8], u[8], dg[8], du[8];
-          if constexpr (HPRE) {
-            unpack8<F16>(hpre[mi & 1][pass][0], g);
-            unpack8<F16>(hpre[mi & 1][pass][1], u);
-          } else {
-            const bf16_t* hr = static_cast<const bf16_t*>(p.aux) + row * p.ld_aux;
-            load8<F16>(hr + col, g);
-            load8<F16>(hr + p.I + col, u);
-          }
+          float part = 0.f;
+          if (m_local < rows && col < p.N) {  // N = I, a multiple of 8
+            float g[8], u[8], dg[8], du[8];
+            if constexpr (HPRE) {
+              unpack8<F16>(hpre[mi & 1][pass][0], g);
+              unpack8<F16>(hpre[mi & 1][pass][1], u);
+            } else {
+              const bf16_t* hr = static_cast<const bf16_t*>(p.aux) + row * p.ld_aux;
+              load8<F16>(hr + col, g);
+              load8<F16>(hr + p.I + col, u);
+            }
+            const float wr = p.roww ? p.roww[row] : 1.0f;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) swiglu_bwd(g[j], u[j], v[j], dg[j], du[j]);
-          bf16_t* dr = static_cast<bf16_t*>(p.out) + row * p.ld_out;
-          store8<F16>(dr + col, dg);
-          store8<F16>(dr + p.I + col, du);
-        } else if (EPI == EPI_STORE_F32) {
+            for (int j = 0; j < 8; ++j)
+              part += v[j] * swiglu_bwd_act(g[j], u[j], wr * v[j], dg[j], du[j]);
+            bf16_t* dr = static_cast<bf16_t*>(p.out) + row * p.ld_out;
+            store8<F16>(dr + col, dg);
+            store8<F16>(dr + p.I + col, du);
+          }
+          if (p.dwp) {
+#pragma unroll
+            for (int off = SEGS / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
+            if (s == 0 && m_local < rows)
+              p.dwp[row * p.dwp_slots + n_tile * WAVES_N + wn] = part;
+          }
+          continue;
+        }
+        if (m_local >= rows) continue;
+        if (EPI == EPI_STORE_F32) {
           // GROUP_M: router logits; GROUP_K: split-K partial weight gradients
           float* rp = MODE == GROUP_M
                           ? static_cast<float*>(p.out) + (row0 + m_local) * p.ld_out
@@ -1370,6 +1381,38 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs p) {
       }
       __syncthreads();
     }
+  }
+  if constexpr (!PAIRED && MODE == GROUP_M && EPI == EPI_SWIGLU_BWD) {
+    // SwiGLU backward with optional row weights and dw partials (one slot per
+    // N tile, summed over the 16 threads of a row: consecutive lanes)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m_local = ty * 4 + i;
+      const int64_t row = row0 + m_local;
+      float part = 0.f;
+      if (m_local < rows) {
+        const float* hr = static_cast<const float*>(p.aux) + row * p.ld_aux;
+        float* dr = static_cast<float*>(p.out) + row * p.ld_out;
+        const float wr = p.roww ? p.roww[row] : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + tx * 4 + j;
+          if (col < p.N) {
+            const float g = hr[col], u = hr[p.I + col];
+            float dg, du;
+            part += acc[i][j] * swiglu_bwd_act(g, u, wr * acc[i][j], dg, du);
+            dr[col] = dg;
+            dr[p.I + col] = du;
+          }
+        }
+      }
+      if (p.dwp) {
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
+        if (tx == 0 && m_local < rows) p.dwp[row * p.dwp_slots + n_tile] = part;
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1527,11 +1570,19 @@ hipError_t launch(K kern, int grid, const GemmArgs& a, hipStream_t s, int thread
 //  - 128 x 256, four waves, buffer->LDS DMA, BK 32, three stages, two blocks
 //    per CU: ranks that are not a multiple of 8 (the LoRA segment, K = r,
 //    then takes element-wise fills).
+inline bool all_vec(const GemmArgs& a) {
+  return a.a[0].vec && a.b[0].vec && (a.K[1] == 0 || (a.a[1].vec && a.b[1].vec));
+}
+
+// Wave columns per N tile of the kernel launch_big runs (the dw partial
+// slots of a SwiGLU-backward launch): 256 / 64 for the register-staged
+// kernel, 256 / 128 for the other two.
+inline int big_waves_n(const GemmArgs& a, int bm) { return bm == 256 && all_vec(a) ? 4 : 2; }
+
 template <int MODE, int EPI, bool PAIRED, bool A_KC, bool B_KC>
 hipError_t launch_big(int grid, const GemmArgs& a, hipStream_t s, int bm) {
   if (bm == 256) {
-    const bool all_vec = a.a[0].vec && a.b[0].vec && (a.K[1] == 0 || (a.a[1].vec && a.b[1].vec));
-    if (!all_vec)
+    if (!all_vec(a))
       return launch(GEMM16(a.dtype, 256, 256, 128, 128, 32, 3, 1, MODE, EPI, PAIRED, A_KC, B_KC, 0), grid, a, s);
     return launch(GEMM16(a.dtype, 256, 256, 128, 64, 64, 2, 1, MODE, EPI, PAIRED, A_KC, B_KC, 1), grid, a, s, 512);
   }
@@ -1712,6 +1763,8 @@ struct SideOut {
   const void* bm = nullptr;   // [E][P][Q]
   void* out = nullptr;        // V [N, Q] in the layer dtype
   float* part = nullptr;      // ceil(P / 256) x N x Q float32 partials
+  const float* roww = nullptr;  // optional: also out_w[n] = roww[n] V[n] (one rounding)
+  void* out_w = nullptr;
 };
 
 // The fused path covers 16-bit layers, Q = r <= 32 with rows of 16 bytes.
@@ -1724,16 +1777,46 @@ inline size_t side_part_bytes(const ExpertDims& d) {
   return static_cast<size_t>(ceil_div(P, 256)) * d.N * d.r * 4;
 }
 
-// V[i] = scale * sum over tiles t (in order) of part[t][i]
+// V[i] = scale * sum over tiles t (in order) of part[t][i]; with roww, also
+// out_w[i] = roww[i / Q] * V[i] (from the float32 sum, one rounding).
 template <typename Elem>
 __global__ __launch_bounds__(256) void side_sum_kernel(const float* __restrict__ part, int tiles,
                                                        int64_t tstride, float scale,
-                                                       Elem* __restrict__ out) {
+                                                       Elem* __restrict__ out,
+                                                       const float* __restrict__ roww, int Q,
+                                                       Elem* __restrict__ out_w) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= tstride) return;
   float acc = 0.f;
   for (int t = 0; t < tiles; ++t) acc += part[t * tstride + i];
   out[i] = from_f32<Elem>(acc * scale);
+  if (roww) out_w[i] = from_f32<Elem>(roww[i / Q] * (acc * scale));
+}
+
+// dst[n][c] = w[n] * src[n][c] over rows x cols (dst may be src), one rounding.
+template <typename Elem>
+__global__ __launch_bounds__(256) void scale_rows_kernel(const Elem* src, const float* __restrict__ w,
+                                                         int64_t total, int cols, Elem* dst) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  dst[i] = from_f32<Elem>(w[i / cols] * to_f32<Elem>(src[i]));
+}
+
+hipError_t scale_rows(int dtype, const void* src, const float* w, int64_t rows, int cols,
+                      void* dst, hipStream_t s) {
+  const int64_t total = rows * cols;
+  if (total <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(scale_rows_kernel<bf16_t>, grid, dim3(256), 0, s,
+                       static_cast<const bf16_t*>(src), w, total, cols, static_cast<bf16_t*>(dst));
+  else if (dtype == MOE_F16)
+    hipLaunchKernelGGL(scale_rows_kernel<f16_t>, grid, dim3(256), 0, s,
+                       static_cast<const f16_t*>(src), w, total, cols, static_cast<f16_t*>(dst));
+  else
+    hipLaunchKernelGGL(scale_rows_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(src), w, total, cols, static_cast<float*>(dst));
+  return hipGetLastError();
 }
 
 // split_ws: at least wgrad_split_bytes(d, P, Q) bytes (unused when that is 0),
@@ -1769,10 +1852,12 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
     const dim3 grid(static_cast<unsigned>((n + 255) / 256));
     if (d.dtype == MOE_BF16)
       hipLaunchKernelGGL(side_sum_kernel<bf16_t>, grid, dim3(256), 0, s, side->part, tiles, n,
-                         d.scale, static_cast<bf16_t*>(side->out));
+                         d.scale, static_cast<bf16_t*>(side->out), side->roww, Q,
+                         static_cast<bf16_t*>(side->out_w));
     else
       hipLaunchKernelGGL(side_sum_kernel<f16_t>, grid, dim3(256), 0, s, side->part, tiles, n,
-                         d.scale, static_cast<f16_t*>(side->out));
+                         d.scale, static_cast<f16_t*>(side->out), side->roww, Q,
+                         static_cast<f16_t*>(side->out_w));
     return hipGetLastError();
   };
   if (S <= 1) {
@@ -1820,15 +1905,57 @@ size_t experts_fwd_ws_bytes(const ExpertDims& d) {
   return tile_ws(nullptr, d).bytes;
 }
 
-size_t experts_bwd_ws_bytes(const ExpertDims& d) {
-  const size_t esz = d.dtype == MOE_F32 ? 4 : 2;
-  size_t b = tile_ws(nullptr, d).bytes;
-  b += align_up(static_cast<size_t>(d.N) * d.r * esz) * 2;        // G B_d, dH B_gu
-  b += align_up(static_cast<size_t>(d.N) * 2 * d.I * esz);         // dH
-  b += align_up(lora_wgrad_split_bytes(d));                         // split-K partials
-  if (d.dtype != MOE_F32) b += align_up(side_part_bytes(d));        // fused side products
-  return b;
+namespace {
+
+// dw partial slots per row of the down backward (the combine backward folded
+// into it): one per wave column of every N tile of the SwiGLU-backward GEMM,
+// the most any of its kernels uses (256-wide tiles of 64-wide waves; float32
+// layers 64-wide tiles of one slot).
+inline int dw_slots_max(const ExpertDims& d) {
+  return d.dtype == MOE_F32 ? ceil_div(d.I, 64) : ceil_div(d.I, 256) * 4;
 }
+
+// Backward workspace: tile lists, G B_d and dH B_gu [N, r], dH [N, 2I],
+// split-K and side-product partials; for the combine backward folded in,
+// also the permuted routing weights [N] f32, w u_d and w G B_d [N, r] and
+// the dw partials [slots, N] f32.
+struct BwdWs {
+  WsLayout L;
+  void *gb, *dhb, *dh, *split;
+  float* vpart;
+  float* w_perm;
+  void *wu_d, *gbw;
+  float* dwp;
+  size_t bytes;
+};
+
+BwdWs bwd_ws(void* ws, const ExpertDims& d) {
+  const size_t esz = d.dtype == MOE_F32 ? 4 : 2;
+  BwdWs B;
+  B.L = tile_ws(ws, d);
+  char* base = static_cast<char*>(ws);
+  size_t off = B.L.bytes;
+  auto take = [&](size_t n) {
+    void* q = base ? base + off : nullptr;
+    off += align_up(n);
+    return q;
+  };
+  B.gb = take(static_cast<size_t>(d.N) * d.r * esz);
+  B.dhb = take(static_cast<size_t>(d.N) * d.r * esz);
+  B.dh = take(static_cast<size_t>(d.N) * 2 * d.I * esz);
+  B.split = take(lora_wgrad_split_bytes(d));
+  B.vpart = static_cast<float*>(take(d.dtype != MOE_F32 ? side_part_bytes(d) : 0));
+  B.w_perm = static_cast<float*>(take(static_cast<size_t>(d.N) * 4));
+  B.wu_d = take(static_cast<size_t>(d.N) * d.r * esz);
+  B.gbw = take(static_cast<size_t>(d.N) * d.r * esz);
+  B.dwp = static_cast<float*>(take(static_cast<size_t>(dw_slots_max(d)) * d.N * 4));
+  B.bytes = off;
+  return B;
+}
+
+}  // namespace
+
+size_t experts_bwd_ws_bytes(const ExpertDims& d) { return bwd_ws(nullptr, d).bytes; }
 
 namespace {
 
@@ -1922,20 +2049,14 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
                               const int32_t* offsets, const moe_weights& w,
                               const moe_saved& sv, void* dx_perm, const moe_lora_grads& gr,
                               const moe_base_grads* base, void* ws, hipStream_t s,
-                              KernelTimer* tm) {
-  const WsLayout L = tile_ws(ws, d);
+                              KernelTimer* tm, const CombineBwd* cb) {
+  const BwdWs B = bwd_ws(ws, d);
+  const WsLayout& L = B.L;
   const int H = d.H, I = d.I, r = d.r;
-  const size_t esz = d.dtype == MOE_F32 ? 4 : 2;
-  char* p = static_cast<char*>(ws) + L.bytes;
-  void* gb = p;
-  p += align_up(static_cast<size_t>(d.N) * r * esz);
-  void* dhb = p;
-  p += align_up(static_cast<size_t>(d.N) * r * esz);
-  void* dh = p;
-  p += align_up(static_cast<size_t>(d.N) * 2 * I * esz);
-  void* split = p;
-  p += align_up(lora_wgrad_split_bytes(d));
-  float* vpart = reinterpret_cast<float*>(p);
+  void* gb = B.gb;    // s G B_d (with cb: s dY B_d, unweighted)
+  void* dhb = B.dhb;  // s dH B_gu
+  void* dh = B.dh;
+  void* split = B.split;
   // The side products G B_d and dH B_gu read the same matrices as the
   // gradients dB_d = G^T u_d and dB_gu = dH^T u_gu; where the shapes allow,
   // one kernel reads each matrix once for both.
@@ -1943,16 +2064,41 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
   const bool fuse_gu = side_fusable(d, 2 * I, r) && aligned16(w.b_gu);
 
   MOE_TRY(build_tiles(L, offsets, d.E, s));
+  // With the combine backward folded in, g holds dY's rows unweighted and
+  // every consumer of G = w dY applies w itself: dB_d = dY^T (w u_d); the
+  // down backward runs on dY and its epilogue scales the product by w (dw
+  // comes from the unweighted product); dA_d = (w s dY B_d)^T act; the full
+  // fine-tuning dW_d = (w dY)^T act after the rows are scaled in place.
+  const void* ud_eff = sv.u_d;   // right operand of dB_d
+  const void* gb_da = gb;        // left operand of dA_d
+  if (cb) {
+    TimedScope ts(tm, MOE_K_DY_GATHER, s);
+    const int64_t row_bytes = static_cast<int64_t>(H) * (d.dtype == MOE_F32 ? 4 : 2);
+    MOE_TRY(launch_gather(cb->dy, cb->sorted_pair, offsets, d.E, cb->k, d.N, row_bytes,
+                          const_cast<void*>(g), s, nullptr));
+  }
+  if (cb) {  // w of each permuted row, and w u_d
+    TimedScope ts(tm, MOE_K_DW_SUM, s);
+    MOE_TRY(launch_perm_weights(d.dtype, cb->topk_w, cb->sorted_pair, d.N, sv.u_d, r, B.w_perm,
+                                B.wu_d, s));
+    ud_eff = B.wu_d;
+    gb_da = B.gbw;
+  }
   if (fuse_d) {  // dB_d = G^T u_d [H, r] and gb = s G B_d in one pass over G
     TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
     SideOut so;
     so.bm = w.b_d;
     so.out = gb;
-    so.part = vpart;
-    MOE_TRY(weight_grad(d, offsets, g, H, sv.u_d, r, gr.db_d, s, split, &so));
+    so.part = B.vpart;
+    if (cb) {
+      so.roww = B.w_perm;
+      so.out_w = B.gbw;
+    }
+    MOE_TRY(weight_grad(d, offsets, g, H, ud_eff, r, gr.db_d, s, split, &so));
   } else {  // gb = s G B_d      (B_d[e] is [H, r]: K = H rows, r contiguous)
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
     MOE_TRY(side_product(d, offsets, L, g, H, w.b_d, static_cast<int64_t>(H) * r, 0, gb, s));
+    if (cb) MOE_TRY(scale_rows(d.dtype, gb, B.w_perm, d.N, r, B.gbw, s));
   }
   {  // dAct = G W_d + gb A_d ; dH = SwiGLU'(h) dAct
     GemmArgs a = base_args(d, offsets, L.big);
@@ -1967,23 +2113,34 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     a.ld_out = 2 * I;
     a.aux = sv.h;
     a.ld_aux = 2 * I;
-    TimedScope ts(tm, MOE_K_DOWN_BWD, s);
-    if (d.dtype != MOE_F32) {
-      a.ntn = ceil_div(I, 256);
-      MOE_TRY((launch_big<GROUP_M, EPI_SWIGLU_BWD, false, true, false>(
-                     gm_grid(d, L.big, a.ntn), a, s, L.big.bm)));
-    } else {
-      a.ntn = ceil_div(I, 64);
-      MOE_TRY(launch(gemm_f32<GROUP_M, EPI_SWIGLU_BWD, false>, gm_grid(d, L.big, a.ntn), a, s));
+    a.ntn = d.dtype != MOE_F32 ? ceil_div(I, 256) : ceil_div(I, 64);
+    if (cb) {
+      a.roww = B.w_perm;
+      a.dwp = B.dwp;
+      a.dwp_slots = d.dtype != MOE_F32 ? a.ntn * big_waves_n(a, L.big.bm) : a.ntn;
+    }
+    {
+      TimedScope ts(tm, MOE_K_DOWN_BWD, s);
+      if (d.dtype != MOE_F32)
+        MOE_TRY((launch_big<GROUP_M, EPI_SWIGLU_BWD, false, true, false>(
+                       gm_grid(d, L.big, a.ntn), a, s, L.big.bm)));
+      else
+        MOE_TRY(launch(gemm_f32<GROUP_M, EPI_SWIGLU_BWD, false>, gm_grid(d, L.big, a.ntn), a, s));
+    }
+    if (cb) {
+      TimedScope ts(tm, MOE_K_DW_SUM, s);
+      MOE_TRY(launch_dw_sum(B.dwp, a.dwp_slots, cb->inv_pos,
+                            static_cast<int64_t>(cb->T) * cb->k, cb->d_topk_w, s));
     }
   }
   {  // dB_d = G^T u_d  [H, r] (unless fused above) ;  dA_d = gb^T act  [r, I]
     TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
-    if (!fuse_d) MOE_TRY(weight_grad(d, offsets, g, H, sv.u_d, r, gr.db_d, s, split));
-    MOE_TRY(weight_grad(d, offsets, gb, r, sv.act, I, gr.da_d, s, split));
+    if (!fuse_d) MOE_TRY(weight_grad(d, offsets, g, H, ud_eff, r, gr.db_d, s, split));
+    MOE_TRY(weight_grad(d, offsets, gb_da, r, sv.act, I, gr.da_d, s, split));
   }
   if (base) {  // full fine-tuning: dW_d = G^T act  [H, I]
     TimedScope ts(tm, MOE_K_BASE_WGRAD, s);
+    if (cb) MOE_TRY(scale_rows(d.dtype, g, B.w_perm, d.N, H, const_cast<void*>(g), s));
     MOE_TRY(weight_grad(d, offsets, g, H, sv.act, I, base->dw_d, s, nullptr));
   }
   if (fuse_gu) {  // dB_gu = dH^T u_gu [2I, r] and dhb = s dH B_gu in one pass over dH
@@ -1991,7 +2148,7 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     SideOut so;
     so.bm = w.b_gu;
     so.out = dhb;
-    so.part = vpart;
+    so.part = B.vpart;
     MOE_TRY(weight_grad(d, offsets, dh, 2 * I, sv.u_gu, r, gr.db_gu, s, split, &so));
   } else {  // dhb = s dH B_gu   (B_gu[e] is [2I, r])
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
@@ -2051,12 +2208,13 @@ hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, cons
                                         const int32_t* offsets, const moe_weights& w,
                                         const moe_saved& sv, void* dx_perm,
                                         const moe_lora_grads& gr, const moe_base_grads* base,
-                                        void* ws, hipStream_t s, KernelTimer* tm) {
+                                        void* ws, hipStream_t s, KernelTimer* tm,
+                                        const CombineBwd* cb) {
   const moe_saved full = lean_saved(d, sv, ws, experts_bwd_ws_bytes(d));
   const WsLayout L = tile_ws(ws, d);
   MOE_TRY(build_tiles(L, offsets, d.E, s));
   MOE_TRY(launch_gate_up(d, L, x_perm, offsets, w, sv.u_gu, full.h, full.act, s, tm));
-  return launch_experts_bwd(d, g, x_perm, offsets, w, full, dx_perm, gr, base, ws, s, tm);
+  return launch_experts_bwd(d, g, x_perm, offsets, w, full, dx_perm, gr, base, ws, s, tm, cb);
 }
 
 // ----------------------------------------------------------------- router projection

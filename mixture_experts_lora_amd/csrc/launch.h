@@ -56,6 +56,15 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_exp,
                               const int32_t* inv_pos, const float* w, int T, int k, int H,
                               void* g, float* dw, hipStream_t s, KernelTimer* tm);
 
+// Folded combine backward: w_perm[i] = w[sorted_pair[i]] (the routing weight
+// of each permuted row) and wu[i][c] = w_perm[i] u[i][c] ([N, r] of `dtype`);
+// d_topk_w[p] = sum over slots s (in order) of dwp[inv_pos[p] * slots + s]
+// (0 where inv_pos[p] < 0).
+hipError_t launch_perm_weights(int dtype, const float* w, const int32_t* sorted_pair, int64_t N,
+                               const void* u, int r, float* w_perm, void* wu, hipStream_t s);
+hipError_t launch_dw_sum(const float* dwp, int slots, const int32_t* inv_pos, int64_t npairs,
+                         float* d_topk_w, hipStream_t s);
+
 // ---- grouped expert GEMMs
 struct ExpertDims {
   int64_t N;  // routed rows
@@ -69,12 +78,28 @@ size_t experts_bwd_ws_bytes(const ExpertDims& d);
 hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int32_t* offsets,
                               const moe_weights& w, const moe_saved& sv, void* ws,
                               hipStream_t s, KernelTimer* tm);
+// The combine backward folded into the experts' backward: G = w dY is never
+// formed. dY's rows are gathered unweighted (in permuted order) into the
+// caller's g buffer, the routing weights are applied inside the kernels, and
+// dw = <dY, y_exp> is taken in the down backward's epilogue as <dAct', act>
+// with dAct' the unweighted product (so y_exp need not be kept).
+struct CombineBwd {
+  const void* dy;        // [T, H]
+  const float* topk_w;   // [T, k]
+  const int32_t* sorted_pair;
+  const int32_t* inv_pos;
+  int T, k;
+  float* d_topk_w;       // [T, k] out
+};
+
 // `base` may be null (LoRA only); otherwise the base-weight gradients are written too.
+// `cb` null: g holds G = w dY rows (read only). Otherwise g is an [N, H]
+// buffer the call fills with dY's rows, and cb's d_topk_w is written.
 hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_perm,
                               const int32_t* offsets, const moe_weights& w,
                               const moe_saved& sv, void* dx_perm, const moe_lora_grads& gr,
                               const moe_base_grads* base, void* ws, hipStream_t s,
-                              KernelTimer* tm);
+                              KernelTimer* tm, const CombineBwd* cb = nullptr);
 
 // Recompute (activation-lean) mode: the forward keeps h and act in its
 // workspace instead of `saved`; the backward recomputes them into its own.
@@ -88,7 +113,8 @@ hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, cons
                                         const int32_t* offsets, const moe_weights& w,
                                         const moe_saved& sv, void* dx_perm,
                                         const moe_lora_grads& gr, const moe_base_grads* base,
-                                        void* ws, hipStream_t s, KernelTimer* tm);
+                                        void* ws, hipStream_t s, KernelTimer* tm,
+                                        const CombineBwd* cb = nullptr);
 
 // ---- merged export W + s B A (per expert, both projections; either output may be NULL)
 size_t merge_ws_bytes(const ExpertDims& d);

@@ -5,8 +5,13 @@ so nothing is allocated inside a step) and issues, on torch's current stream:
 
   forward   moe_route -> moe_permute (+ gather) -> moe_grouped_lora_fwd
             -> moe_unpermute_combine
-  backward  moe_unpermute_combine_bwd -> moe_route_bwd -> moe_grouped_lora_bwd
-            -> moe_unpermute_combine (weights 1: dX_perm summed back to tokens)
+  backward  moe_grouped_lora_combine_bwd (the combine backward folded into
+            the experts' backward: d_topk_w from the down backward, no G)
+            -> moe_route_bwd -> moe_unpermute_combine (weights 1: dX_perm
+            summed back to tokens)
+  With fold_combine_bwd=False the backward runs the separate calls
+  moe_unpermute_combine_bwd -> moe_route_bwd -> moe_grouped_lora_bwd, which
+  read the expert outputs y_exp, so those are then kept from the forward.
 
 MoELoRAFunction wraps the same calls as a torch.autograd.Function whose
 gradients are dX, d logits and the four LoRA gradients (base weights frozen).
@@ -27,6 +32,7 @@ from __future__ import annotations
 import torch
 
 from . import (Shape, moe_accumulate, moe_grouped_full_bwd, moe_grouped_lora_bwd,
+               moe_grouped_lora_combine_bwd,
                moe_grouped_lora_bwd_recompute, moe_grouped_lora_fwd, moe_grouped_lora_fwd_lean,
                moe_permute, moe_route, moe_route_bwd, moe_router_bwd, moe_router_fwd,
                moe_router_workspace_bytes, moe_unpermute_combine, moe_unpermute_combine_bwd,
@@ -80,6 +86,11 @@ class MoELoRALayer:
     in the backward's), and neither is x_perm (the backward gathers it again
     from x, so backward() needs x).
 
+    fold_combine_bwd=True (the default) runs the combine backward inside the
+    experts' backward, so the expert outputs y_exp are a forward transient
+    (held in the scratch rows the backward later uses for dY's rows) rather
+    than a saved activation.
+
     scratch: a LayerScratch to share with other layers or chunks (one is made
     when None). out: optional views {"y", "dx", "d_logits"} to write the
     outputs into (a chunk writes its rows of the whole layer's outputs).
@@ -88,8 +99,9 @@ class MoELoRALayer:
     def __init__(self, shape: Shape, router: str, device="cuda", full_ft: bool = False,
                  recompute: bool = False, scratch: LayerScratch | None = None,
                  out: dict | None = None, grads: dict | None = None,
-                 base_grads: dict | None = None):
+                 base_grads: dict | None = None, fold_combine_bwd: bool = True):
         self.shape, self.router, self.full_ft, self.recompute = shape, router, full_ft, recompute
+        self.fold = fold_combine_bwd
         T, H, I, E, k, r, N = shape.T, shape.H, shape.I, shape.E, shape.k, shape.r, shape.N
         dt = shape.torch_dtype
         z = lambda *s, dtype=dt: torch.empty(s, device=device, dtype=dtype)  # noqa: E731
@@ -102,9 +114,14 @@ class MoELoRALayer:
         self.counts, self.offsets = z(E, dtype=i32), z(E + 1, dtype=i32)
         self.sorted_pair, self.inv_pos = z(N, dtype=i32), z(N, dtype=i32)
         self.x_perm = scratch.row_view(2, shape) if recompute else z(N, H)
-        self.saved = {"u_gu": z(N, r), "u_d": z(N, r), "y_exp": z(N, H)}
+        self.saved = {"u_gu": z(N, r), "u_d": z(N, r)}
         if not recompute:
             self.saved.update(h=z(N, 2 * I), act=z(N, I))
+        if self.fold:
+            # forward transient: consumed by the combine, then the rows hold dY's
+            self.y_exp = scratch.row_view(0, shape)
+        else:
+            self.y_exp = self.saved["y_exp"] = z(N, H)
         out = out or {}
         self.y = out["y"] if "y" in out else z(T, H)
         self.dx = out["dx"] if "dx" in out else z(T, H)
@@ -137,8 +154,9 @@ class MoELoRALayer:
         moe_route(logits, s.k, self.router, self.topk_ids, self.topk_w, stream)
         self._permute(x, stream)
         fwd = moe_grouped_lora_fwd_lean if self.recompute else moe_grouped_lora_fwd
-        fwd(s, self.x_perm, self.offsets, weights, self.saved, self.ws_fwd, stream)
-        moe_unpermute_combine(s, self.saved["y_exp"], self.inv_pos, self.topk_w, self.y, stream)
+        fwd(s, self.x_perm, self.offsets, weights, {**self.saved, "y_exp": self.y_exp},
+            self.ws_fwd, stream)
+        moe_unpermute_combine(s, self.y_exp, self.inv_pos, self.topk_w, self.y, stream)
         return self.y
 
     def backward(self, dy, logits, weights: dict, stream=None, x=None):
@@ -147,7 +165,17 @@ class MoELoRALayer:
             if x is None:
                 raise ValueError("the activation-lean backward gathers x_perm again: pass x")
             self._permute(x, stream)   # same routing, so the same permutation and rows
-        moe_unpermute_combine_bwd(s, dy, self.saved["y_exp"], self.inv_pos, self.topk_w,
+        if self.fold:
+            moe_grouped_lora_combine_bwd(s, dy, self.topk_w, self.sorted_pair, self.inv_pos,
+                                         self.x_perm, self.offsets, weights, self.saved,
+                                         self.dy_perm, self.dx_perm, self.grads, self.d_topk_w,
+                                         self.ws_bwd, base_grads=self.base_grads,
+                                         recompute=self.recompute, stream=stream)
+            moe_route_bwd(logits, self.topk_ids, self.d_topk_w, s.k, self.router, self.d_logits,
+                          stream)
+            moe_unpermute_combine(s, self.dx_perm, self.inv_pos, None, self.dx, stream)
+            return self.dx, self.d_logits, self.grads
+        moe_unpermute_combine_bwd(s, dy, self.y_exp, self.inv_pos, self.topk_w,
                                   self.dy_perm, self.d_topk_w, stream)
         moe_route_bwd(logits, self.topk_ids, self.d_topk_w, s.k, self.router, self.d_logits,
                       stream)

@@ -57,14 +57,18 @@ def test_workspace_never_holds_a_merged_delta(lib):
         assert st == 0
         esz = 4 if cfg.dtype == "f32" else 2
         delta = cfg.E * 2 * cfg.I * cfg.H * esz   # one materialised W + B A for gate_up
-        # forward scratch is a tile list only; backward holds dH [N, 2I], two
-        # [N, r] and, for 16-bit layers, the float32 partials of the side
+        # forward scratch is a tile list only; backward holds dH [N, 2I], four
+        # [N, r] (G B_d, dH B_gu, and for the folded combine backward w u_d and
+        # w G B_d), for 16-bit layers the float32 partials of the side
         # products fused into the B gradients (one [N, r] per 256 features of
-        # the wider of H and 2I); these layers have experts enough for no
-        # split-K partials
+        # the wider of H and 2I), the routing weight per row and the dw
+        # partial sums (float32 [slots, N], a slot per 64 columns of I);
+        # these layers have experts enough for no split-K partials
         assert f < 1 << 20
         side = -(-max(cfg.H, 2 * cfg.I) // 256) * cfg.N * cfg.r * 4 if cfg.dtype != "f32" else 0
-        assert b <= cfg.N * (2 * cfg.I + 2 * cfg.r) * esz + side + (1 << 20)
+        slots = -(-cfg.I // 64) if cfg.dtype == "f32" else -(-cfg.I // 256) * 4
+        assert b <= (cfg.N * (2 * cfg.I + 4 * cfg.r) * esz + side + cfg.N * 4 * (1 + slots)
+                     + (1 << 20))
         if cfg.T * cfg.k < cfg.E * cfg.H:            # the regime the pages' memory model favours
             assert b < delta
         assert p > 0
