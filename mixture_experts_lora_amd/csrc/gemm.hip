@@ -753,69 +753,92 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
     // ---- Register-staged main loop: every wave loads its share of a k tile
     // into VGPRs (16 bytes per lane per 1 KB piece, the same lane offsets as
     // the DMA plans, out-of-range lanes read zeros) and writes it to the LDS
-    // slot the tile belongs to. Two LDS slots and NRB register buffers: tile
+    // slot the tile belongs to. Two LDS slots and one register buffer: tile
     // it+1 is written during tile it's second k-step (its slot was last read
-    // before the previous barrier), and the load of tile it+1+NRB is issued
-    // into the buffer just freed, so each load has NRB tiles of MFMAs to
-    // arrive. Buffer indices are compile-time (the tile loop is unrolled by
-    // NRB); the compiler's own waits on the loaded registers keep the other
-    // buffers' loads in flight.
-    constexpr int NRB = VST;
+    // before the previous barrier), and the load of tile it+2 is issued into
+    // the buffer just freed, so each load has a whole k tile of MFMAs to
+    // arrive. Tile 1 is loaded together with tile 0 into a prologue-only
+    // buffer (the accumulators hold nothing yet, so their registers are
+    // free): a block waits for one load latency before its first MFMA.
+    //
+    // The steady state (the tiles whose staged load is a whole in-range tile
+    // of the main segment) runs two tiles per iteration, so the LDS slot of
+    // every access is a compile-time constant: fragment reads and staging
+    // writes take their whole offset in the instruction's immediate field
+    // from loop-invariant per-lane bases, and the loads need no masking.
+    // The first tile, the tiles around the LoRA segment and the K tail, and
+    // the last tile take the general path (slot chosen at run time, loads
+    // masked).
+    static_assert(VST == 1, "one register buffer");
+    static_assert(NST == 2, "register staging uses two LDS slots");
     constexpr int KS = BK / 16;
     static_assert(KS % 2 == 0, "fragment double-buffering alternates per k-step");
-    static_assert(NRB == 1 || NRB == 2, "one or two register buffers");
-    static_assert(NST == 2, "register staging uses two LDS slots");
-    u32x4 ra[NRB][GA::NIW], rb[NRB][GB::NIW];
-    auto vload = [&](auto& P, int k0, u32x4* r, auto geo, bool live) __attribute__((always_inline)) {
-      typedef decltype(geo) G;
-      const bool kc = decltype(geo)::KCV;
-      const uint32_t soff = kc ? static_cast<uint32_t>(k0) * 2
-                               : static_cast<uint32_t>(static_cast<int64_t>(k0) * P.ld * 2);
+    u32x4 ra[GA::NIW], rb[GB::NIW];
+    // Buffer resource of a plan (wave-uniform: built in SGPRs).
+    auto make_rs = [&](const auto& P) __attribute__((always_inline)) {
       // readfirstlane returns int: widen through uint32_t, never by sign extension
       const uint64_t base = reinterpret_cast<uint64_t>(P.base);
       const uint64_t lo = static_cast<uint32_t>(
           __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base)));
       const uint64_t hi = static_cast<uint32_t>(
           __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base >> 32)));
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          reinterpret_cast<void*>((hi << 32) | lo), static_cast<short>(0),
-          __builtin_amdgcn_readfirstlane(P.nrec), 0x00020000);
-      const bool tail = kc && (k0 + BK > P.klim);
+      return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((hi << 32) | lo),
+                                               static_cast<short>(0),
+                                               __builtin_amdgcn_readfirstlane(P.nrec), 0x00020000);
+    };
+    __amdgpu_buffer_rsrc_t rsa = make_rs(pa0), rsb = make_rs(pb0);
+    // CLEAN: the tile is a whole, in-range tile of the current plans (no
+    // masking, every lane's offset as planned)
+    auto vload = [&](auto& P, const __amdgpu_buffer_rsrc_t& rs, int k0, u32x4* r, auto geo,
+                     bool live, auto cleanc) __attribute__((always_inline)) {
+      typedef decltype(geo) G;
+      constexpr bool CLEAN = decltype(cleanc)::value;
+      const bool kc = decltype(geo)::KCV;
+      const uint32_t soff = kc ? static_cast<uint32_t>(k0) * 2
+                               : static_cast<uint32_t>(static_cast<int64_t>(k0) * P.ld * 2);
+      const bool tail = !CLEAN && kc && (k0 + BK > P.klim);
 #pragma unroll
       for (int i = 0; i < G::NIW; ++i) {
         const int j = wave + NW * i;
         if (G::TI % NW == 0 || j < G::TI) {
-          uint32_t vo = live ? P.vo[i] : kOOB;
-          if (tail) {
-            const int rr = G::RPI * j + lane / G::CPR;
-            const int c = (lane % G::CPR) ^ kswz<BK>(rr);
-            if (k0 + c * 8 >= P.klim) vo = kOOB;
+          uint32_t vo = P.vo[i];
+          if constexpr (!CLEAN) {
+            if (!live) vo = kOOB;
+            if (tail) {
+              const int rr = G::RPI * j + lane / G::CPR;
+              const int c = (lane % G::CPR) ^ kswz<BK>(rr);
+              if (k0 + c * 8 >= P.klim) vo = kOOB;
+            }
           }
           r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, __builtin_amdgcn_readfirstlane(soff), 0);
         }
       }
     };
-    // Branch-free issue. A k-step without branches lets the staging stores
-    // and loads interleave with its MFMAs, and with two register buffers the
-    // compiler's waits for a tile's loads count the next tile's loads as
-    // still in flight only if every path issues the same loads (its
-    // in-order load counter is otherwise merged conservatively). So: the
-    // plans switch to the LoRA segment's once, before its first tile is
-    // loaded (tiles are loaded in order), and live = false issues the loads
-    // with every lane out of range (they return zeros and touch no memory)
-    // instead of skipping them.
+    // Branch-free issue: the plans switch to the LoRA segment's once, before
+    // its first tile is loaded (tiles are loaded in order), and live = false
+    // issues the loads with every lane out of range (they return zeros and
+    // touch no memory) instead of skipping them, so every path issues the
+    // same loads and the compiler's waits stay exact.
     auto switch_plans = [&]() __attribute__((always_inline)) {
       pa0 = pa1;
       pb0 = pb1;
+      rsa = make_rs(pa0);
+      rsb = make_rs(pb0);
     };
-    auto load_tile = [&](int j, u32x4* a, u32x4* b, bool live = true) __attribute__((always_inline)) {
+    auto load_tile = [&](int j, u32x4* a, u32x4* b, bool live, auto cleanc) __attribute__((always_inline)) {
       const int k0 = (j >= nk0 ? j - nk0 : j) * BK;
-      vload(pa0, k0, a, GeoK<GA, A_KC>(), live);
-      vload(pb0, k0, b, GeoK<GB, B_KC>(), live);
+      vload(pa0, rsa, k0, a, GeoK<GA, A_KC>(), live, cleanc);
+      vload(pb0, rsb, k0, b, GeoK<GB, B_KC>(), live, cleanc);
     };
-    auto store_tile = [&](int j, const u32x4* a, const u32x4* b) __attribute__((always_inline)) {
-      char* sa = smem + (j % NST) * ST;
-      char* sb = sa + A_BYTES;
+    // LDS layout [A slot 0 | A slot 1 | B slot 0 | B slot 1]: every access of
+    // a slot lies within 64 KB of its operand's region start, so a per-lane
+    // base register plus the instruction's immediate offset reaches it.
+    constexpr int B_REGION = 2 * A_BYTES;
+    static_assert(A_BYTES <= 32768 && B_BYTES <= 32768, "slot offsets fit the DS immediate");
+    // slot: LDS slot (0 or 1) the tile goes to
+    auto store_tile = [&](int slot, const u32x4* a, const u32x4* b) __attribute__((always_inline)) {
+      char* sa = smem + slot * A_BYTES;
+      char* sb = smem + B_REGION + slot * B_BYTES;
 #pragma unroll
       for (int i = 0; i < GA::NIW; ++i) {
         const int jj = wave + NW * i;
@@ -829,191 +852,169 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
           *reinterpret_cast<u32x4*>(sb + jj * 1024 + 16 * lane) = b[i];
       }
     };
-    bf16x8 af[NRB >= 2 ? 1 : 2][MF], bf[NRB >= 2 ? 1 : 2][NF];
-    // With one register buffer, tile 1 is loaded into a buffer of its own
-    // together with tile 0 (the accumulators hold nothing yet, so their
-    // registers are free), and the first k tile stores it from there: a
-    // block waits for one load latency before its first MFMA, not two.
-    constexpr bool T1 = NRB == 1;
-    u32x4 ta[T1 ? GA::NIW : 1], tb[T1 ? GB::NIW : 1];
-    if (nk > 0) {
-      if (nk0 == 0) switch_plans();
-      load_tile(0, ra[0], rb[0]);
-      if constexpr (T1) {
-        if (1 == nk0) switch_plans();
-        load_tile(1, ta, tb, 1 < nk);
-        store_tile(0, ra[0], rb[0]);
+    bf16x8 af[2][MF], bf[2][NF];
+    // Fragment addresses: per-lane bases (per k-step for k-contiguous tiles,
+    // per fragment for output-contiguous ones, which advance by a constant
+    // per k-step) plus compile-time offsets. The wave's own row/column offset
+    // sits in the base; the fragment index and the slot are immediates.
+    // k-contiguous: base_k[ks] + (fr_base[f] - fr_base[0]) * BK * 2
+    // output-contiguous: base_f[f] + ks * 16 * ROWS * 2 (+ 4 * ROWS * 2)
+    const char* abase[A_KC ? KS : MF];
+    const char* bbase[B_KC ? KS : NF];
+#pragma unroll
+    for (int q = 0; q < (A_KC ? KS : MF); ++q)
+      abase[q] = smem + (A_KC ? fa_base[0] * BK * 2 + FA.off[q] : FA.off[q]);
+#pragma unroll
+    for (int q = 0; q < (B_KC ? KS : NF); ++q)
+      bbase[q] = smem + B_REGION + (B_KC ? fb_base[0] * BK * 2 + FB.off[q] : FB.off[q]);
+    // compile-time fragment offsets relative to fragment 0 (they depend on
+    // the wave only through fr_base[0])
+    auto frag_rd = [&](const char* const* base, auto kcc, auto rowsc, int f, int frel, int ks,
+                       int slot_off) __attribute__((always_inline)) {
+      constexpr bool KC = decltype(kcc)::value;
+      constexpr int ROWS = decltype(rowsc)::value;
+      if constexpr (KC) {
+        return *reinterpret_cast<const bf16x8*>(base[ks] + slot_off + frel * BK * 2);
       } else {
-        store_tile(0, ra[0], rb[0]);
-#pragma unroll
-        for (int q = 1; q <= NRB; ++q) {
-          if (q == nk0) switch_plans();
-          if (q < nk) load_tile(q, ra[q % NRB], rb[q % NRB]);
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int mi = 0; mi < MF; ++mi) af[0][mi] = read_frag<BM, BK, A_KC, MF>(smem, FA, mi, fa_base[mi], 0);
-#pragma unroll
-      for (int ni = 0; ni < NF; ++ni) bf[0][ni] = read_frag<BN, BK, B_KC, NF>(smem + A_BYTES, FB, ni, fb_base[ni], 0);
-    }
-    // one k tile; tile it+1 sits in register buffer BUF = (it + 1) % NRB.
-    // MFMA = false: the wave's rows are all past the tile's valid rows (the
-    // ragged last tile of an expert); it still loads, stores and meets every
-    // barrier, but issues no MFMAs.
-    // With two register buffers (NRB = 2) the fragments are single-buffered
-    // (FSB): the next k-step's fragments are read after this k-step's MFMAs,
-    // and the other wave of the SIMD covers that LDS latency. This frees the
-    // registers of the second buffer.
-    constexpr bool FSB = NRB >= 2;
-    auto next_frags = [&](int it, int ks, int dst, int ns, auto mfmac) __attribute__((always_inline)) {
-      constexpr bool RD = decltype(mfmac)::value;  // only waves that multiply read fragments
-      const char* sa = smem + (it % NST) * ST;
-      if (!RD) {
-        if (ks + 1 >= ns && it + 1 < nk) barrier_lds();
-      } else if (ks + 1 < ns) {
-#pragma unroll
-        for (int mi = 0; mi < MF; ++mi)
-          af[dst][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
-#pragma unroll
-        for (int ni = 0; ni < NF; ++ni)
-          bf[dst][ni] = read_frag<BN, BK, B_KC, NF>(sa + A_BYTES, FB, ni, fb_base[ni], ks + 1);
-      } else if (it + 1 < nk) {
-        // every wave has read all of tile it and written tile it+1
-        barrier_lds();
-        const char* na = smem + ((it + 1) % NST) * ST;
-#pragma unroll
-        for (int mi = 0; mi < MF; ++mi)
-          af[dst][mi] = read_frag<BM, BK, A_KC, MF>(na, FA, mi, fa_base[mi], 0);
-#pragma unroll
-        for (int ni = 0; ni < NF; ++ni)
-          bf[dst][ni] = read_frag<BN, BK, B_KC, NF>(na + A_BYTES, FB, ni, fb_base[ni], 0);
+        const char* q = base[f] + slot_off + ks * 16 * ROWS * 2;
+        v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(q));
+        v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(q + 4 * ROWS * 2));
+        v8s r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, r);
       }
     };
+    auto read_frags = [&](int slot, int ks, int dst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int mi = 0; mi < MF; ++mi)
+        af[dst][mi] = frag_rd(abase, std::integral_constant<bool, A_KC>(),
+                              std::integral_constant<int, BM>(), mi, mi * 32, ks, slot * A_BYTES);
+#pragma unroll
+      for (int ni = 0; ni < NF; ++ni) {
+        // fr_base[ni] - fr_base[0]: compile time (paired: gate fragments, then up ones)
+        const int frel = PAIRED ? (ni < NF / 2 ? ni * 32 : BN / 2 + (ni - NF / 2) * 32) : ni * 32;
+        bf[dst][ni] = frag_rd(bbase, std::integral_constant<bool, B_KC>(),
+                              std::integral_constant<int, BN>(), ni, frel, ks, slot * B_BYTES);
+      }
+    };
+    u32x4 ta[GA::NIW], tb[GB::NIW];  // tile 1, prologue only
+    if (nk > 0) {
+      if (nk0 == 0) switch_plans();
+      load_tile(0, ra, rb, true, std::false_type());
+      if (1 == nk0) switch_plans();
+      load_tile(1, ta, tb, 1 < nk, std::false_type());
+      store_tile(0, ra, rb);
+      __syncthreads();
+      read_frags(0, 0, 0);
+    }
     // k-steps of the last tile holding valid k (the rest of it is zeros)
     const int klast = MODE == GROUP_M ? (nk1 > 0 ? p.K[1] - (nk1 - 1) * BK : p.K[0] - (nk0 - 1) * BK)
                                       : krows - (nk0 - 1) * BK;
     const int ns_last = (klast + 15) / 16;
-    // NS k-steps of the tile are multiplied; LAST: the last tile, which
+    // One k tile. PAR: the tile's LDS slot when known at compile time (-1:
+    // it % 2 at run time). MFMA = false: the wave's rows or columns all lie
+    // past the valid ones; it still loads, stores and meets every barrier,
+    // but issues no MFMAs and reads no fragments. LAST: the last tile, which
     // stages and loads nothing and leaves its k-step loop after the k-steps
     // that hold valid k (a LoRA segment of rank 16 fills one of a 64-wide
-    // tile's four; the rest is zeros). One path with early exits, so the
-    // accumulators stay in place.
-    auto ktile = [&](int it, auto bufc, auto mfmac, auto nsc, auto lastc,
-                     auto firstc) __attribute__((always_inline)) {
-      constexpr bool FIRST = decltype(firstc)::value;
-      static_assert(!FIRST || T1, "the first tile's own buffer exists with one register buffer");
-      constexpr int BUF = decltype(bufc)::value;
+    // tile's four; the rest is zeros); one path with early exits, so the
+    // accumulators stay in place. FIRST: tile 1 is stored from the prologue
+    // buffer. CLEAN: the load this tile issues (tile it+2) is a whole,
+    // in-range tile of the plans already in place.
+    auto ktile = [&](int it, auto parc, auto mfmac, auto lastc, auto firstc,
+                     auto cleanc) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(parc)::value;
       constexpr bool MFMA = decltype(mfmac)::value;
-      constexpr int NS = decltype(nsc)::value;
       constexpr bool LAST = decltype(lastc)::value;
-      static_assert(NS >= 1 && NS <= KS && (LAST || NS == KS), "k-steps of a tile");
-      const char* sa = smem + (it % NST) * ST;
-      const char* sb = sa + A_BYTES;
-      // the tile loaded in this k tile is it+1+NRB
-      if (it + 1 + NRB == nk0) switch_plans();
+      constexpr bool FIRST = decltype(firstc)::value;
+      constexpr bool CLEAN = decltype(cleanc)::value;
+      const int slot = PAR >= 0 ? PAR : (it & 1);
+      if (!CLEAN && it + 2 == nk0) switch_plans();  // the tile loaded here is it+2
 #pragma unroll
-      for (int ks = 0; ks < NS; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         if constexpr (LAST) {
           if (ks >= ns_last) break;
         }
-        const int cur = FSB ? 0 : ks & 1;
-        if constexpr (FSB) {
-        } else if (ks + 1 < NS) {
-          if constexpr (MFMA) {
-#pragma unroll
-            for (int mi = 0; mi < MF; ++mi)
-              af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(sa, FA, mi, fa_base[mi], ks + 1);
-#pragma unroll
-            for (int ni = 0; ni < NF; ++ni)
-              bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(sb, FB, ni, fb_base[ni], ks + 1);
-          }
+        const int cur = ks & 1;
+        if (ks + 1 < KS) {
+          if constexpr (MFMA) read_frags(slot, ks + 1, cur ^ 1);
         } else if (!LAST && it + 1 < nk) {
           // Before the last k-step's MFMAs: every wave has read all of tile
           // it (its slot may be refilled next) and has written tile it+1, so
           // one barrier covers both, and the first fragment reads of tile
           // it+1 overlap this k-step's MFMAs.
           barrier_lds();
-          if constexpr (MFMA) {
-            const char* na = smem + ((it + 1) % NST) * ST;
-#pragma unroll
-            for (int mi = 0; mi < MF; ++mi)
-              af[cur ^ 1][mi] = read_frag<BM, BK, A_KC, MF>(na, FA, mi, fa_base[mi], 0);
-#pragma unroll
-            for (int ni = 0; ni < NF; ++ni)
-              bf[cur ^ 1][ni] = read_frag<BN, BK, B_KC, NF>(na + A_BYTES, FB, ni, fb_base[ni], 0);
-          }
+          if constexpr (MFMA) read_frags(slot ^ 1, 0, cur ^ 1);
         }
         // tile it+1's slot was last read in tile it-1, before the last barrier
         if (!LAST && ks == 1) {
           // past the last tile this stores the zeros of an out-of-range
           // load into a slot nobody reads again
-          if constexpr (FIRST) store_tile(it + 1, ta, tb);
-          else store_tile(it + 1, ra[BUF], rb[BUF]);
-          const int jn = it + 1 + NRB;
-          load_tile(min(jn, nk - 1), ra[BUF], rb[BUF], jn < nk);
+          if constexpr (FIRST) store_tile(slot ^ 1, ta, tb);
+          else store_tile(slot ^ 1, ra, rb);
+          const int jn = it + 2;
+          if constexpr (CLEAN) load_tile(jn, ra, rb, true, std::true_type());
+          else load_tile(min(jn, nk - 1), ra, rb, jn < nk, std::false_type());
         }
         if constexpr (MFMA) {
           // Instruction order within the k-step, by measurement: one LDS read
           // after each MFMA, and in the staging k-step the stores and loads
-          // early, two of each after each of the first four MFMAs (2-7% faster
-          // per GEMM than the compiler's own order or its MFMA/LDS
-          // interleaving strategy).
+          // early, two of each after each of the first four MFMAs.
 #pragma unroll
           for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
             for (int ni = 0; ni < NF; ++ni)
               acc[mi][ni] = mfma32<F16>(bf[cur][ni], af[cur][mi], acc[mi][ni]);
-          {
-            if (!LAST && ks == 1) {  // the staging stores and loads early in the k-step
+          if (!LAST && ks == 1) {
 #pragma unroll
-              for (int i = 0; i < MF * NF / 2; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // two LDS writes
-                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // two buffer loads
-              }
+            for (int i = 0; i < MF * NF / 2; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+              __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // two LDS writes
+              __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // two buffer loads
+            }
 #pragma unroll
-              for (int i = 0; i < MF * NF / 2; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
-              }
-            } else {
+            for (int i = 0; i < MF * NF / 2; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+            }
+          } else {
 #pragma unroll
-              for (int i = 0; i < MF * NF; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-              }
+            for (int i = 0; i < MF * NF; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
             }
           }
         }
-        if constexpr (FSB) next_frags(it, ks, 0, NS, mfmac);
+        // Each k-step is a scheduling region of its own: otherwise the
+        // scheduler fills the groups above with MFMAs of the next k-step,
+        // putting two MFMAs on one accumulator back to back (a dependent
+        // 32x32x16 MFMA issues after about 52 cycles instead of 32).
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     // The wave-uniform choice is made once, outside the k loop, so the loop
     // itself has no extra branch.
     auto kloop = [&](auto mfmac) __attribute__((always_inline)) {
-      using Full = std::integral_constant<int, KS>;
+      using Yes = std::true_type;
       using No = std::false_type;
+      using Rt = std::integral_constant<int, -1>;
       const int nkf = nk - 1;  // full tiles before the last
-      if constexpr (NRB >= 2) {
-        // pairs of tiles, so that the buffer index is compile-time; the odd
-        // tile is peeled rather than branched around inside the loop
-        int it = 0;
-        for (; it + 1 < nkf; it += 2) {
-          ktile(it, std::integral_constant<int, 1>(), mfmac, Full(), No(), No());
-          ktile(it + 1, std::integral_constant<int, 0>(), mfmac, Full(), No(), No());
-        }
-        if (it < nkf) ktile(it, std::integral_constant<int, 1>(), mfmac, Full(), No(), No());
-      } else {
-        using B0 = std::integral_constant<int, 0>;
-        if (nkf > 0) ktile(0, B0(), mfmac, Full(), No(), std::true_type());
-        for (int it = 1; it < nkf; ++it) ktile(it, B0(), mfmac, Full(), No(), No());
+      // Tiles 1..C are clean: the tile each stages (it + 2) is a whole tile
+      // of the main segment (K tail tile excluded).
+      const int last_clean = MODE == GROUP_M ? nk0 - 1 - (p.K[0] % BK != 0 ? 1 : 0) : -1;
+      const int C = min(nkf - 1, last_clean - 2);
+      if (nkf > 0) ktile(0, Rt(), mfmac, No(), Yes(), No());
+      int it = 1;
+      for (; it + 1 <= C; it += 2) {
+        ktile(it, std::integral_constant<int, 1>(), mfmac, No(), No(), Yes());
+        ktile(it + 1, std::integral_constant<int, 0>(), mfmac, No(), No(), Yes());
       }
-      if (nk > 0) {
-        using Yes = std::true_type;
-        using B0 = std::integral_constant<int, 0>;
-        ktile(nkf, B0(), mfmac, Full(), Yes(), No());
+      if (it <= C) {
+        ktile(it, std::integral_constant<int, 1>(), mfmac, No(), No(), Yes());
+        ++it;
       }
+      for (; it < nkf; ++it) ktile(it, Rt(), mfmac, No(), No(), No());
+      if (nk > 0) ktile(nkf, Rt(), mfmac, Yes(), No(), No());
     };
     // Waves whose rows all lie past the tile's valid rows, or whose columns
     // all lie past the valid columns, neither read fragments nor multiply.
