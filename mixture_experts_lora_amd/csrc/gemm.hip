@@ -67,7 +67,7 @@ struct GemmArgs {
   int M, N;         // GROUP_K: output extent; GROUP_M: N = output columns (features)
   int E;
   const int32_t* offsets;  // [E+1]
-  const int4* tiles;       // GROUP_M: {expert, first row, valid rows, -}
+  const int4* tiles;       // GROUP_M: {expert, first row, valid rows, raster group}
   const int32_t* ntiles;   // GROUP_M: number of M tiles (device)
   int ntn;                 // number of N tiles
   int ntm;                 // GROUP_K: number of M tiles
@@ -103,6 +103,21 @@ struct GemmArgs {
 __device__ __forceinline__ int xcd_remap(int b, int total) {
   const int x = b & 7, j = b >> 3, q = total >> 3, rem = total & 7;
   return x * q + (x < rem ? x : rem) + j;
+}
+
+// Tile-list entries are {expert, first row, valid rows, group}: an expert's M
+// tiles form groups of at most 8 consecutive entries, and `group` holds the
+// group's first entry times 16 plus its size. Logical tiles L = gs * ntn ..
+// (gs + gsz) * ntn - 1 belong to the group starting at entry gs, M tile
+// fastest, so L / ntn is always one of that group's entries. Returns the
+// entry of logical tile L and sets its N tile.
+constexpr int kTileGroup = 8;
+__device__ __forceinline__ int group_tile(const int4* tiles, int L, int ntn, int& n_tile) {
+  const int g = tiles[L / ntn].w;
+  const int gs = g >> 4, gsz = g & 15;
+  const int rem = L - gs * ntn;
+  n_tile = rem / gsz;
+  return gs + rem % gsz;
 }
 
 // One operand of one tile: where element (mn, k) lives and which ones exist.
@@ -589,17 +604,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
     const int mtot = *p.ntiles;
     const int total = mtot * p.ntn;
     if (static_cast<int>(blockIdx.x) >= total) return;
-    // XCD-contiguous ranges, then groups of 8 M tiles swept across all N tiles,
-    // so the tiles an XCD runs together share A rows and weight columns in L2.
+    // XCD-contiguous ranges, then groups of up to 8 M tiles of one expert
+    // swept across all N tiles, so the tiles an XCD runs together share A
+    // rows and the expert's weight columns in L2.
     const int L = xcd_remap(blockIdx.x, total);
-    constexpr int GM = 8;
-    const int mg = L / (GM * p.ntn);
-    const int gbase = mg * GM;
-    const int gsz = min(GM, mtot - gbase);
-    const int rem = L - gbase * p.ntn;
-    n_tile = rem / gsz;
-    const int mt = gbase + rem % gsz;
-    const int4 t = p.tiles[mt];
+    const int4 t = p.tiles[group_tile(p.tiles, L, p.ntn, n_tile)];
     e = t.x;
     row0 = t.y;
     rows = t.z;
@@ -1434,8 +1443,8 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs p) {
 
 // ----------------------------------------------------------------- tile list
 // One block of 1024 threads (E <= 1024). Two lists in one launch, for two tile
-// heights: M tiles of `bm` rows per expert, in expert order; empty experts get
-// none.
+// heights: M tiles of `bm` rows per expert, in expert order, with their raster
+// groups (group_tile); empty experts get none.
 __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                      int bm0, int4* __restrict__ tiles0,
                                                      int32_t* __restrict__ ntiles0, int bm1,
@@ -1470,7 +1479,9 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
     base += incl - nt;
     for (int i = 0; i < nt; ++i) {
       const int r = i * bm;
-      tiles[base + i] = make_int4(e, lo + r, min(bm, cnt - r), 0);
+      const int g0 = i / kTileGroup * kTileGroup;
+      const int grp = (base + g0) * 16 + min(kTileGroup, nt - g0);
+      tiles[base + i] = make_int4(e, lo + r, min(bm, cnt - r), grp);
     }
     if (threadIdx.x == 0) *(l ? ntiles1 : ntiles0) = total;
   }
