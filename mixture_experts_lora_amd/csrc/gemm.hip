@@ -2373,10 +2373,189 @@ hipError_t launch_router_bwd(const float* d_logits, const void* w_r, int T, int 
 }
 
 // ----------------------------------------------------------------- merged export
-// W'[e] = W[e] + s B[e] A[e] for both stacked projections, as grouped GEMMs
-// whose "tokens" are the output rows of each expert's weight (2I for gate_up,
-// H for down; K = r) and whose epilogue adds the base weight read from aux.
+// W'[e] = W[e] + s B[e] A[e] for both stacked projections. 16-bit layers use
+// merge_kernel below; float32 layers a grouped GEMM whose "tokens" are the
+// output rows of each expert's weight (2I for gate_up, H for down; K = r) and
+// whose epilogue adds the base weight read from aux.
 namespace {
+
+// One stacked projection, 16-bit layers: W [E][R][C], B [E][R][r],
+// A [E][r][C]. One block of four waves per 64-row x 256-column tile of an
+// expert's W (grid: x = row tile * ntc + column tile, y = expert); wave w
+// takes columns 64w .. 64w+63. The pass is bound by streaming W in and W' out,
+// so each wave first issues the rank-r operand loads (small, L2-resident),
+// then all of its base-weight loads (8 rows x 64 columns per instruction,
+// 16 bytes a lane), and only then waits for the operands: the base weight
+// arrives while the product runs on MFMA (k = 16 per step, zero past r). The
+// product goes through the wave's own LDS tile, 32 rows at a time, so each
+// lane ends with 8 consecutive elements of a row: W' = W + s (B A) as one
+// float32 sum, rounded once, stored in 16 bytes. VEC: C % 8 == 0 and W, W'
+// 16-byte aligned; otherwise every W / W' element is accessed on its own. W'
+// may be W itself: each element is read and written by the same lane.
+constexpr int kMergeRows = 64, kMergeCols = 256, kMergeLd = 72;
+
+template <bool F16, bool VEC, int KS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? (KS < 4 ? 4 : 2)
+                                                                          : (KS < 2 ? 4 : 2))))
+void merge_kernel(const bf16_t* W, const bf16_t* __restrict__ Bm,
+                  const bf16_t* __restrict__ Am, bf16_t* out, int R, int C, int r, int ntc,
+                  float scale, bool avec, bool bvec) {
+  // row stride 72 floats: the two half-waves of a fragment store (rows i and
+  // i + 4) fall on disjoint banks
+  __shared__ float P[4][32][kMergeLd];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rt = blockIdx.x / ntc, ct = blockIdx.x - rt * ntc;
+  const int row0 = rt * kMergeRows;
+  const int col0 = ct * kMergeCols + wave * 64;
+  if (col0 >= C) return;  // wave-uniform; the kernel has no block barrier
+  const int64_t e = blockIdx.y;
+  const bf16_t* We = W + e * R * C;
+  bf16_t* Oe = out + e * R * C;
+  const uint16_t* Be = reinterpret_cast<const uint16_t*>(Bm) + e * R * r;
+  const uint16_t* Ae = reinterpret_cast<const uint16_t*>(Am) + e * r * C;
+  const int li = lane & 31, lk = (lane >> 5) * 8;
+
+  // Rank-r operands of all k steps (KS of them cover r, zero past r). A-side
+  // fragments are B's rows (the product's rows): 16-byte loads when bvec. The
+  // B-side fragments need 8 consecutive k of one column of A ([r][C]), so the
+  // wave's 64 columns of A are loaded by rows (16 bytes a lane when avec) and
+  // written transposed into the wave's LDS tile, At[column][k], from which
+  // each fragment is one 16-byte read. The same LDS later holds the product.
+  const int ks_n = (r + 15) / 16;
+  uint16_t (*At)[kMergeLd] = reinterpret_cast<uint16_t (*)[kMergeLd]>(P[wave]);
+  u32x4 ach[2 * KS];
+#pragma unroll
+  for (int i = 0; i < 2 * KS; ++i) {  // chunk m: k = m / 8, columns 8 (m % 8) .. + 7
+    const int m = i * 64 + lane, k = m >> 3, c = col0 + (m & 7) * 8;
+    const uint16_t* src = Ae + static_cast<int64_t>(k) * C + c;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (i < 2 * ks_n && k < r && c < C) {
+      if (avec) {
+        v = *reinterpret_cast<const u32x4*>(src);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = src[2 * t] | (static_cast<uint32_t>(src[2 * t + 1]) << 16);
+      }
+    }
+    ach[i] = v;
+  }
+  u32x4 fa[KS][2], fb[KS][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int n = row0 + 32 * f + li, k0 = ks * 16 + lk;
+      const uint16_t* src = Be + static_cast<int64_t>(n) * r + k0;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ks < ks_n && n < R) {
+        if (bvec) {
+          if (k0 < r) v = *reinterpret_cast<const u32x4*>(src);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t lo = k0 + 2 * t < r ? src[2 * t] : 0u;
+            const uint32_t hi = k0 + 2 * t + 1 < r ? src[2 * t + 1] : 0u;
+            v[t] = lo | (hi << 16);
+          }
+        }
+      }
+      fa[ks][f] = v;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // base weight: load j covers rows 8j .. 8j+7 of the tile, lane -> row
+  // 8j + lane/8, columns lc .. lc+7
+  const int lr = lane >> 3, lc = col0 + (lane & 7) * 8;
+  u32x4 wv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = row0 + 8 * j + lr;
+    const bf16_t* src = We + static_cast<int64_t>(row) * C + lc;
+    if constexpr (VEC) {
+      wv[j] = row < R && lc < C ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src))
+                                : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      uint32_t v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t lo = row < R && lc + 2 * t < C ? src[2 * t] : 0u;
+        const uint32_t hi = row < R && lc + 2 * t + 1 < C ? src[2 * t + 1] : 0u;
+        v[t] = lo | (hi << 16);
+      }
+      wv[j] = u32x4{v[0], v[1], v[2], v[3]};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // At: every chunk of k steps below ks_n is written (zeros past r)
+#pragma unroll
+  for (int i = 0; i < 2 * KS; ++i) {
+    if (i < 2 * ks_n) {
+      const int m = i * 64 + lane, k = m >> 3, cl = (m & 7) * 8;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        At[cl + 2 * t][k] = static_cast<uint16_t>(ach[i][t] & 0xffffu);
+        At[cl + 2 * t + 1][k] = static_cast<uint16_t>(ach[i][t] >> 16);
+      }
+    }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      fb[ks][g] = ks < ks_n ? *reinterpret_cast<const u32x4*>(&At[32 * g + li][ks * 16 + lk])
+                            : u32x4{0u, 0u, 0u, 0u};
+
+  float (*Pw)[kMergeLd] = P[wave];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x16 acc[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[g][q] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      if (ks < ks_n)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          acc[g] = mfma32<F16>(__builtin_bit_cast(bf16x8, fa[ks][h]),
+                               __builtin_bit_cast(bf16x8, fb[ks][g]), acc[g]);
+    wave_lds_sync();  // the At reads (h = 0) or the previous half's reads are done
+    // acc[g] register q: product row 8(q/4) + 4(lane/32) + q%4 of this
+    // half, column 32g + lane%32 of the wave's 64
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        Pw[8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)][32 * g + li] = scale * acc[g][q];
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rl = 8 * j + lr, row = row0 + 32 * h + rl;
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(&Pw[rl][(lane & 7) * 8]);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(&Pw[rl][(lane & 7) * 8 + 4]);
+      float v[8];
+      unpack8<F16>(wv[4 * h + j], v);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[t] += p0[t];
+        v[4 + t] += p1[t];
+      }
+      if (row >= R) continue;
+      bf16_t* dst = Oe + static_cast<int64_t>(row) * C + lc;
+      if constexpr (VEC) {
+        if (lc < C) store8<F16>(dst, v);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (lc + t < C) dst[t] = f32_to_h16<F16>(v[t]);
+      }
+    }
+  }
+}
 
 __global__ void uniform_offsets_kernel(int32_t* off, int E, int rows) {
   for (int e = threadIdx.x; e <= E; e += blockDim.x) off[e] = e * rows;
@@ -2407,6 +2586,26 @@ ExpertDims merge_dims(const ExpertDims& d, int rows) {
 
 hipError_t merge_one(const ExpertDims& d, int rows, int cols, const void* w, const void* a,
                      const void* b, void* out, void* ws, hipStream_t s) {
+  if (d.dtype != MOE_F32) {
+    const int64_t ntc = ceil_div(cols, kMergeCols), nt = ceil_div(rows, kMergeRows) * ntc;
+    if (nt > INT32_MAX || d.r > 64) return hipErrorInvalidValue;
+    const bool vec = cols % 8 == 0 && aligned16(w) && aligned16(out);
+    const bool f16 = d.dtype == MOE_F16;
+    auto pick = [&](auto ks) {
+      constexpr int KS = decltype(ks)::value;
+      return f16 ? (vec ? merge_kernel<true, true, KS> : merge_kernel<true, false, KS>)
+                 : (vec ? merge_kernel<false, true, KS> : merge_kernel<false, false, KS>);
+    };
+    auto kern = d.r <= 16   ? pick(std::integral_constant<int, 1>())
+                : d.r <= 32 ? pick(std::integral_constant<int, 2>())
+                            : pick(std::integral_constant<int, 4>());
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nt), d.E), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(w), static_cast<const bf16_t*>(b),
+                       static_cast<const bf16_t*>(a), static_cast<bf16_t*>(out), rows, cols, d.r,
+                       static_cast<int>(ntc), d.scale, aligned16(a),
+                       d.r % 8 == 0 && aligned16(b));
+    return hipGetLastError();
+  }
   const ExpertDims m = merge_dims(d, rows);
   const MergeWs M = merge_ws(ws, m);
   hipLaunchKernelGGL(uniform_offsets_kernel, dim3(1), dim3(256), 0, s, M.offsets, d.E, rows);
@@ -2430,11 +2629,6 @@ hipError_t merge_one(const ExpertDims& d, int rows, int cols, const void* w, con
   g.ld_aux = cols;
   g.scale = d.scale;
   const int grid_m = static_cast<int>(tile_cap(m.N, d.E, M.L.small.bm));
-  if (d.dtype != MOE_F32) {
-    g.ntn = ceil_div(cols, 256);
-    return launch(GEMM16(g.dtype, 128, 256, 64, 128, 32, 3, 2, GROUP_M, EPI_ADD, false, true, false, 0),
-                  grid_m * g.ntn, g, s);
-  }
   g.ntn = ceil_div(cols, 64);
   return launch(gemm_f32<GROUP_M, EPI_ADD, false>, grid_m * g.ntn, g, s);
 }

@@ -100,6 +100,36 @@ def test_merged_weights_reproduce_the_layer(name):
     close("Y merged vs split", to_numpy(yb), to_numpy(ya), TOL[cfg.dtype])
 
 
+def _unaligned(t):
+    """A contiguous copy of t whose data starts 2 bytes past a 16-byte boundary."""
+    buf = torch.empty(t.numel() + 8, device=t.device, dtype=t.dtype)
+    v = buf[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 == 2
+    return v
+
+
+@pytest.mark.parametrize("name", ["mini-bf16", "mini-skew", "mini-r64", "mini-f16", "mini-r1"])
+def test_merge_unaligned_weights(name):
+    """Base weights and outputs that cannot be read in 16-byte pieces take the
+    element-wise path: same results bit for bit, and within one ulp of the oracle."""
+    mel = _mel()
+    cfg = PARITY_CONFIGS[name]
+    say(f"[merge unaligned] {name}")
+    inp = make_inputs(cfg, 24, device="cuda", with_dy=False)
+    ref_out, ws = _merge(mel, cfg, inp)
+    w = {n: inp[n] for n in WEIGHTS}
+    w["w_gu"], w["w_d"] = _unaligned(inp["w_gu"]), _unaligned(inp["w_d"])
+    out = {n: _unaligned(torch.full_like(inp[n], float("nan"))) for n in ("w_gu", "w_d")}
+    mel.moe_merge_lora(mel.Shape.of(cfg), w, out["w_gu"], out["w_d"], ws)
+    torch.cuda.synchronize()
+    h = {n: to_numpy(inp[n]) for n in WEIGHTS}
+    ref = oracle.merge_lora(h, cfg.lora_scale)
+    for n in ("w_gu", "w_d"):
+        assert torch.equal(out[n], ref_out[n]), n
+        _check(n, to_numpy(out[n]), ref[n], cfg.dtype)
+
+
 def test_full_size_merge():
     """gpt-oss-20b-shaped weights: merged on the GPU, sampled experts against the oracle."""
     mel = _mel()
