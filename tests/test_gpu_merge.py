@@ -109,17 +109,19 @@ def _unaligned(t):
     return v
 
 
+@pytest.mark.parametrize("which", ["base", "all"])
 @pytest.mark.parametrize("name", ["mini-bf16", "mini-skew", "mini-r64", "mini-f16", "mini-r1"])
-def test_merge_unaligned_weights(name):
-    """Base weights and outputs that cannot be read in 16-byte pieces take the
-    element-wise path: same results bit for bit, and within one ulp of the oracle."""
+def test_merge_unaligned_weights(name, which):
+    """Base weights and outputs (and with "all" the LoRA factors too) that
+    cannot be read in 16-byte pieces take the element-wise paths: same results
+    bit for bit, and within one ulp of the oracle."""
     mel = _mel()
     cfg = PARITY_CONFIGS[name]
-    say(f"[merge unaligned] {name}")
+    say(f"[merge unaligned] {name} {which}")
     inp = make_inputs(cfg, 24, device="cuda", with_dy=False)
     ref_out, ws = _merge(mel, cfg, inp)
-    w = {n: inp[n] for n in WEIGHTS}
-    w["w_gu"], w["w_d"] = _unaligned(inp["w_gu"]), _unaligned(inp["w_d"])
+    moved = ("w_gu", "w_d") if which == "base" else WEIGHTS
+    w = {n: _unaligned(inp[n]) if n in moved else inp[n] for n in WEIGHTS}
     out = {n: _unaligned(torch.full_like(inp[n], float("nan"))) for n in ("w_gu", "w_d")}
     mel.moe_merge_lora(mel.Shape.of(cfg), w, out["w_gu"], out["w_d"], ws)
     torch.cuda.synchronize()
