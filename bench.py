@@ -68,6 +68,7 @@ def kernel_bytes(name, cfg):
         "dy_gather": T * H * es + N * H * es + N * 4,         # dY in, its permuted rows out
         # routing weight per row, w u_d, and the dw partial sums of the down backward
         "dw_sum": N * 12 + 2 * N * cfg.r * es + N * 4 * dw_slots(cfg) + N * 8,
+        "row_scale": 2 * N * H * es + N * 4,                  # dY rows scaled in place by w
         "route_bwd": 2 * T * E * 4 + T * k * 8,                # logits in, dlogits out; ids, dw
         "unpermute": N * H * es + T * H * es + N * 4,         # dX_perm in, dX out, inv_pos
         "router_fwd": T * H * es + E * H * es + T * E * 4,    # x, W_r in; logits out

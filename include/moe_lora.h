@@ -360,7 +360,7 @@ typedef enum {
   MOE_K_DOWN_BWD = 8, MOE_K_GATE_UP_BWD = 9, MOE_K_LORA_SIDE = 10, MOE_K_LORA_WGRAD = 11,
   MOE_K_UNPERMUTE = 12, MOE_K_BASE_WGRAD = 13, MOE_K_ROUTER_FWD = 14, MOE_K_ROUTER_BWD = 15,
   MOE_K_ACCUMULATE = 16, MOE_K_MERGE = 17, MOE_K_DY_GATHER = 18, MOE_K_DW_SUM = 19,
-  MOE_K_COUNT = 20
+  MOE_K_ROW_SCALE = 20, MOE_K_COUNT = 21
 } moe_kernel_id;
 moe_status moe_kernel_timer_enable(int32_t on);
 /* Time only the kernels whose bit (1u << id) is set in mask (all, by default):

@@ -15,7 +15,7 @@ KERNEL_IDS = {"route": 0, "permute": 1, "gather": 2, "gate_up_fwd": 3, "down_fwd
               "combine": 5, "combine_bwd": 6, "route_bwd": 7, "down_bwd": 8, "gate_up_bwd": 9,
               "lora_side": 10, "lora_wgrad": 11, "unpermute": 12, "base_wgrad": 13,
               "router_fwd": 14, "router_bwd": 15, "accumulate": 16, "merge": 17,
-              "dy_gather": 18, "dw_sum": 19}
+              "dy_gather": 18, "dw_sum": 19, "row_scale": 20}
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
            "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",

@@ -1806,28 +1806,48 @@ __global__ __launch_bounds__(256) void side_sum_kernel(const float* __restrict__
 }
 
 // dst[n][c] = w[n] * src[n][c] over rows x cols (dst may be src), one rounding.
-template <typename Elem>
+// VEC: cols % 8 == 0 and both 16-byte aligned: one 16-byte piece per thread.
+template <typename Elem, bool VEC>
 __global__ __launch_bounds__(256) void scale_rows_kernel(const Elem* src, const float* __restrict__ w,
                                                          int64_t total, int cols, Elem* dst) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * (VEC ? 8 : 1);
   if (i >= total) return;
-  dst[i] = from_f32<Elem>(w[i / cols] * to_f32<Elem>(src[i]));
+  const float wr = w[i / cols];
+  if constexpr (VEC) {
+    u32x4 v = *reinterpret_cast<const u32x4*>(src + i);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint16_t lo = static_cast<uint16_t>(v[t] & 0xffffu), hi = static_cast<uint16_t>(v[t] >> 16);
+      const float a = wr * to_f32<Elem>(__builtin_bit_cast(Elem, lo));
+      const float b = wr * to_f32<Elem>(__builtin_bit_cast(Elem, hi));
+      v[t] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_f32<Elem>(a))) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_f32<Elem>(b))) << 16);
+    }
+    *reinterpret_cast<u32x4*>(dst + i) = v;
+  } else {
+    dst[i] = from_f32<Elem>(wr * to_f32<Elem>(src[i]));
+  }
 }
 
 hipError_t scale_rows(int dtype, const void* src, const float* w, int64_t rows, int cols,
                       void* dst, hipStream_t s) {
   const int64_t total = rows * cols;
   if (total <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(scale_rows_kernel<bf16_t>, grid, dim3(256), 0, s,
-                       static_cast<const bf16_t*>(src), w, total, cols, static_cast<bf16_t*>(dst));
-  else if (dtype == MOE_F16)
-    hipLaunchKernelGGL(scale_rows_kernel<f16_t>, grid, dim3(256), 0, s,
-                       static_cast<const f16_t*>(src), w, total, cols, static_cast<f16_t*>(dst));
-  else
-    hipLaunchKernelGGL(scale_rows_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(src), w, total, cols, static_cast<float*>(dst));
+  const bool vec = dtype != MOE_F32 && cols % 8 == 0 && aligned16(src) && aligned16(dst);
+  const dim3 grid(static_cast<unsigned>((total / (vec ? 8 : 1) + 255) / 256));
+  if (dtype == MOE_BF16) {
+    auto k = vec ? scale_rows_kernel<bf16_t, true> : scale_rows_kernel<bf16_t, false>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, static_cast<const bf16_t*>(src), w, total, cols,
+                       static_cast<bf16_t*>(dst));
+  } else if (dtype == MOE_F16) {
+    auto k = vec ? scale_rows_kernel<f16_t, true> : scale_rows_kernel<f16_t, false>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, static_cast<const f16_t*>(src), w, total, cols,
+                       static_cast<f16_t*>(dst));
+  } else {
+    auto k = scale_rows_kernel<float, false>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, static_cast<const float*>(src), w, total, cols,
+                       static_cast<float*>(dst));
+  }
   return hipGetLastError();
 }
 
@@ -2151,8 +2171,11 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     MOE_TRY(weight_grad(d, offsets, gb_da, r, sv.act, I, gr.da_d, s, split));
   }
   if (base) {  // full fine-tuning: dW_d = G^T act  [H, I]
+    if (cb) {
+      TimedScope ts(tm, MOE_K_ROW_SCALE, s);
+      MOE_TRY(scale_rows(d.dtype, g, B.w_perm, d.N, H, const_cast<void*>(g), s));
+    }
     TimedScope ts(tm, MOE_K_BASE_WGRAD, s);
-    if (cb) MOE_TRY(scale_rows(d.dtype, g, B.w_perm, d.N, H, const_cast<void*>(g), s));
     MOE_TRY(weight_grad(d, offsets, g, H, sv.act, I, base->dw_d, s, nullptr));
   }
   if (fuse_gu) {  // dB_gu = dH^T u_gu [2I, r] and dhb = s dH B_gu in one pass over dH
