@@ -43,6 +43,12 @@
  *    accumulate in float32. Router logits, combine weights and their
  *    gradients are always float32; indices are int32.
  *  - Outputs are fully overwritten (gradients are not accumulated into).
+ *  - Token-row buffers that the gather and combine kernels move in 16-byte
+ *    pieces start on a 16-byte boundary (any torch allocation does): x and
+ *    x_perm of moe_permute, y_perm and y (or dx_perm and dx) of
+ *    moe_unpermute_combine, dy, y_exp and dy_perm of the combine backwards.
+ *    Weights and the other activations may sit anywhere (unaligned operands
+ *    take element-wise loads).
  *  - Arguments are checked before anything is enqueued. Errors:
  *      MOE_ERR_INVALID_ARG   a NULL pointer that is not optional, T < 1,
  *                            k < 1, k > E, E < 1, E > 1024, H < 1, I < 1,
@@ -50,6 +56,8 @@
  *                            `dtype` above 32 GiB (one activation tensor),
  *                            2I * H bytes of `dtype` at or above 2 GiB (one
  *                            expert's weight matrix), unknown router or dtype
+ *                            or a token-row buffer (below) off a 16-byte
+ *                            boundary
  *      MOE_ERR_UNSUPPORTED   H or I not a multiple of 8, r > 64, k > 32
  *      MOE_ERR_WORKSPACE     workspace smaller than moe_workspace_bytes says
  *      MOE_ERR_HIP           a launch failed (moe_last_error() has the text)

@@ -26,6 +26,14 @@ moe_status hip_fail(hipError_t e, const char* where) {
     if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "null pointer: " #p);        \
   } while (0)
 
+// Token-row buffers that the row kernels (gather, combine and their
+// backwards) move in 16-byte pieces must start on a 16-byte boundary.
+#define CHECK_ROWS(p)                                                                 \
+  do {                                                                                \
+    if ((reinterpret_cast<uintptr_t>(p) & 15) != 0)                                   \
+      return fail(MOE_ERR_INVALID_ARG, #p " does not start on a 16-byte boundary");   \
+  } while (0)
+
 moe_status check_router(int32_t router) {
   if (router < MOE_SOFTMAX_TOPK || router > MOE_SIGMOID_TOPK_RENORM)
     return fail(MOE_ERR_INVALID_ARG, "unknown router mode " + std::to_string(router));
@@ -216,7 +224,11 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, const vo
   CHECK_PTR(offsets);
   CHECK_PTR(sorted_pair);
   CHECK_PTR(inv_pos);
-  if (x_perm) CHECK_PTR(x);
+  if (x_perm) {
+    CHECK_PTR(x);
+    CHECK_ROWS(x);
+    CHECK_ROWS(x_perm);
+  }
   if (x_perm && x_perm == x) return fail(MOE_ERR_INVALID_ARG, "x_perm aliases x");
   const moe::ExpertDims d = dims_of(shape);
   const size_t need = moe::permute_ws_bytes(d.N, d.E);
@@ -246,7 +258,11 @@ moe_status moe_permute_noalloc(const moe_shape* shape, const int32_t* topk_ids, 
   CHECK_PTR(offsets);
   CHECK_PTR(sorted_pair);
   CHECK_PTR(inv_pos);
-  if (x_perm) CHECK_PTR(x);
+  if (x_perm) {
+    CHECK_PTR(x);
+    CHECK_ROWS(x);
+    CHECK_ROWS(x_perm);
+  }
   if (x_perm && x_perm == x) return fail(MOE_ERR_INVALID_ARG, "x_perm aliases x");
   const moe::ExpertDims d = dims_of(shape);
   const size_t need = moe::permute_ws_bytes(d.N, d.E);
@@ -334,6 +350,8 @@ moe_status moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
   CHECK_PTR(y_perm);
   CHECK_PTR(inv_pos);
   CHECK_PTR(y);
+  CHECK_ROWS(y_perm);
+  CHECK_ROWS(y);
   if (y == y_perm) return fail(MOE_ERR_INVALID_ARG, "y aliases y_perm");
   hipError_t e = moe::launch_combine(shape->dtype, y_perm, inv_pos, topk_w, shape->T, shape->k,
                                      shape->H, y, as_stream(stream), moe::active_timer());
@@ -352,6 +370,9 @@ moe_status moe_unpermute_combine_bwd(const moe_shape* shape, const void* dy,
   CHECK_PTR(topk_w);
   CHECK_PTR(dy_perm);
   CHECK_PTR(d_topk_w);
+  CHECK_ROWS(dy);
+  CHECK_ROWS(y_exp);
+  CHECK_ROWS(dy_perm);
   if (dy_perm == dy || dy_perm == y_exp)
     return fail(MOE_ERR_INVALID_ARG, "dy_perm aliases an input");
   hipError_t e = moe::launch_combine_bwd(shape->dtype, dy, y_exp, inv_pos, topk_w, shape->T,
@@ -483,6 +504,8 @@ moe_status moe_grouped_lora_combine_bwd(const moe_shape* shape, const void* dy,
   CHECK_PTR(sorted_pair);
   CHECK_PTR(inv_pos);
   CHECK_PTR(d_topk_w);
+  CHECK_ROWS(dy);
+  CHECK_ROWS(dy_perm);
   const bool lean = recompute != 0;
   if (dy_perm == dy || dy_perm == x_perm || dy_perm == dx_perm)
     return fail(MOE_ERR_INVALID_ARG, "dy_perm aliases another tensor");

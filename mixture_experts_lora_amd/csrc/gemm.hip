@@ -1806,7 +1806,9 @@ __global__ __launch_bounds__(256) void side_sum_kernel(const float* __restrict__
 }
 
 // dst[n][c] = w[n] * src[n][c] over rows x cols (dst may be src), one rounding.
-// VEC: cols % 8 == 0 and both 16-byte aligned: one 16-byte piece per thread.
+// VEC (16-bit, cols % 8 == 0, both 16-byte aligned: the dY rows of full
+// fine-tuning) one 16-byte piece per thread; otherwise (float32 rows, and the
+// [N, r] side products when r % 8 != 0) one element per thread.
 template <typename Elem, bool VEC>
 __global__ __launch_bounds__(256) void scale_rows_kernel(const Elem* src, const float* __restrict__ w,
                                                          int64_t total, int cols, Elem* dst) {

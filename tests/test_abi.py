@@ -127,6 +127,42 @@ def test_null_pointers_rejected(lib):
                                     None) == 1
 
 
+def test_token_rows_must_be_16_byte_aligned(lib):
+    """The gather and combine kernels move token rows in 16-byte pieces: their
+    row buffers off a 16-byte boundary are refused before any launch."""
+    P = ctypes.c_void_p
+    fake, odd = P(0x10000), P(0x20002)
+    sh = shape()
+    ws_bytes = 1 << 30
+    # moe_permute with a gather: x, x_perm
+    assert lib.moe_permute(ctypes.byref(sh), fake, odd, fake, fake, fake, fake, P(0x30000), fake,
+                           ws_bytes, None) == 1
+    assert b"16-byte" in lib.moe_last_error()
+    assert lib.moe_permute(ctypes.byref(sh), fake, P(0x30000), fake, fake, fake, fake, odd, fake,
+                           ws_bytes, None) == 1
+    assert lib.moe_permute_noalloc(ctypes.byref(sh), fake, odd, fake, fake, fake, fake,
+                                   P(0x30000), None) == 1
+    # combine (and unpermute): y_perm, y
+    assert lib.moe_unpermute_combine(ctypes.byref(sh), odd, fake, None, P(0x30000), None) == 1
+    assert lib.moe_unpermute_combine(ctypes.byref(sh), fake, fake, None, odd, None) == 1
+    # combine backward: dy, y_exp, dy_perm
+    for args in ((odd, fake, P(0x30000)), (fake, odd, P(0x30000)), (fake, P(0x40000), odd)):
+        dy, y_exp, dy_perm = args
+        assert lib.moe_unpermute_combine_bwd(ctypes.byref(sh), dy, y_exp, fake, fake, dy_perm,
+                                             fake, None) == 1
+    # the folded combine backward: dy, dy_perm
+    from mixture_experts_lora_amd._lib import MoeLoraGrads, MoeSaved, MoeWeights
+    w = MoeWeights(*(0x10000,) * 6)
+    sv = MoeSaved(*(0x30000 + i * 0x1000 for i in range(5)))
+    g = MoeLoraGrads(*(0x50000 + i * 0x1000 for i in range(4)))
+    for dy, dy_perm in ((odd, P(0x60000)), (fake, odd)):
+        assert lib.moe_grouped_lora_combine_bwd(
+            ctypes.byref(sh), dy, fake, fake, fake, P(0x70000), fake, ctypes.byref(w),
+            ctypes.byref(sv), 0, dy_perm, P(0x80000), ctypes.byref(g), None, fake, fake,
+            ws_bytes, None) == 1
+        assert b"16-byte" in lib.moe_last_error()
+
+
 def test_noalloc_permute_rejects_tables_beyond_its_array(lib):
     """moe_permute_noalloc's table (E * ceil(T k / 64) int32) must fit its
     4 MiB device array; a larger one is refused before any GPU call."""

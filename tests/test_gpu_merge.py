@@ -26,6 +26,19 @@ def _mel():
     return mel
 
 
+# float16 layers with ranks above 16, so every (dtype, k-step count) pair of
+# the merge kernel runs (ranks up to 16, 32 and 64 take one, two and four
+# k steps)
+EXTRA = {
+    "mini-f16-r32": PARITY_CONFIGS["mini-f16"].with_(name="mini-f16-r32", r=32),
+    "mini-f16-r64": PARITY_CONFIGS["mini-f16"].with_(name="mini-f16-r64", r=64, lora_scale=0.5),
+}
+
+
+def _cfg(name):
+    return EXTRA[name] if name in EXTRA else PARITY_CONFIGS[name]
+
+
 def _check(name, got, ref, dtype):
     close(name, got, ref, TOL[dtype])
     got = np.asarray(got, np.float64)
@@ -47,10 +60,10 @@ def _merge(mel, cfg, inp, **kw):
     return out, ws
 
 
-@pytest.mark.parametrize("name", list(PARITY_CONFIGS))
+@pytest.mark.parametrize("name", list(PARITY_CONFIGS) + list(EXTRA))
 def test_merge_matches_oracle(name):
     mel = _mel()
-    cfg = PARITY_CONFIGS[name]
+    cfg = _cfg(name)
     say(f"[merge] {name} H={cfg.H} I={cfg.I} E={cfg.E} r={cfg.r} {cfg.dtype} s={cfg.lora_scale}")
     inp = make_inputs(cfg, 21, device="cuda", with_dy=False)
     out, _ = _merge(mel, cfg, inp)
@@ -110,13 +123,14 @@ def _unaligned(t):
 
 
 @pytest.mark.parametrize("which", ["base", "all"])
-@pytest.mark.parametrize("name", ["mini-bf16", "mini-skew", "mini-r64", "mini-f16", "mini-r1"])
+@pytest.mark.parametrize("name", ["mini-bf16", "mini-skew", "mini-r64", "mini-f16", "mini-r1",
+                                  "mini-f16-r32", "mini-f16-r64"])
 def test_merge_unaligned_weights(name, which):
     """Base weights and outputs (and with "all" the LoRA factors too) that
     cannot be read in 16-byte pieces take the element-wise paths: same results
     bit for bit, and within one ulp of the oracle."""
     mel = _mel()
-    cfg = PARITY_CONFIGS[name]
+    cfg = _cfg(name)
     say(f"[merge unaligned] {name} {which}")
     inp = make_inputs(cfg, 24, device="cuda", with_dy=False)
     ref_out, ws = _merge(mel, cfg, inp)

@@ -115,6 +115,9 @@ PARITY_CONFIGS = {
     "mini-f16-skew": LayerConfig("mini-f16-skew", T=1100, H=264, I=136, E=16, k=4, r=32,
                                  dtype="f16", router="sigmoid_topk_renorm", zipf_s=1.2,
                                  n_dead=4, lora_scale=2.0),
+    # half with a rank that is not a multiple of 8 (element-wise side-product rows)
+    "mini-f16-r4": LayerConfig("mini-f16-r4", T=200, H=136, I=72, E=5, k=2, r=4,
+                               dtype="f16", router="softmax_topk_renorm"),
     # the largest expert count and top-k the library accepts: about two rows per expert
     "max-E-k": LayerConfig("max-E-k", T=64, H=64, I=32, E=1024, k=32, r=8,
                            dtype="bf16", router="softmax_topk"),
