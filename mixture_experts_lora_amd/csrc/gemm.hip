@@ -1672,10 +1672,11 @@ int wgrad_tiles(const ExpertDims& d, int P, int Q) {
 }
 
 // Row chunks per expert: enough to reach ~512 workgroups when fewer than 256
-// would run, never chunks of fewer than 256 rows on average, and none for the
-// full fine-tuning gradients (P, Q >= 256: tiles enough, partials too large).
+// would run, never chunks of fewer than 256 rows on average, and only for the
+// LoRA gradients of rank <= 32 (the full fine-tuning gradients have tiles
+// enough and would need large partials; higher ranks are rare).
 int wgrad_splits(const ExpertDims& d, int P, int Q) {
-  if (P >= 256 && Q >= 256) return 1;
+  if (std::min(P, Q) > 32) return 1;
   const int64_t blocks = static_cast<int64_t>(d.E) * wgrad_tiles(d, P, Q);
   if (blocks >= 256) return 1;
   const int64_t by_rows = static_cast<int64_t>(d.N) / (static_cast<int64_t>(d.E) * 256);
@@ -1732,20 +1733,28 @@ hipError_t weight_grad_launch(const ExpertDims& d, GemmArgs& a, int E, int P, in
                   E * a.ntm, a, s);
   }
   if (d.dtype != MOE_F32) {
+    // Split partials (EPI_STORE_F32) only come from gradients with a side of
+    // at most 32 (wgrad_splits): the other tile shapes exist for EPI_STORE only.
+    constexpr bool WIDE = EPI == EPI_STORE;
     if (Q <= 64 && P > 64) {  // [big, r]
       a.ntn = 1;
       a.ntm = ceil_div(P, 256);
       if (Q <= 32)
         return launch(GEMM16(a.dtype, 256, 32, 64, 32, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
                       E * a.ntm, a, s);
-      return launch(GEMM16(a.dtype, 256, 64, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
-                    E * a.ntm, a, s);
+      if constexpr (WIDE)
+        return launch(GEMM16(a.dtype, 256, 64, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
+                      E * a.ntm, a, s);
+      return hipErrorInvalidValue;
     }
     if (P >= 256 && Q >= 256) {  // [big, big]: full fine-tuning weight gradients
-      a.ntm = ceil_div(P, 128);
-      a.ntn = ceil_div(Q, 256);
-      return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
-                    E * a.ntm * a.ntn, a, s);
+      if constexpr (WIDE) {
+        a.ntm = ceil_div(P, 128);
+        a.ntn = ceil_div(Q, 256);
+        return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
+                      E * a.ntm * a.ntn, a, s);
+      }
+      return hipErrorInvalidValue;
     }
     // [r, big] (or both small)
     a.ntn = ceil_div(Q, 256);
@@ -1754,9 +1763,12 @@ hipError_t weight_grad_launch(const ExpertDims& d, GemmArgs& a, int E, int P, in
       return launch(GEMM16(a.dtype, 32, 256, 32, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
                     E * a.ntn, a, s);
     }
-    a.ntm = ceil_div(P, 64);
-    return launch(GEMM16(a.dtype, 64, 256, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
-                  E * a.ntm * a.ntn, a, s);
+    if constexpr (WIDE) {
+      a.ntm = ceil_div(P, 64);
+      return launch(GEMM16(a.dtype, 64, 256, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
+                    E * a.ntm * a.ntn, a, s);
+    }
+    return hipErrorInvalidValue;
   }
   a.ntm = ceil_div(P, 64);
   a.ntn = ceil_div(Q, 64);

@@ -118,9 +118,25 @@ PARITY_CONFIGS = {
     # half with a rank that is not a multiple of 8 (element-wise side-product rows)
     "mini-f16-r4": LayerConfig("mini-f16-r4", T=200, H=136, I=72, E=5, k=2, r=4,
                                dtype="f16", router="softmax_topk_renorm"),
+    # half with the widest rank (r > 32 tile shapes) and with split weight gradients
+    "mini-f16-r64": LayerConfig("mini-f16-r64", T=160, H=192, I=160, E=3, k=2, r=64,
+                                dtype="f16", router="softmax_topk"),
+    "mini-f16-split": LayerConfig("mini-f16-split", T=2000, H=320, I=192, E=4, k=2, r=16,
+                                  dtype="f16", router="sigmoid_topk_renorm", zipf_s=1.2,
+                                  n_dead=1),
+    # split weight gradients of a rank that is not a multiple of 8 (the B
+    # gradients without their fused side products)
+    "mini-split-r12": LayerConfig("mini-split-r12", T=1800, H=256, I=160, E=3, k=2, r=12,
+                                  dtype="bf16", router="softmax_topk_renorm"),
+    "mini-f16-split-r12": LayerConfig("mini-f16-split-r12", T=1800, H=256, I=160, E=3, k=2,
+                                      r=12, dtype="f16", router="topk_softmax"),
     # the largest expert count and top-k the library accepts: about two rows per expert
     "max-E-k": LayerConfig("max-E-k", T=64, H=64, I=32, E=1024, k=32, r=8,
                            dtype="bf16", router="softmax_topk"),
+    "max-E-k-f32": LayerConfig("max-E-k-f32", T=64, H=64, I=32, E=1024, k=32, r=8,
+                               dtype="f32", router="topk_softmax"),
+    "max-E-k-f16": LayerConfig("max-E-k-f16", T=64, H=64, I=32, E=1024, k=32, r=8,
+                               dtype="f16", router="sigmoid_topk_renorm"),
 }
 
 
