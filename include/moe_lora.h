@@ -312,6 +312,32 @@ moe_status moe_grouped_lora_combine_bwd(const moe_shape *shape, const void *dy,
                                         float *d_topk_w, void *ws, size_t ws_bytes,
                                         void *stream);
 
+/* The layer input read in token order (faster-moe page, "Implementation
+ * details": the LoRA products run on the routed pairs only; here the expert
+ * GEMMs also fetch each pair's row of x themselves, so x_perm is never
+ * formed). x is [T, H] of `dtype` in token order, and row i of the permuted
+ * order is row sorted_pair[i] / k of x (sorted_pair from moe_permute, which
+ * can then be called with x_perm = NULL). The GEMMs that read x_perm in the
+ * calls above (gate_up, its LoRA side product X A_gu^T, dA_gu and, with base,
+ * dW_gu) read those rows of x instead; everything else, and every result, is
+ * as in moe_grouped_lora_fwd / moe_grouped_lora_fwd_lean (lean != 0) and
+ * moe_grouped_lora_combine_bwd. Errors as those calls, plus a NULL
+ * sorted_pair, and MOE_ERR_UNSUPPORTED when x is 2 GiB or larger (use x_perm
+ * and the calls above).  */
+moe_status moe_grouped_lora_fwd_gather(const moe_shape *shape, const void *x,
+                                       const int32_t *sorted_pair, const int32_t *offsets,
+                                       const moe_weights *weights, const moe_saved *saved,
+                                       int32_t lean, void *ws, size_t ws_bytes, void *stream);
+moe_status moe_grouped_lora_combine_bwd_gather(const moe_shape *shape, const void *dy,
+                                               const float *topk_w, const int32_t *sorted_pair,
+                                               const int32_t *inv_pos, const void *x,
+                                               const int32_t *offsets, const moe_weights *weights,
+                                               const moe_saved *saved, int32_t recompute,
+                                               void *dy_perm, void *dx_perm,
+                                               const moe_lora_grads *grads,
+                                               const moe_base_grads *base, float *d_topk_w,
+                                               void *ws, size_t ws_bytes, void *stream);
+
 /* Router projection and its input gradient, for callers that start from
  * hidden states rather than logits. The pages keep the router frozen (faster-
  * moe page, "Implementation details"), so there is no router weight

@@ -26,7 +26,8 @@ from ._lib import MoeBaseGrads, MoeLoraGrads, MoeSaved, MoeShape, MoeWeights, RO
 
 __all__ = [
     "Shape", "moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
-    "moe_permute_noalloc", "moe_grouped_lora_combine_bwd",
+    "moe_permute_noalloc", "moe_grouped_lora_combine_bwd", "moe_grouped_lora_fwd_gather",
+    "moe_grouped_lora_combine_bwd_gather",
     "moe_grouped_lora_fwd", "moe_unpermute_combine", "moe_unpermute_combine_bwd",
     "moe_grouped_lora_bwd", "moe_grouped_full_bwd", "moe_workspace_bytes_lean",
     "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute", "moe_router_workspace_bytes",
@@ -217,6 +218,21 @@ def moe_grouped_lora_fwd_lean(shape: Shape, x_perm, offsets, weights: dict, save
         wsp, wsb, _stream(stream)), "moe_grouped_lora_fwd_lean")
 
 
+def moe_grouped_lora_fwd_gather(shape: Shape, x, sorted_pair, offsets, weights: dict,
+                                saved: dict, ws, lean=False, stream=None):
+    """moe_grouped_lora_fwd (lean: moe_grouped_lora_fwd_lean) reading the rows of
+    x [T, H] in token order through sorted_pair instead of x_perm."""
+    need = moe_workspace_bytes_lean(shape)[0] if lean else moe_workspace_bytes(shape)[0]
+    wsp, wsb = _ws(ws, need, "ws")
+    w = _weights(shape, weights)
+    s = _saved(shape, saved, lean=lean)
+    check(_lib.load().moe_grouped_lora_fwd_gather(
+        ctypes.byref(shape.c()), _ptr(x, (shape.T, shape.H), shape.torch_dtype, "x"),
+        _ptr(sorted_pair, (shape.N,), torch.int32, "sorted_pair"),
+        _ptr(offsets, (shape.E + 1,), torch.int32, "offsets"), ctypes.byref(w), ctypes.byref(s),
+        1 if lean else 0, wsp, wsb, _stream(stream)), "moe_grouped_lora_fwd_gather")
+
+
 def moe_unpermute_combine(shape: Shape, y_perm, inv_pos, topk_w, y, stream=None):
     dt = shape.torch_dtype
     check(_lib.load().moe_unpermute_combine(
@@ -240,7 +256,7 @@ def moe_unpermute_combine_bwd(shape: Shape, dy, y_exp, inv_pos, topk_w, dy_perm,
 
 
 def _bwd_args(shape: Shape, dy_perm, x_perm, offsets, weights: dict, saved: dict, dx_perm,
-              grads: dict, ws, lean=False):
+              grads: dict, ws, lean=False, x_rows=None):
     need = moe_workspace_bytes_lean(shape)[1] if lean else moe_workspace_bytes(shape)[1]
     wsp, wsb = _ws(ws, need, "ws")
     E, H, I, r, dt = shape.E, shape.H, shape.I, shape.r, shape.torch_dtype
@@ -251,7 +267,7 @@ def _bwd_args(shape: Shape, dy_perm, x_perm, offsets, weights: dict, saved: dict
                      _ptr(grads["da_d"], (E, r, I), dt, "da_d"),
                      _ptr(grads["db_d"], (E, H, r), dt, "db_d"))
     head = (ctypes.byref(shape.c()), _ptr(dy_perm, (shape.N, H), dt, "dy_perm"),
-            _ptr(x_perm, (shape.N, H), dt, "x_perm"),
+            _ptr(x_perm, (x_rows or shape.N, H), dt, "x" if x_rows else "x_perm"),
             _ptr(offsets, (E + 1,), torch.int32, "offsets"), ctypes.byref(w), ctypes.byref(s),
             _ptr(dx_perm, (shape.N, H), dt, "dx_perm"), ctypes.byref(g))
     return head, (w, s, g), wsp, wsb
@@ -316,6 +332,29 @@ def moe_grouped_lora_combine_bwd(shape: Shape, dy, topk_w, sorted_pair, inv_pos,
         dyp, dxp, g, ctypes.byref(b) if b is not None else None,
         _ptr(d_topk_w, (T, k), torch.float32, "d_topk_w"), wsp, wsb, _stream(stream)),
         "moe_grouped_lora_combine_bwd")
+
+
+def moe_grouped_lora_combine_bwd_gather(shape: Shape, dy, topk_w, sorted_pair, inv_pos, x,
+                                        offsets, weights: dict, saved: dict, dy_perm, dx_perm,
+                                        grads: dict, d_topk_w, ws, base_grads=None,
+                                        recompute=False, stream=None):
+    """moe_grouped_lora_combine_bwd reading the rows of x [T, H] in token order
+    through sorted_pair instead of x_perm."""
+    head, keep, wsp, wsb = _bwd_args(shape, dy_perm, x, offsets, weights, saved, dx_perm,
+                                     grads, ws, lean=recompute, x_rows=shape.T)
+    shp, dyp, xp, off, w, sv, dxp, g = head
+    T, k, N, H, E, I, dt = shape.T, shape.k, shape.N, shape.H, shape.E, shape.I, shape.torch_dtype
+    b = None
+    if base_grads is not None:
+        b = MoeBaseGrads(_ptr(base_grads["dw_gu"], (E, 2 * I, H), dt, "dw_gu"),
+                         _ptr(base_grads["dw_d"], (E, H, I), dt, "dw_d"))
+    check(_lib.load().moe_grouped_lora_combine_bwd_gather(
+        shp, _ptr(dy, (T, H), dt, "dy"), _ptr(topk_w, (T, k), torch.float32, "topk_w"),
+        _ptr(sorted_pair, (N,), torch.int32, "sorted_pair"),
+        _ptr(inv_pos, (N,), torch.int32, "inv_pos"), xp, off, w, sv, 1 if recompute else 0,
+        dyp, dxp, g, ctypes.byref(b) if b is not None else None,
+        _ptr(d_topk_w, (T, k), torch.float32, "d_topk_w"), wsp, wsb, _stream(stream)),
+        "moe_grouped_lora_combine_bwd_gather")
 
 
 def _dtype_of(t, name):

@@ -23,7 +23,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_bwd", "moe_permute",
            "moe_grouped_lora_fwd_lean", "moe_grouped_lora_bwd_recompute",
            "moe_router_workspace_bytes", "moe_router_fwd", "moe_router_bwd", "moe_accumulate",
            "moe_merge_workspace_bytes", "moe_merge_lora", "moe_permute_noalloc",
-           "moe_grouped_lora_combine_bwd",
+           "moe_grouped_lora_combine_bwd", "moe_grouped_lora_fwd_gather",
+           "moe_grouped_lora_combine_bwd_gather",
            "moe_status_str",
            "moe_last_error",
            "moe_kernel_timer_enable", "moe_kernel_timer_select", "moe_kernel_timer_reset",
@@ -107,6 +108,16 @@ def load() -> ctypes.CDLL:
                                               ctypes.POINTER(MoeLoraGrads),
                                               ctypes.POINTER(MoeBaseGrads), P, P,
                                               ctypes.c_size_t, P]),
+        "moe_grouped_lora_combine_bwd_gather": (st, [ctypes.POINTER(MoeShape), P, P, P, P, P, P,
+                                                     ctypes.POINTER(MoeWeights),
+                                                     ctypes.POINTER(MoeSaved), I32, P, P,
+                                                     ctypes.POINTER(MoeLoraGrads),
+                                                     ctypes.POINTER(MoeBaseGrads), P, P,
+                                                     ctypes.c_size_t, P]),
+        "moe_grouped_lora_fwd_gather": (st, [ctypes.POINTER(MoeShape), P, P, P,
+                                             ctypes.POINTER(MoeWeights),
+                                             ctypes.POINTER(MoeSaved), I32, P, ctypes.c_size_t,
+                                             P]),
         "moe_router_workspace_bytes": (st, [I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]),
         "moe_router_fwd": (st, [P, P, I32, I32, I32, I32, P, P, ctypes.c_size_t, P]),
         "moe_router_bwd": (st, [P, P, I32, I32, I32, I32, P, P, ctypes.c_size_t, P]),

@@ -288,12 +288,28 @@ moe_status moe_permute_noalloc(const moe_shape* shape, const int32_t* topk_ids, 
 
 namespace {
 
+// x rows read by the GEMMs through sorted_pair: one buffer resource spans x
+moe_status check_gather(const moe_shape* shape, const int32_t* sorted_pair) {
+  CHECK_PTR(sorted_pair);
+  const int64_t bytes = int64_t(shape->T) * shape->H * (shape->dtype == MOE_F32 ? 4 : 2);
+  if (bytes >= (int64_t{1} << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "x of " + std::to_string(bytes) +
+                                         " bytes: gathered rows need x below 2 GiB (use x_perm)");
+  return MOE_OK;
+}
+
+// x_perm: x_perm, or x in token order when sorted_pair is given (gathered)
 moe_status grouped_fwd(const char* name, bool lean, const moe_shape* shape, const void* x_perm,
-                       const int32_t* offsets, const moe_weights* weights, const moe_saved* saved,
-                       void* ws, size_t ws_bytes, void* stream) {
+                       const int32_t* sorted_pair, const int32_t* offsets,
+                       const moe_weights* weights, const moe_saved* saved, void* ws,
+                       size_t ws_bytes, void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   CHECK_PTR(x_perm);
+  if (sorted_pair) {
+    st = check_gather(shape, sorted_pair);
+    if (st != MOE_OK) return st;
+  }
   CHECK_PTR(offsets);
   CHECK_PTR(weights);
   CHECK_PTR(saved);
@@ -317,9 +333,10 @@ moe_status grouped_fwd(const char* name, bool lean, const moe_shape* shape, cons
     return fail(MOE_ERR_WORKSPACE, "forward workspace needs " + std::to_string(need) + " bytes");
   if ((!lean && (saved->h == x_perm || saved->act == x_perm)) || saved->y_exp == x_perm)
     return fail(MOE_ERR_INVALID_ARG, "a saved activation aliases x_perm");
-  hipError_t e = lean ? moe::launch_experts_fwd_lean(d, x_perm, offsets, *weights, *saved, ws,
+  const moe::XRows x{x_perm, sorted_pair, shape->k, shape->T};
+  hipError_t e = lean ? moe::launch_experts_fwd_lean(d, x, offsets, *weights, *saved, ws,
                                                      as_stream(stream), moe::active_timer())
-                      : moe::launch_experts_fwd(d, x_perm, offsets, *weights, *saved, ws,
+                      : moe::launch_experts_fwd(d, x, offsets, *weights, *saved, ws,
                                                 as_stream(stream), moe::active_timer());
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
 }
@@ -330,16 +347,25 @@ moe_status moe_grouped_lora_fwd(const moe_shape* shape, const void* x_perm,
                                 const int32_t* offsets, const moe_weights* weights,
                                 const moe_saved* saved, void* ws, size_t ws_bytes,
                                 void* stream) {
-  return grouped_fwd("moe_grouped_lora_fwd", false, shape, x_perm, offsets, weights, saved, ws,
-                     ws_bytes, stream);
+  return grouped_fwd("moe_grouped_lora_fwd", false, shape, x_perm, nullptr, offsets, weights,
+                     saved, ws, ws_bytes, stream);
 }
 
 moe_status moe_grouped_lora_fwd_lean(const moe_shape* shape, const void* x_perm,
                                      const int32_t* offsets, const moe_weights* weights,
                                      const moe_saved* saved, void* ws, size_t ws_bytes,
                                      void* stream) {
-  return grouped_fwd("moe_grouped_lora_fwd_lean", true, shape, x_perm, offsets, weights, saved,
-                     ws, ws_bytes, stream);
+  return grouped_fwd("moe_grouped_lora_fwd_lean", true, shape, x_perm, nullptr, offsets, weights,
+                     saved, ws, ws_bytes, stream);
+}
+
+moe_status moe_grouped_lora_fwd_gather(const moe_shape* shape, const void* x,
+                                       const int32_t* sorted_pair, const int32_t* offsets,
+                                       const moe_weights* weights, const moe_saved* saved,
+                                       int32_t lean, void* ws, size_t ws_bytes, void* stream) {
+  CHECK_PTR(sorted_pair);
+  return grouped_fwd("moe_grouped_lora_fwd_gather", lean != 0, shape, x, sorted_pair, offsets,
+                     weights, saved, ws, ws_bytes, stream);
 }
 
 moe_status moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
@@ -447,11 +473,12 @@ moe_status grouped_bwd(const char* name, bool lean, const moe_shape* shape,
                                     dx_perm, grads, base, ws, ws_bytes);
   if (st != MOE_OK) return st;
   const moe::ExpertDims d = dims_of(shape);
+  const moe::XRows x{x_perm, nullptr, shape->k, shape->T};
   hipError_t e =
-      lean ? moe::launch_experts_bwd_recompute(d, dy_perm, x_perm, offsets, *weights, *saved,
+      lean ? moe::launch_experts_bwd_recompute(d, dy_perm, x, offsets, *weights, *saved,
                                                dx_perm, *grads, base, ws, as_stream(stream),
                                                moe::active_timer())
-           : moe::launch_experts_bwd(d, dy_perm, x_perm, offsets, *weights, *saved, dx_perm,
+           : moe::launch_experts_bwd(d, dy_perm, x, offsets, *weights, *saved, dx_perm,
                                      *grads, base, ws, as_stream(stream), moe::active_timer());
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
 }
@@ -488,17 +515,22 @@ moe_status moe_grouped_lora_bwd_recompute(const moe_shape* shape, const void* dy
                      weights, saved, dx_perm, grads, base, ws, ws_bytes, stream);
 }
 
-moe_status moe_grouped_lora_combine_bwd(const moe_shape* shape, const void* dy,
-                                        const float* topk_w, const int32_t* sorted_pair,
-                                        const int32_t* inv_pos, const void* x_perm,
-                                        const int32_t* offsets, const moe_weights* weights,
-                                        const moe_saved* saved, int32_t recompute,
-                                        void* dy_perm, void* dx_perm,
-                                        const moe_lora_grads* grads, const moe_base_grads* base,
-                                        float* d_topk_w, void* ws, size_t ws_bytes,
-                                        void* stream) {
+namespace {
+
+// gather: x_perm is x in token order, its rows read through sorted_pair
+moe_status combine_bwd_impl(const char* name, bool gather, const moe_shape* shape,
+                            const void* dy, const float* topk_w, const int32_t* sorted_pair,
+                            const int32_t* inv_pos, const void* x_perm, const int32_t* offsets,
+                            const moe_weights* weights, const moe_saved* saved, int32_t recompute,
+                            void* dy_perm, void* dx_perm, const moe_lora_grads* grads,
+                            const moe_base_grads* base, float* d_topk_w, void* ws,
+                            size_t ws_bytes, void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
+  if (gather) {
+    st = check_gather(shape, sorted_pair);
+    if (st != MOE_OK) return st;
+  }
   CHECK_PTR(dy);
   CHECK_PTR(topk_w);
   CHECK_PTR(sorted_pair);
@@ -523,14 +555,45 @@ moe_status moe_grouped_lora_combine_bwd(const moe_shape* shape, const void* dy,
   cb.T = shape->T;
   cb.k = shape->k;
   cb.d_topk_w = d_topk_w;
+  const moe::XRows x{x_perm, gather ? sorted_pair : nullptr, shape->k, shape->T};
   hipError_t e =
-      lean ? moe::launch_experts_bwd_recompute(d, dy_perm, x_perm, offsets, *weights, *saved,
+      lean ? moe::launch_experts_bwd_recompute(d, dy_perm, x, offsets, *weights, *saved,
                                                dx_perm, *grads, base, ws, as_stream(stream),
                                                moe::active_timer(), &cb)
-           : moe::launch_experts_bwd(d, dy_perm, x_perm, offsets, *weights, *saved, dx_perm,
+           : moe::launch_experts_bwd(d, dy_perm, x, offsets, *weights, *saved, dx_perm,
                                      *grads, base, ws, as_stream(stream), moe::active_timer(),
                                      &cb);
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_lora_combine_bwd");
+  return e == hipSuccess ? MOE_OK : hip_fail(e, name);
+}
+
+}  // namespace
+
+moe_status moe_grouped_lora_combine_bwd(const moe_shape* shape, const void* dy,
+                                        const float* topk_w, const int32_t* sorted_pair,
+                                        const int32_t* inv_pos, const void* x_perm,
+                                        const int32_t* offsets, const moe_weights* weights,
+                                        const moe_saved* saved, int32_t recompute,
+                                        void* dy_perm, void* dx_perm,
+                                        const moe_lora_grads* grads, const moe_base_grads* base,
+                                        float* d_topk_w, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  return combine_bwd_impl("moe_grouped_lora_combine_bwd", false, shape, dy, topk_w, sorted_pair,
+                          inv_pos, x_perm, offsets, weights, saved, recompute, dy_perm, dx_perm,
+                          grads, base, d_topk_w, ws, ws_bytes, stream);
+}
+
+moe_status moe_grouped_lora_combine_bwd_gather(const moe_shape* shape, const void* dy,
+                                               const float* topk_w, const int32_t* sorted_pair,
+                                               const int32_t* inv_pos, const void* x,
+                                               const int32_t* offsets, const moe_weights* weights,
+                                               const moe_saved* saved, int32_t recompute,
+                                               void* dy_perm, void* dx_perm,
+                                               const moe_lora_grads* grads,
+                                               const moe_base_grads* base, float* d_topk_w,
+                                               void* ws, size_t ws_bytes, void* stream) {
+  return combine_bwd_impl("moe_grouped_lora_combine_bwd_gather", true, shape, dy, topk_w,
+                          sorted_pair, inv_pos, x, offsets, weights, saved, recompute, dy_perm,
+                          dx_perm, grads, base, d_topk_w, ws, ws_bytes, stream);
 }
 
 namespace {

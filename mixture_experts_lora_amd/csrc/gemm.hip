@@ -59,6 +59,14 @@ struct Opnd {
   int64_t ld;       // leading dimension in elements
   int kcontig;      // 1: (mn, k) at ptr[mn*ld + k]; 0: at ptr[k*ld + mn]
   int vec;          // 16-byte chunks allowed (alignment and extents are multiples of 8)
+  // Gathered rows (the layer input read in token order): row i of the
+  // permuted order is row rows[i] / rows_div of ptr, which holds rows_bytes
+  // bytes. Null rows: the operand's rows are in permuted order. Only the A
+  // operand of GROUP_M (rows along mn) and the B operand of GROUP_K (rows
+  // along k) are ever gathered.
+  const int32_t* rows;
+  int rows_div;
+  int64_t rows_bytes;
 };
 
 struct GemmArgs {
@@ -130,6 +138,10 @@ struct View {
   int mn_lim;  // valid local mn in [0, mn_lim) (simple mapping)
   int paired;  // gate_up weight rows: local n < half -> gate row pbase+n, else up row I+pbase+n-half
   int half, pbase, I;
+  // gathered rows (Opnd::rows from this tile's first row on, and its divisor):
+  // mn (k-contiguous) or k (output-contiguous) index i is row grow[i] / gk of base
+  const int32_t* grow;
+  int gk;
 };
 
 template <typename T>
@@ -144,11 +156,18 @@ __device__ __forceinline__ int64_t map_mn(const View<T>& v, int n, bool& ok) {
 }
 
 template <typename T>
+__device__ __forceinline__ int64_t gathered_row(const View<T>& v, int64_t i) {
+  return v.grow ? static_cast<int64_t>(static_cast<uint32_t>(v.grow[i]) / static_cast<uint32_t>(v.gk))
+                : i;
+}
+
+template <typename T>
 __device__ __forceinline__ T load_elem(const View<T>& v, int n, int k) {
   bool ok;
   const int64_t g = map_mn(v, n, ok);
   if (!ok || k >= v.klim) return T(0);
-  return v.kcontig ? v.base[g * v.ld + k] : v.base[static_cast<int64_t>(k) * v.ld + g];
+  return v.kcontig ? v.base[gathered_row(v, g) * v.ld + k]
+                   : v.base[gathered_row(v, k) * v.ld + g];
 }
 
 // ----------------------------------------------------------------- epilogue helpers
@@ -339,10 +358,11 @@ __device__ __forceinline__ void make_plan(Plan<ROWS, BK, KC, NW>& P, const View<
       const int c = p ^ kswz<BK>(r);
       bool ok;
       const int64_t g = map_mn(v, r, ok);
-      if (ok && r < ROWS) vo = static_cast<uint32_t>((g * v.ld + c * 8) * 2);
+      if (ok && r < ROWS) vo = static_cast<uint32_t>((gathered_row(v, g) * v.ld + c * 8) * 2);
     } else {
+      // gathered: the offsets depend on the k tile's rows (gather_vo)
       const int cn = p ^ nswz<ROWS>(r);
-      if (cn * 8 < v.mn_lim && r < BK) vo = static_cast<uint32_t>((r * v.ld + cn * 8) * 2);
+      if (cn * 8 < v.mn_lim && r < BK && !v.grow) vo = static_cast<uint32_t>((r * v.ld + cn * 8) * 2);
     }
     P.vo[i] = vo;
   }
@@ -362,14 +382,48 @@ __device__ __forceinline__ u32x4 tile_rsrc(const Plan<ROWS, BK, KC, NW>& P, int 
     return P.rs;
   }
   soff = 0;
+  if (P.view.grow) return P.rs;  // gathered rows: per-lane offsets from the start
   const int64_t adv = static_cast<int64_t>(k0) * P.ld * 2;
   return buffer_rsrc(static_cast<const char*>(P.base) + adv, clamp_records(P.bytes - adv));
+}
+
+// Lane offset of instruction j of an output-contiguous tile at k0 whose rows
+// are gathered: the instruction covers the tile's k rows RPI*j .. RPI*j+RPI-1
+// (wave-uniform), whose row numbers come in through scalar loads (constant
+// address space: they go through the scalar cache and are counted apart from
+// the DMA loads in flight), so the DMA pipeline's vector-memory waits stay
+// exact. table (optional): the byte offsets of the block's rows from row tw0
+// on, in LDS (read instead of the scalar loads).
+template <int ROWS, int BK, bool KC, int NW>
+__device__ __forceinline__ uint32_t gather_vo(const Plan<ROWS, BK, KC, NW>& P, int k0, int j,
+                                              int lane, const uint32_t* table = nullptr,
+                                              int tw0 = 0) {
+  typedef Geo<ROWS, BK, KC, NW> G;
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  if (P.klim <= 0) return kOOB;
+  const int r0 = k0 + G::RPI * j, last = P.klim - 1, t = lane / G::CPR;
+  const int cn = (lane % G::CPR) ^ nswz<ROWS>(G::RPI * j + t);
+  if (table) {
+    const uint32_t off = table[min(r0 + t, last) - tw0];
+    if (r0 + t > last || cn * 8 >= P.view.mn_lim) return kOOB;
+    return off + static_cast<uint32_t>(cn) * 16;
+  }
+  const cptr rows = (cptr)(P.view.grow);
+  int sp = 0;
+#pragma unroll
+  for (int q = 0; q < G::RPI; ++q) {
+    const int v = rows[min(r0 + q, last)];
+    if (t == q) sp = v;
+  }
+  if (r0 + t > last || cn * 8 >= P.view.mn_lim) return kOOB;
+  const uint32_t row = static_cast<uint32_t>(sp) / static_cast<uint32_t>(P.view.gk);
+  return static_cast<uint32_t>((static_cast<int64_t>(row) * P.ld + cn * 8) * 2);
 }
 
 // Issue one tile: DMA when possible, else an element-wise fill.
 template <int ROWS, int BK, bool KC, int NW>
 __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC, NW>& P, int k0, char* lds, int wave,
-                                     int lane) {
+                                     int lane, const uint32_t* gtab = nullptr, int tw0 = 0) {
   typedef Geo<ROWS, BK, KC, NW> G;
   if (P.vec) {
     uint32_t soff;
@@ -380,6 +434,7 @@ __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC, NW>& P, int k0, ch
       const int j = wave + NW * i;
       if (G::TI % NW == 0 || j < G::TI) {
         uint32_t vo = P.vo[i];
+        if (!KC && P.view.grow) vo = gather_vo(P, k0, j, lane, gtab, tw0);
         if (tail) {
           const int r = G::RPI * j + lane / G::CPR;
           const int c = (lane % G::CPR) ^ kswz<BK>(r);
@@ -408,15 +463,17 @@ __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC, NW>& P, int k0, ch
 }
 
 // One DMA instruction (index i of this wave's share) of a tile; DMA plans only.
+// gvo: the lane offset when the caller has formed it already (gathered rows)
 template <int ROWS, int BK, bool KC, int NW>
 __device__ __forceinline__ void fill_one(const Plan<ROWS, BK, KC, NW>& P, int k0, char* lds,
-                                         int wave, int lane, int i) {
+                                         int wave, int lane, int i, int64_t gvo = -1) {
   typedef Geo<ROWS, BK, KC, NW> G;
   const int j = wave + NW * i;
   if (G::TI % NW != 0 && j >= G::TI) return;
   uint32_t soff;
   const u32x4 rs = tile_rsrc(P, k0, soff);
   uint32_t vo = P.vo[i];
+  if (!KC && P.view.grow) vo = gvo >= 0 ? static_cast<uint32_t>(gvo) : gather_vo(P, k0, j, lane);
   if (KC && k0 + BK > P.klim) {  // k tail of a k-contiguous operand: mask by lane
     const int r = G::RPI * j + lane / G::CPR;
     const int c = (lane % G::CPR) ^ kswz<BK>(r);
@@ -587,7 +644,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
                 "vmcnt range");
   // GROUP_KV: + the block's [BM][32] tile of the side-product B
   constexpr int VB_BYTES = MODE == GROUP_KV ? BM * 32 * 2 : 0;
-  __shared__ __attribute__((aligned(1024))) char smem[NST * ST + VB_BYTES];
+  // GROUP_K with a gathered, output-contiguous B (the LoRA A gradient over
+  // x's rows): byte offsets of up to GT_ROWS of the block's rows, formed once
+  constexpr int GT_ROWS = MODE == GROUP_K && !B_KC && BM <= 32 && VST == 0 ? 4096 : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * ST + VB_BYTES + GT_ROWS * 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a wave-uniform (scalar) value, so that everything derived
@@ -646,6 +706,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
       va.klim = K;
       va.mn_lim = rows;
       abytes = static_cast<int64_t>(rows) * A.ld * 2;
+      if (A.rows) {
+        va.base = static_cast<const bf16_t*>(A.ptr);
+        va.grow = A.rows + row0;
+        va.gk = A.rows_div;
+        abytes = A.rows_bytes;
+      }
       const bf16_t* wb = static_cast<const bf16_t*>(B.ptr) + static_cast<int64_t>(e) * B.estride;
       vb.klim = K;
       if (PAIRED) {
@@ -674,6 +740,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
       vb.klim = krows;
       vb.mn_lim = p.N - n0;
       bbytes = static_cast<int64_t>(krows) * B.ld * 2 - static_cast<int64_t>(n0) * 2;
+      if (B.rows) {
+        vb.base = static_cast<const bf16_t*>(B.ptr) + n0;
+        vb.grow = B.rows + row0;
+        vb.gk = B.rows_div;
+        bbytes = B.rows_bytes - static_cast<int64_t>(n0) * 2;
+      }
     }
     make_plan<BM, BK, A_KC, NW>(PA, va, abytes, A.vec, wave, lane);
     make_plan<BN, BK, B_KC, NW>(PB, vb, bbytes, B.vec, wave, lane);
@@ -691,12 +763,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
   const int nk = nk0 + nk1;
   const bool dma0 = pa0.vec && pb0.vec, dma1 = pa1.vec && pb1.vec;
 
+  // GROUP_K with gathered B rows: their byte offsets in LDS, when formed, for
+  // the rows from gw0 on
+  const uint32_t* gtab = nullptr;
+  int gw0 = 0;
   auto issue = [&](int j) {  // a whole stage at once (prologue, element-wise fills)
     char* sa = smem + (j % NST) * ST;
     char* sb = sa + A_BYTES;
     if (j < nk0) {
       fill<BM, BK, A_KC, NW>(pa0, j * BK, sa, wave, lane);
-      fill<BN, BK, B_KC, NW>(pb0, j * BK, sb, wave, lane);
+      fill<BN, BK, B_KC, NW>(pb0, j * BK, sb, wave, lane, gtab, gw0);
     } else {
       fill<BM, BK, A_KC, NW>(pa1, (j - nk0) * BK, sa, wave, lane);
       fill<BN, BK, B_KC, NW>(pb1, (j - nk0) * BK, sb, wave, lane);
@@ -1033,9 +1109,38 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
     if (live) kloop(std::true_type());
     else kloop(std::false_type());
   } else {
+    // Gathered B rows (GROUP_K): the lane offsets of a refill depend on its
+    // rows' numbers, so they are formed one iteration ahead (their scalar
+    // loads then complete under a k tile of MFMAs instead of delaying the
+    // refill's DMA issue).
+    const bool gath = MODE == GROUP_K && !B_KC && pb0.view.grow != nullptr;
+    uint32_t gvo[GB::NIW];
+    // The rows' byte offsets, GT_ROWS at a time from row gw0 on: formed before
+    // the first DMA, and again (rare: experts of more than GT_ROWS rows) when
+    // a refill passes the window, which then waits for the DMA in flight.
+    uint32_t* gt = reinterpret_cast<uint32_t*>(smem + NST * ST + VB_BYTES);
+    auto gather_window = [&](int w0) __attribute__((always_inline)) {
+      __syncthreads();
+      for (int i = tid; i < GT_ROWS && w0 + i < krows; i += NW * 64)
+        gt[i] = static_cast<uint32_t>(pb0.view.grow[w0 + i]) /
+                static_cast<uint32_t>(pb0.view.gk) * static_cast<uint32_t>(pb0.ld) * 2u;
+      __syncthreads();
+      gw0 = w0;
+    };
+    if (GT_ROWS > 0 && gath) {
+      gather_window(0);
+      gtab = gt;
+    }
+    auto gather_plan = [&](int j) __attribute__((always_inline)) {
+      if (gtab && (j + 1) * BK > gw0 + GT_ROWS) gather_window(j * BK);
+#pragma unroll
+      for (int i = 0; i < GB::NIW; ++i)
+        gvo[i] = gather_vo(pb0, j * BK, wave + NW * i, lane, gtab, gw0);
+    };
   #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
       if (s < nk) issue(s);
+    if (gath && NST - 1 < nk) gather_plan(NST - 1);
     for (int it = 0; it < nk; ++it) {
       // stage `it` must have landed; the DMA-only stages after it may stay in flight
       {
@@ -1069,6 +1174,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
       const char* sb = sa + A_BYTES;
       constexpr int KS = BK / 16;
       constexpr int NT = GA::NIW + GB::NIW;
+      uint32_t gcur[GB::NIW];
+#pragma unroll
+      for (int i = 0; i < GB::NIW; ++i) gcur[i] = gvo[i];
+      if (gath && jn + 1 < nk) gather_plan(jn + 1);
       // Fragments are double-buffered in registers: the LDS reads of k-step
       // ks+1 are in flight while the MFMAs of k-step ks run.
       bf16x8 af[2][MF], bf[2][NF];
@@ -1092,6 +1201,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
           for (int t = ks * NT / KS; t < (ks + 1) * NT / KS; ++t) {
             if (t < GA::NIW)
               fill_one<BM, BK, A_KC, NW>(PA, k0n, san, wave, lane, t);
+            else if (gath)
+              fill_one<BN, BK, B_KC, NW>(PB, k0n, sbn, wave, lane, t - GA::NIW, gcur[t - GA::NIW]);
             else
               fill_one<BN, BK, B_KC, NW>(PB, k0n, sbn, wave, lane, t - GA::NIW);
           }
@@ -1350,6 +1461,11 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs p) {
       K = p.K[seg];
       va.base = static_cast<const float*>(A.ptr) + row0 * A.ld;
       va.mn_lim = rows;
+      if (A.rows) {
+        va.base = static_cast<const float*>(A.ptr);
+        va.grow = A.rows + row0;
+        va.gk = A.rows_div;
+      }
       const float* wb = static_cast<const float*>(B.ptr) + static_cast<int64_t>(e) * B.estride;
       if (PAIRED) {
         vb.base = wb; vb.paired = 1; vb.half = BN; vb.pbase = n_tile * BN; vb.I = p.I;
@@ -1364,6 +1480,11 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs p) {
       va.mn_lim = p.M - m0;
       vb.base = static_cast<const float*>(B.ptr) + row0 * B.ld + n0;
       vb.mn_lim = p.N - n0;
+      if (B.rows) {
+        vb.base = static_cast<const float*>(B.ptr) + n0;
+        vb.grow = B.rows + row0;
+        vb.gk = B.rows_div;
+      }
     }
     va.klim = K;
     vb.klim = K;
@@ -1502,10 +1623,27 @@ Opnd opnd(const void* ptr, int64_t estride, int64_t ld, int kcontig, bool vec_ok
   o.ld = ld;
   o.kcontig = kcontig;
   o.vec = vec_ok && (ld % 8 == 0) && aligned16(ptr) && (estride % 8 == 0);
+  o.rows = nullptr;
+  o.rows_div = 1;
+  o.rows_bytes = 0;
   return o;
 }
 
-Opnd none() { return Opnd{nullptr, 0, 0, 1, 0}; }
+Opnd none() { return Opnd{nullptr, 0, 0, 1, 0, nullptr, 1, 0}; }
+
+inline int esz_of(const ExpertDims& d) { return d.dtype == MOE_F32 ? 4 : 2; }
+
+// The layer input [rows, ld] as an operand: x_perm as it is, or x in token
+// order read through sorted_pair.
+Opnd opnd_x(const XRows& x, int64_t ld, int kcontig, int esz) {
+  Opnd o = opnd(x.ptr, 0, ld, kcontig, true);
+  if (x.rows) {
+    o.rows = x.rows;
+    o.rows_div = x.k;
+    o.rows_bytes = static_cast<int64_t>(x.T) * ld * esz;
+  }
+  return o;
+}
 
 // Tile list capacity for `bm`-row tiles.
 inline int64_t tile_cap(int64_t N, int E, int bm) { return (N + bm - 1) / bm + E + 1; }
@@ -1622,12 +1760,12 @@ GemmArgs base_args(const ExpertDims& d, const int32_t* offsets, const TileList& 
 
 // out[rows, r] = scale * A[rows, K] * L_e (L_e is [r, K] when l_kcontig, else [K, r]).
 hipError_t side_product(const ExpertDims& d, const int32_t* offsets, const WsLayout& L,
-                        const void* A, int K, const void* Lw, int64_t l_estride, int l_kcontig,
+                        const Opnd& A, int K, const void* Lw, int64_t l_estride, int l_kcontig,
                         void* out, hipStream_t s) {
   const TileList& t = L.small;
   GemmArgs a = base_args(d, offsets, t);
   const bool r_vec = d.r % 8 == 0;
-  a.a[0] = opnd(A, 0, K, 1, true);
+  a.a[0] = A;
   a.b[0] = l_kcontig ? opnd(Lw, l_estride, K, 1, true) : opnd(Lw, l_estride, d.r, 0, r_vec);
   a.K[0] = K;
   a.K[1] = 0;
@@ -1871,7 +2009,7 @@ hipError_t scale_rows(int dtype, const void* src, const float* w, int64_t rows, 
 // side (optional, side_fusable only): also form V = scale D Bm.
 hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* Lm, int P,
                        const void* Rm, int Q, void* out, hipStream_t s, void* split_ws,
-                       const SideOut* side = nullptr) {
+                       const SideOut* side = nullptr, const XRows* rx = nullptr) {
   GemmArgs a{};
   a.vsplit = 1;
   if (side) {
@@ -1889,7 +2027,7 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
   a.out_estride = static_cast<int64_t>(P) * Q;
   a.ld_out = Q;
   a.a[0] = opnd(Lm, 0, P, 0, P % 8 == 0);
-  a.b[0] = opnd(Rm, 0, Q, 0, Q % 8 == 0);
+  a.b[0] = rx ? opnd_x(*rx, Q, 0, esz_of(d)) : opnd(Rm, 0, Q, 0, Q % 8 == 0);
   const int S = split_ws ? wgrad_splits(d, P, Q) : 1;
   auto side_sum = [&]() -> hipError_t {
     if (!side) return hipSuccess;
@@ -2006,12 +2144,12 @@ size_t experts_bwd_ws_bytes(const ExpertDims& d) { return bwd_ws(nullptr, d).byt
 namespace {
 
 // h = X W_gu^T + u_gu B_gu^T ; act = SwiGLU(h)   (tile lists already built)
-hipError_t launch_gate_up(const ExpertDims& d, const WsLayout& L, const void* x_perm,
+hipError_t launch_gate_up(const ExpertDims& d, const WsLayout& L, const XRows& x,
                           const int32_t* offsets, const moe_weights& w, const void* u_gu,
                           void* h, void* act, hipStream_t s, KernelTimer* tm) {
   const int H = d.H, I = d.I, r = d.r;
   GemmArgs a = base_args(d, offsets, L.big);
-  a.a[0] = opnd(x_perm, 0, H, 1, true);
+  a.a[0] = opnd_x(x, H, 1, esz_of(d));
   a.b[0] = opnd(w.w_gu, static_cast<int64_t>(2) * I * H, H, 1, true);
   a.a[1] = opnd(u_gu, 0, r, 1, r % 8 == 0);
   a.b[1] = opnd(w.b_gu, static_cast<int64_t>(2) * I * r, r, 1, r % 8 == 0);
@@ -2050,7 +2188,7 @@ inline moe_saved lean_saved(const ExpertDims& d, const moe_saved& sv, void* ws, 
 
 }  // namespace
 
-hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int32_t* offsets,
+hipError_t launch_experts_fwd(const ExpertDims& d, const XRows& x, const int32_t* offsets,
                               const moe_weights& w, const moe_saved& sv, void* ws,
                               hipStream_t s, KernelTimer* tm) {
   const WsLayout L = tile_ws(ws, d);
@@ -2058,14 +2196,14 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
   MOE_TRY(build_tiles(L, offsets, d.E, s));
   {  // u_gu = s X A_gu^T
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
-    MOE_TRY(side_product(d, offsets, L, x_perm, H, w.a_gu, static_cast<int64_t>(r) * H, 1,
-                         sv.u_gu, s));
+    MOE_TRY(side_product(d, offsets, L, opnd_x(x, H, 1, esz_of(d)), H, w.a_gu,
+                         static_cast<int64_t>(r) * H, 1, sv.u_gu, s));
   }
-  MOE_TRY(launch_gate_up(d, L, x_perm, offsets, w, sv.u_gu, sv.h, sv.act, s, tm));
+  MOE_TRY(launch_gate_up(d, L, x, offsets, w, sv.u_gu, sv.h, sv.act, s, tm));
   {  // u_d = s act A_d^T
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
-    MOE_TRY(side_product(d, offsets, L, sv.act, I, w.a_d, static_cast<int64_t>(r) * I, 1,
-                         sv.u_d, s));
+    MOE_TRY(side_product(d, offsets, L, opnd(sv.act, 0, I, 1, true), I, w.a_d,
+                         static_cast<int64_t>(r) * I, 1, sv.u_d, s));
   }
   {  // y_exp = act W_d^T + u_d B_d^T
     GemmArgs a = base_args(d, offsets, L.big);
@@ -2091,7 +2229,7 @@ hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int
   return hipSuccess;
 }
 
-hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_perm,
+hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const XRows& x,
                               const int32_t* offsets, const moe_weights& w,
                               const moe_saved& sv, void* dx_perm, const moe_lora_grads& gr,
                               const moe_base_grads* base, void* ws, hipStream_t s,
@@ -2143,7 +2281,8 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     MOE_TRY(weight_grad(d, offsets, g, H, ud_eff, r, gr.db_d, s, split, &so));
   } else {  // gb = s G B_d      (B_d[e] is [H, r]: K = H rows, r contiguous)
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
-    MOE_TRY(side_product(d, offsets, L, g, H, w.b_d, static_cast<int64_t>(H) * r, 0, gb, s));
+    MOE_TRY(side_product(d, offsets, L, opnd(g, 0, H, 1, true), H, w.b_d,
+                         static_cast<int64_t>(H) * r, 0, gb, s));
     if (cb) MOE_TRY(scale_rows(d.dtype, gb, B.w_perm, d.N, r, B.gbw, s));
   }
   {  // dAct = G W_d + gb A_d ; dH = SwiGLU'(h) dAct
@@ -2201,8 +2340,8 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
     MOE_TRY(weight_grad(d, offsets, dh, 2 * I, sv.u_gu, r, gr.db_gu, s, split, &so));
   } else {  // dhb = s dH B_gu   (B_gu[e] is [2I, r])
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
-    MOE_TRY(side_product(d, offsets, L, dh, 2 * I, w.b_gu, static_cast<int64_t>(2) * I * r, 0,
-                         dhb, s));
+    MOE_TRY(side_product(d, offsets, L, opnd(dh, 0, 2 * I, 1, true), 2 * I, w.b_gu,
+                         static_cast<int64_t>(2) * I * r, 0, dhb, s));
   }
   {  // dX = dH W_gu + dhb A_gu
     GemmArgs a = base_args(d, offsets, L.big);
@@ -2228,11 +2367,11 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
   {  // dB_gu = dH^T u_gu  [2I, r] (unless fused above) ;  dA_gu = dhb^T X  [r, H]
     TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
     if (!fuse_gu) MOE_TRY(weight_grad(d, offsets, dh, 2 * I, sv.u_gu, r, gr.db_gu, s, split));
-    MOE_TRY(weight_grad(d, offsets, dhb, r, x_perm, H, gr.da_gu, s, split));
+    MOE_TRY(weight_grad(d, offsets, dhb, r, x.ptr, H, gr.da_gu, s, split, nullptr, &x));
   }
   if (base) {  // full fine-tuning: dW_gu = dH^T X  [2I, H]
     TimedScope ts(tm, MOE_K_BASE_WGRAD, s);
-    MOE_TRY(weight_grad(d, offsets, dh, 2 * I, x_perm, H, base->dw_gu, s, nullptr));
+    MOE_TRY(weight_grad(d, offsets, dh, 2 * I, x.ptr, H, base->dw_gu, s, nullptr, nullptr, &x));
   }
   return hipSuccess;
 }
@@ -2245,15 +2384,15 @@ size_t experts_bwd_lean_ws_bytes(const ExpertDims& d) {
   return align_up(experts_bwd_ws_bytes(d)) + lean_extra_bytes(d);
 }
 
-hipError_t launch_experts_fwd_lean(const ExpertDims& d, const void* x_perm,
+hipError_t launch_experts_fwd_lean(const ExpertDims& d, const XRows& x,
                                    const int32_t* offsets, const moe_weights& w,
                                    const moe_saved& sv, void* ws, hipStream_t s,
                                    KernelTimer* tm) {
   const moe_saved full = lean_saved(d, sv, ws, experts_fwd_ws_bytes(d));
-  return launch_experts_fwd(d, x_perm, offsets, w, full, ws, s, tm);
+  return launch_experts_fwd(d, x, offsets, w, full, ws, s, tm);
 }
 
-hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, const void* x_perm,
+hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, const XRows& x,
                                         const int32_t* offsets, const moe_weights& w,
                                         const moe_saved& sv, void* dx_perm,
                                         const moe_lora_grads& gr, const moe_base_grads* base,
@@ -2262,8 +2401,8 @@ hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, cons
   const moe_saved full = lean_saved(d, sv, ws, experts_bwd_ws_bytes(d));
   const WsLayout L = tile_ws(ws, d);
   MOE_TRY(build_tiles(L, offsets, d.E, s));
-  MOE_TRY(launch_gate_up(d, L, x_perm, offsets, w, sv.u_gu, full.h, full.act, s, tm));
-  return launch_experts_bwd(d, g, x_perm, offsets, w, full, dx_perm, gr, base, ws, s, tm, cb);
+  MOE_TRY(launch_gate_up(d, L, x, offsets, w, sv.u_gu, full.h, full.act, s, tm));
+  return launch_experts_bwd(d, g, x, offsets, w, full, dx_perm, gr, base, ws, s, tm, cb);
 }
 
 // ----------------------------------------------------------------- router projection

@@ -66,6 +66,15 @@ hipError_t launch_dw_sum(const float* dwp, int slots, const int32_t* inv_pos, in
                          float* d_topk_w, hipStream_t s);
 
 // ---- grouped expert GEMMs
+// The layer input as the expert GEMMs read it: x_perm [N, H] in permuted
+// order (rows null), or x [T, H] in token order, row i of the permuted order
+// being token rows[i] / k (rows = sorted_pair; the GEMMs gather it).
+struct XRows {
+  const void* ptr;
+  const int32_t* rows;
+  int k, T;
+};
+
 struct ExpertDims {
   int64_t N;  // routed rows
   int H, I, E, r, dtype;
@@ -75,7 +84,7 @@ struct ExpertDims {
 size_t experts_fwd_ws_bytes(const ExpertDims& d);
 size_t experts_bwd_ws_bytes(const ExpertDims& d);
 
-hipError_t launch_experts_fwd(const ExpertDims& d, const void* x_perm, const int32_t* offsets,
+hipError_t launch_experts_fwd(const ExpertDims& d, const XRows& x, const int32_t* offsets,
                               const moe_weights& w, const moe_saved& sv, void* ws,
                               hipStream_t s, KernelTimer* tm);
 // The combine backward folded into the experts' backward: G = w dY is never
@@ -95,7 +104,7 @@ struct CombineBwd {
 // `base` may be null (LoRA only); otherwise the base-weight gradients are written too.
 // `cb` null: g holds G = w dY rows (read only). Otherwise g is an [N, H]
 // buffer the call fills with dY's rows, and cb's d_topk_w is written.
-hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_perm,
+hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const XRows& x,
                               const int32_t* offsets, const moe_weights& w,
                               const moe_saved& sv, void* dx_perm, const moe_lora_grads& gr,
                               const moe_base_grads* base, void* ws, hipStream_t s,
@@ -105,11 +114,11 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const void* x_
 // workspace instead of `saved`; the backward recomputes them into its own.
 size_t experts_fwd_lean_ws_bytes(const ExpertDims& d);
 size_t experts_bwd_lean_ws_bytes(const ExpertDims& d);
-hipError_t launch_experts_fwd_lean(const ExpertDims& d, const void* x_perm,
+hipError_t launch_experts_fwd_lean(const ExpertDims& d, const XRows& x,
                                    const int32_t* offsets, const moe_weights& w,
                                    const moe_saved& sv, void* ws, hipStream_t s,
                                    KernelTimer* tm);
-hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, const void* x_perm,
+hipError_t launch_experts_bwd_recompute(const ExpertDims& d, const void* g, const XRows& x,
                                         const int32_t* offsets, const moe_weights& w,
                                         const moe_saved& sv, void* dx_perm,
                                         const moe_lora_grads& gr, const moe_base_grads* base,

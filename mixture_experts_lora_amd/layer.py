@@ -3,15 +3,17 @@
 MoELoRALayer owns every buffer of one layer shape (allocated once with torch,
 so nothing is allocated inside a step) and issues, on torch's current stream:
 
-  forward   moe_route -> moe_permute (+ gather) -> moe_grouped_lora_fwd
-            -> moe_unpermute_combine
-  backward  moe_grouped_lora_combine_bwd (the combine backward folded into
-            the experts' backward: d_topk_w from the down backward, no G)
+  forward   moe_route -> moe_permute (indices only) -> moe_grouped_lora_fwd_gather
+            (the GEMMs read x's rows through sorted_pair) -> moe_unpermute_combine
+  backward  moe_grouped_lora_combine_bwd_gather (the combine backward folded
+            into the experts' backward: d_topk_w from the down backward, no G)
             -> moe_route_bwd -> moe_unpermute_combine (weights 1: dX_perm
             summed back to tokens)
-  With fold_combine_bwd=False the backward runs the separate calls
-  moe_unpermute_combine_bwd -> moe_route_bwd -> moe_grouped_lora_bwd, which
-  read the expert outputs y_exp, so those are then kept from the forward.
+  With gather_x=False, moe_permute also gathers x_perm and the calls without
+  _gather read it. With fold_combine_bwd=False the backward runs the separate
+  calls moe_unpermute_combine_bwd -> moe_route_bwd -> moe_grouped_lora_bwd
+  (on x_perm), which read the expert outputs y_exp, so those are then kept
+  from the forward.
 
 MoELoRAFunction wraps the same calls as a torch.autograd.Function whose
 gradients are dX, d logits and the four LoRA gradients (base weights frozen).
@@ -32,7 +34,8 @@ from __future__ import annotations
 import torch
 
 from . import (Shape, moe_accumulate, moe_grouped_full_bwd, moe_grouped_lora_bwd,
-               moe_grouped_lora_combine_bwd,
+               moe_grouped_lora_combine_bwd, moe_grouped_lora_combine_bwd_gather,
+               moe_grouped_lora_fwd_gather,
                moe_grouped_lora_bwd_recompute, moe_grouped_lora_fwd, moe_grouped_lora_fwd_lean,
                moe_permute, moe_route, moe_route_bwd, moe_router_bwd, moe_router_fwd,
                moe_router_workspace_bytes, moe_unpermute_combine, moe_unpermute_combine_bwd,
@@ -45,12 +48,13 @@ GRAD_NAMES = ("da_gu", "db_gu", "da_d", "db_d")
 class LayerScratch:
     """Buffers a layer needs only while one of its calls runs: the workspace
     shared by forward and backward, the permute workspace, the permuted
-    gradient rows (G and dX_perm), d_topk_w and, in the activation-lean mode,
-    x_perm (the backward gathers it again). Several layers or chunks that run
+    gradient rows (G and dX_perm), d_topk_w and, in the activation-lean mode
+    with x_perm (x_perm_rows), x_perm (the backward gathers it again). Several
+    layers or chunks that run
     one after another can share one LayerScratch; it is sized for the largest
     shape passed in and handed out as views."""
 
-    def __init__(self, shapes, recompute: bool, device="cuda"):
+    def __init__(self, shapes, recompute: bool, device="cuda", x_perm_rows: bool = True):
         shapes = list(shapes)
         es = max(s.torch_dtype.itemsize for s in shapes)
         ws = perm = rows = tk = 0
@@ -64,7 +68,7 @@ class LayerScratch:
         u8 = dict(device=device, dtype=torch.uint8)
         self.ws = torch.empty(max(ws, 1), **u8)
         self.ws_perm = torch.empty(max(perm, 1), **u8)
-        nrow = 3 if recompute else 2          # G, dX_perm (+ x_perm)
+        nrow = 3 if recompute and x_perm_rows else 2          # G, dX_perm (+ x_perm)
         self.rows = torch.empty(max(nrow * rows * es, 1), **u8)
         self.rows_each = rows * es
         self.d_topk_w = torch.empty(max(tk, 1), device=device, dtype=torch.float32)
@@ -79,6 +83,11 @@ class LayerScratch:
         return b.view(shape.torch_dtype).view(shape.N, shape.H)
 
 
+def _gatherable(shape: Shape) -> bool:
+    """The GEMMs read x's rows through sorted_pair when x is below 2 GiB."""
+    return shape.T * shape.H * shape.torch_dtype.itemsize < (1 << 31)
+
+
 class MoELoRALayer:
     """full_ft=True also computes the base-weight gradients (full fine-tuning).
     recompute=True is the activation-lean mode: h and act are not kept between
@@ -91,6 +100,10 @@ class MoELoRALayer:
     (held in the scratch rows the backward later uses for dY's rows) rather
     than a saved activation.
 
+    gather_x=True (the default, with fold_combine_bwd, for x below 2 GiB): the
+    expert GEMMs read x's rows in token order through sorted_pair, so x_perm
+    is never formed (no gather pass, nothing of it held); backward() needs x.
+
     scratch: a LayerScratch to share with other layers or chunks (one is made
     when None). out: optional views {"y", "dx", "d_logits"} to write the
     outputs into (a chunk writes its rows of the whole layer's outputs).
@@ -99,21 +112,26 @@ class MoELoRALayer:
     def __init__(self, shape: Shape, router: str, device="cuda", full_ft: bool = False,
                  recompute: bool = False, scratch: LayerScratch | None = None,
                  out: dict | None = None, grads: dict | None = None,
-                 base_grads: dict | None = None, fold_combine_bwd: bool = True):
+                 base_grads: dict | None = None, fold_combine_bwd: bool = True,
+                 gather_x: bool = True):
         self.shape, self.router, self.full_ft, self.recompute = shape, router, full_ft, recompute
         self.fold = fold_combine_bwd
+        self.gather = gather_x and fold_combine_bwd and _gatherable(shape)
         T, H, I, E, k, r, N = shape.T, shape.H, shape.I, shape.E, shape.k, shape.r, shape.N
         dt = shape.torch_dtype
         z = lambda *s, dtype=dt: torch.empty(s, device=device, dtype=dtype)  # noqa: E731
         i32, f32 = torch.int32, torch.float32
         if scratch is None:
-            scratch = LayerScratch([shape], recompute, device)
+            scratch = LayerScratch([shape], recompute, device, x_perm_rows=not self.gather)
         assert scratch.recompute == recompute
         self.scratch = scratch
         self.topk_ids, self.topk_w = z(T, k, dtype=i32), z(T, k, dtype=f32)
         self.counts, self.offsets = z(E, dtype=i32), z(E + 1, dtype=i32)
         self.sorted_pair, self.inv_pos = z(N, dtype=i32), z(N, dtype=i32)
-        self.x_perm = scratch.row_view(2, shape) if recompute else z(N, H)
+        if self.gather:
+            self.x_perm = None
+        else:
+            self.x_perm = scratch.row_view(2, shape) if recompute else z(N, H)
         self.saved = {"u_gu": z(N, r), "u_d": z(N, r)}
         if not recompute:
             self.saved.update(h=z(N, 2 * I), act=z(N, I))
@@ -141,7 +159,7 @@ class MoELoRALayer:
         """Bytes held from forward to backward: the saved activations and, unless
         the backward gathers it again, x_perm (the routing results and indices
         aside)."""
-        t = list(self.saved.values()) + ([] if self.recompute else [self.x_perm])
+        t = list(self.saved.values()) + ([] if self.recompute or self.gather else [self.x_perm])
         return sum(v.numel() * v.element_size() for v in t)
 
     def _permute(self, x, stream):
@@ -153,24 +171,31 @@ class MoELoRALayer:
         s = self.shape
         moe_route(logits, s.k, self.router, self.topk_ids, self.topk_w, stream)
         self._permute(x, stream)
-        fwd = moe_grouped_lora_fwd_lean if self.recompute else moe_grouped_lora_fwd
-        fwd(s, self.x_perm, self.offsets, weights, {**self.saved, "y_exp": self.y_exp},
-            self.ws_fwd, stream)
+        saved = {**self.saved, "y_exp": self.y_exp}
+        if self.gather:
+            moe_grouped_lora_fwd_gather(s, x, self.sorted_pair, self.offsets, weights, saved,
+                                        self.ws_fwd, lean=self.recompute, stream=stream)
+        else:
+            fwd = moe_grouped_lora_fwd_lean if self.recompute else moe_grouped_lora_fwd
+            fwd(s, self.x_perm, self.offsets, weights, saved, self.ws_fwd, stream)
         moe_unpermute_combine(s, self.y_exp, self.inv_pos, self.topk_w, self.y, stream)
         return self.y
 
     def backward(self, dy, logits, weights: dict, stream=None, x=None):
         s = self.shape
-        if self.recompute:
+        if self.gather:
+            if x is None:
+                raise ValueError("the backward reads x's rows through sorted_pair: pass x")
+        elif self.recompute:
             if x is None:
                 raise ValueError("the activation-lean backward gathers x_perm again: pass x")
             self._permute(x, stream)   # same routing, so the same permutation and rows
         if self.fold:
-            moe_grouped_lora_combine_bwd(s, dy, self.topk_w, self.sorted_pair, self.inv_pos,
-                                         self.x_perm, self.offsets, weights, self.saved,
-                                         self.dy_perm, self.dx_perm, self.grads, self.d_topk_w,
-                                         self.ws_bwd, base_grads=self.base_grads,
-                                         recompute=self.recompute, stream=stream)
+            bwd = moe_grouped_lora_combine_bwd_gather if self.gather else moe_grouped_lora_combine_bwd
+            bwd(s, dy, self.topk_w, self.sorted_pair, self.inv_pos,
+                x if self.gather else self.x_perm, self.offsets, weights, self.saved,
+                self.dy_perm, self.dx_perm, self.grads, self.d_topk_w, self.ws_bwd,
+                base_grads=self.base_grads, recompute=self.recompute, stream=stream)
             moe_route_bwd(logits, self.topk_ids, self.d_topk_w, s.k, self.router, self.d_logits,
                           stream)
             moe_unpermute_combine(s, self.dx_perm, self.inv_pos, None, self.dx, stream)
@@ -209,7 +234,7 @@ class MoELoRAChunkedLayer:
     is what lowers the peak."""
 
     def __init__(self, shape: Shape, router: str, chunks: int, device="cuda",
-                 full_ft: bool = False, recompute: bool = False):
+                 full_ft: bool = False, recompute: bool = False, gather_x: bool = True):
         if chunks < 1 or chunks > shape.T:
             raise ValueError(f"chunks must be in [1, T], got {chunks}")
         self.shape, self.router, self.chunks = shape, router, chunks
@@ -220,7 +245,8 @@ class MoELoRAChunkedLayer:
         self.bounds = list(zip(bounds[:-1], bounds[1:]))
         shapes = [Shape(hi - lo, shape.H, shape.I, shape.E, shape.k, shape.r, shape.dtype,
                         shape.lora_scale) for lo, hi in self.bounds]
-        self.scratch = LayerScratch(shapes, recompute, device)
+        gather = gather_x and all(_gatherable(sh) for sh in shapes)
+        self.scratch = LayerScratch(shapes, recompute, device, x_perm_rows=not gather)
         self.y = torch.empty(T, H, device=device, dtype=dt)
         self.dx = torch.empty(T, H, device=device, dtype=dt)
         self.d_logits = torch.empty(T, E, device=device, dtype=torch.float32)
@@ -233,7 +259,7 @@ class MoELoRAChunkedLayer:
             g = None if i < 2 else spare
             part = MoELoRALayer(sh, router, device, full_ft, recompute, self.scratch, out,
                                 grads=None if g is None else g[0],
-                                base_grads=None if g is None else g[1])
+                                base_grads=None if g is None else g[1], gather_x=gather)
             if i == 1:
                 spare = (part.grads, part.base_grads)
             self.parts.append(part)

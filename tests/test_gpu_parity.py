@@ -24,13 +24,16 @@ def _mel():
     return mel
 
 
-def _check_layer(name, seed, fold):
+def _check_layer(name, seed, fold, gather=True):
     mel = _mel()
     cfg = PARITY_CONFIGS[name]
-    say(f"[parity] {name} seed={seed} fold={fold} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} "
-        f"k={cfg.k} r={cfg.r} {cfg.dtype} {cfg.router}")
+    say(f"[parity] {name} seed={seed} fold={fold} gather={gather} T={cfg.T} H={cfg.H} "
+        f"I={cfg.I} E={cfg.E} k={cfg.k} r={cfg.r} {cfg.dtype} {cfg.router}")
     inp = gpu_inputs(cfg, seed)
-    layer = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, fold_combine_bwd=fold)
+    layer = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, fold_combine_bwd=fold,
+                             gather_x=gather)
+    # the GEMMs read x's rows through sorted_pair exactly when folded and gathering
+    assert (layer.x_perm is None) == (fold and gather)
     w = {n: inp[n] for n in WEIGHTS}
     layer.forward(inp["x"], inp["logits"], w)
     torch.cuda.synchronize()
@@ -49,7 +52,9 @@ def _check_layer(name, seed, fold):
     np.testing.assert_array_equal(to_numpy(layer.offsets), c["offsets"])
     np.testing.assert_array_equal(to_numpy(layer.sorted_pair), c["sorted_pair"])
     np.testing.assert_array_equal(to_numpy(layer.inv_pos), c["inv_pos"])
-    np.testing.assert_array_equal(to_numpy(layer.x_perm), oracle.gather_rows(h["x"], c["sorted_pair"], cfg.k))
+    if layer.x_perm is not None:
+        np.testing.assert_array_equal(to_numpy(layer.x_perm),
+                                      oracle.gather_rows(h["x"], c["sorted_pair"], cfg.k))
     close("topk_w", to_numpy(layer.topk_w), c["w"], 1e-5)
     # saved activations, rows in permuted order
     N = cfg.N
@@ -83,6 +88,14 @@ def test_layer_matches_oracle(name, seed):
     """The layer as it runs by default: the combine backward folded into the
     experts' backward (moe_grouped_lora_combine_bwd)."""
     _check_layer(name, seed, fold=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mini-bf16", "mini-skew", "mini-r1", "mini-f16",
+                                  "mini-split", "mini-f32-split", "max-E-k"])
+def test_layer_with_x_perm_matches_oracle(name):
+    """The folded backward with x gathered into x_perm first
+    (moe_grouped_lora_fwd / moe_grouped_lora_combine_bwd on x_perm)."""
+    _check_layer(name, 0, fold=True, gather=False)
 
 
 @pytest.mark.parametrize("name", list(PARITY_CONFIGS))
@@ -121,16 +134,20 @@ def test_full_fine_tuning_base_grads(name):
 @pytest.mark.parametrize("name", ["tiny", "mini-bf16", "mini-skew", "mini-r1", "mini-f32",
                                   "mini-f16-skew"])
 @pytest.mark.parametrize("full_ft", [False, True])
-def test_recompute_mode_is_bit_identical(name, full_ft):
+@pytest.mark.parametrize("gather", [True, False])
+def test_recompute_mode_is_bit_identical(name, full_ft, gather):
     """Activation-lean mode (h and act recomputed in the backward by the same
-    kernel): every output and gradient equals the saving mode's bit for bit."""
+    kernel): every output and gradient equals the saving mode's bit for bit,
+    with x's rows read through sorted_pair or gathered into x_perm (the lean
+    backward then gathers it again), and the two agree with each other."""
     mel = _mel()
     cfg = PARITY_CONFIGS[name]
-    say(f"[recompute] {name} full_ft={full_ft}")
+    say(f"[recompute] {name} full_ft={full_ft} gather={gather}")
     inp = gpu_inputs(cfg, 7)
     w = {n: inp[n] for n in WEIGHTS}
-    a = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=full_ft)
-    b = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=full_ft, recompute=True)
+    a = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=full_ft, gather_x=gather)
+    b = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=full_ft, recompute=True,
+                         gather_x=gather)
     a.step(inp["x"], inp["logits"], inp["dy"], w)
     b.step(inp["x"], inp["logits"], inp["dy"], w)
     torch.cuda.synchronize()
@@ -256,11 +273,12 @@ def test_autograd_function_full_fine_tuning():
 
 @pytest.mark.parametrize("name", ["mini-bf16", "mini-f16"])
 def test_unaligned_weights(name):
-    """Weights handed over as views that start 2 bytes past a 16-byte
+    """Weights and x handed over as views that start 2 bytes past a 16-byte
     boundary. The 256-row expert GEMMs cannot read them in 16-byte pieces and
     take the buffer->LDS kernel with element-wise fills (the LoRA side
     products and gradients likewise fall back to element-wise fills and to
-    their unfused kernels); every result against the oracle."""
+    their unfused kernels, and x's rows are fetched element by element through
+    sorted_pair); every result against the oracle."""
     mel = _mel()
     cfg = PARITY_CONFIGS[name]
     say(f"[unaligned] {name}")
@@ -273,8 +291,13 @@ def test_unaligned_weights(name):
         v.copy_(t)
         assert v.data_ptr() % 16 != 0
         w[n] = v
+    # x too: the GEMMs read its rows through sorted_pair (element-wise fills)
+    xb = torch.empty(inp["x"].numel() + 8, dtype=inp["x"].dtype, device="cuda")
+    x = xb[1:1 + inp["x"].numel()].view(inp["x"].shape)
+    x.copy_(inp["x"])
     layer = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router)
-    layer.step(inp["x"], inp["logits"], inp["dy"], w)
+    assert layer.x_perm is None
+    layer.step(x, inp["logits"], inp["dy"], w)
     torch.cuda.synchronize()
     h = {n: to_numpy(v) for n, v in inp.items()}
     Y, g, c = oracle.layer_forward_backward(h["x"], h["logits"], h["dy"], h, cfg.k, cfg.router,

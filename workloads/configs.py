@@ -130,6 +130,12 @@ PARITY_CONFIGS = {
                                   dtype="bf16", router="softmax_topk_renorm"),
     "mini-f16-split-r12": LayerConfig("mini-f16-split-r12", T=1800, H=256, I=160, E=3, k=2,
                                       r=12, dtype="f16", router="topk_softmax"),
+    # heavily skewed routing at E = 256 (23 live experts, five of more than
+    # 4096 rows): the LoRA A gradient over x's gathered rows runs over all of
+    # a hot expert's rows in one block, past the 4096 rows whose offsets one
+    # pass of its LDS table holds
+    "mini-hot": LayerConfig("mini-hot", T=4500, H=264, I=72, E=256, k=8, r=16,
+                            dtype="bf16", router="sigmoid_topk_renorm", zipf_s=1.2, n_dead=8),
     # the largest expert count and top-k the library accepts: about two rows per expert
     "max-E-k": LayerConfig("max-E-k", T=64, H=64, I=32, E=1024, k=32, r=8,
                            dtype="bf16", router="softmax_topk"),
