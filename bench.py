@@ -2,11 +2,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
 
-One step is the whole hot path over one batch: route, permute + gather,
-grouped gate_up (+LoRA, SwiGLU) and down (+LoRA) GEMMs, combine, and the
-backward (the combine backward folded into the down backward: dY's rows
-gathered, dw from the down backward's epilogue; route, down and gate_up with
-SwiGLU', LoRA weight gradients, unpermute-sum). Inputs are seeded synthetic tensors already
+One step is the whole hot path over one batch: route, permute, grouped
+gate_up (+LoRA, SwiGLU) and down (+LoRA) GEMMs reading x's rows through the
+permutation, combine, and the backward (the combine backward folded into the
+down backward, whose GEMMs read dY's rows through the permutation and whose
+epilogue gives dw; route, down and gate_up with SwiGLU', LoRA weight
+gradients, unpermute-sum). Inputs are seeded synthetic tensors already
 resident in HBM when timing starts. Prints one JSON line.
 
 value    = algorithmic TFLOP/s of the step, F = 12 N H I + 6 N r (2H + 3I)
@@ -314,6 +315,9 @@ def main():
     ap.add_argument("--chunks", type=int, default=1,
                     help="run the layer over its tokens in this many chunks sharing one set "
                          "of workspaces (long contexts: lower peak memory)")
+    ap.add_argument("--gather-dy", choices=("on", "off"), default="on",
+                    help="the backward's GEMMs read dY's rows in token order (on) or from a "
+                         "copy in expert order (off)")
     ap.add_argument("--merge", action="store_true",
                     help="only time the merged export W + s B A of both projections")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
@@ -368,12 +372,13 @@ def main():
             sum(v.numel() * v.element_size() for v in layer.shared.saved.values())
             if layer.shared is not None else 0)
     else:
+        gdy = args.gather_dy == "on"
         if args.chunks > 1:
             layer = mel.MoELoRAChunkedLayer(shape, cfg.router, args.chunks, full_ft=args.full_ft,
-                                            recompute=args.recompute)
+                                            recompute=args.recompute, gather_dy=gdy)
         else:
             layer = mel.MoELoRALayer(shape, cfg.router, full_ft=args.full_ft,
-                                     recompute=args.recompute)
+                                     recompute=args.recompute, gather_dy=gdy)
         step = lambda: layer.step(inp["x"], inp["logits"], inp["dy"], weights)  # noqa: E731
         fwd = lambda: layer.forward(inp["x"], inp["logits"], weights)  # noqa: E731
         bwd = lambda: layer.backward(inp["dy"], inp["logits"], weights, x=inp["x"])  # noqa: E731

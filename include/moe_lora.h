@@ -319,8 +319,15 @@ moe_status moe_grouped_lora_combine_bwd(const moe_shape *shape, const void *dy,
  * order is row sorted_pair[i] / k of x (sorted_pair from moe_permute, which
  * can then be called with x_perm = NULL). The GEMMs that read x_perm in the
  * calls above (gate_up, its LoRA side product X A_gu^T, dA_gu and, with base,
- * dW_gu) read those rows of x instead; everything else, and every result, is
- * as in moe_grouped_lora_fwd / moe_grouped_lora_fwd_lean (lean != 0) and
+ * dW_gu) read those rows of x instead. In the backward, dy_perm = NULL has
+ * the GEMMs that read dY's rows in permuted order (the down backward, dB_d
+ * and its side product dY B_d) read row sorted_pair[i] / k of dy likewise,
+ * so no permuted copy is formed (MOE_ERR_INVALID_ARG with base, whose dW_d
+ * needs w dY in permuted order, and for H <= 32); otherwise dy_perm is
+ * written as in moe_grouped_lora_combine_bwd. Which is faster depends on the
+ * shape: the copy streams well, the gathered reads skip it. Everything else,
+ * and every result, is as in
+ * moe_grouped_lora_fwd / moe_grouped_lora_fwd_lean (lean != 0) and
  * moe_grouped_lora_combine_bwd. Errors as those calls, plus a NULL
  * sorted_pair, and MOE_ERR_UNSUPPORTED when x is 2 GiB or larger (use x_perm
  * and the calls above).  */

@@ -256,7 +256,7 @@ def moe_unpermute_combine_bwd(shape: Shape, dy, y_exp, inv_pos, topk_w, dy_perm,
 
 
 def _bwd_args(shape: Shape, dy_perm, x_perm, offsets, weights: dict, saved: dict, dx_perm,
-              grads: dict, ws, lean=False, x_rows=None):
+              grads: dict, ws, lean=False, x_rows=None, dy_optional=False):
     need = moe_workspace_bytes_lean(shape)[1] if lean else moe_workspace_bytes(shape)[1]
     wsp, wsb = _ws(ws, need, "ws")
     E, H, I, r, dt = shape.E, shape.H, shape.I, shape.r, shape.torch_dtype
@@ -266,7 +266,8 @@ def _bwd_args(shape: Shape, dy_perm, x_perm, offsets, weights: dict, saved: dict
                      _ptr(grads["db_gu"], (E, 2 * I, r), dt, "db_gu"),
                      _ptr(grads["da_d"], (E, r, I), dt, "da_d"),
                      _ptr(grads["db_d"], (E, H, r), dt, "db_d"))
-    head = (ctypes.byref(shape.c()), _ptr(dy_perm, (shape.N, H), dt, "dy_perm"),
+    head = (ctypes.byref(shape.c()),
+            _ptr(dy_perm, (shape.N, H), dt, "dy_perm", optional=dy_optional),
             _ptr(x_perm, (x_rows or shape.N, H), dt, "x" if x_rows else "x_perm"),
             _ptr(offsets, (E + 1,), torch.int32, "offsets"), ctypes.byref(w), ctypes.byref(s),
             _ptr(dx_perm, (shape.N, H), dt, "dx_perm"), ctypes.byref(g))
@@ -339,9 +340,11 @@ def moe_grouped_lora_combine_bwd_gather(shape: Shape, dy, topk_w, sorted_pair, i
                                         grads: dict, d_topk_w, ws, base_grads=None,
                                         recompute=False, stream=None):
     """moe_grouped_lora_combine_bwd reading the rows of x [T, H] in token order
-    through sorted_pair instead of x_perm."""
+    through sorted_pair instead of x_perm. dy_perm None: dY's rows are read the
+    same way, with no permuted copy (not with base_grads, nor for H <= 32)."""
     head, keep, wsp, wsb = _bwd_args(shape, dy_perm, x, offsets, weights, saved, dx_perm,
-                                     grads, ws, lean=recompute, x_rows=shape.T)
+                                     grads, ws, lean=recompute, x_rows=shape.T,
+                                     dy_optional=True)
     shp, dyp, xp, off, w, sv, dxp, g = head
     T, k, N, H, E, I, dt = shape.T, shape.k, shape.N, shape.H, shape.E, shape.I, shape.torch_dtype
     b = None

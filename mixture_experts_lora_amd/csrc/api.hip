@@ -537,14 +537,23 @@ moe_status combine_bwd_impl(const char* name, bool gather, const moe_shape* shap
   CHECK_PTR(inv_pos);
   CHECK_PTR(d_topk_w);
   CHECK_ROWS(dy);
-  CHECK_ROWS(dy_perm);
   const bool lean = recompute != 0;
-  if (dy_perm == dy || dy_perm == x_perm || dy_perm == dx_perm)
-    return fail(MOE_ERR_INVALID_ARG, "dy_perm aliases another tensor");
-  // the expert part: the same checks as the separate backward calls (dy_perm
-  // is written here, so it takes the place of the G input)
-  st = grouped_bwd_check(lean, shape, dy_perm, x_perm, offsets, weights, saved, dx_perm, grads,
-                         base, ws, ws_bytes);
+  // Reading x in token order, a NULL dy_perm asks the GEMMs to read dY's rows
+  // in place too; not with the base-weight gradients (dW_d needs w dY in
+  // expert order), nor for H <= 32 (no tile shape of the dB_d gradient gathers).
+  const bool gather_dy = gather && dy_perm == nullptr;
+  if (gather_dy && base)
+    return fail(MOE_ERR_INVALID_ARG, "dy_perm is required with base-weight gradients");
+  if (gather_dy && shape->H <= 32) return fail(MOE_ERR_INVALID_ARG, "dy_perm is required for H <= 32");
+  if (!gather_dy) {
+    CHECK_ROWS(dy_perm);
+    if (dy_perm == dy || dy_perm == x_perm || dy_perm == dx_perm)
+      return fail(MOE_ERR_INVALID_ARG, "dy_perm aliases another tensor");
+  }
+  // the expert part: the same checks as the separate backward calls (the dY
+  // rows take the place of the G input)
+  st = grouped_bwd_check(lean, shape, gather_dy ? dy : dy_perm, x_perm, offsets, weights, saved,
+                         dx_perm, grads, base, ws, ws_bytes);
   if (st != MOE_OK) return st;
   const moe::ExpertDims d = dims_of(shape);
   moe::CombineBwd cb;
@@ -555,6 +564,7 @@ moe_status combine_bwd_impl(const char* name, bool gather, const moe_shape* shap
   cb.T = shape->T;
   cb.k = shape->k;
   cb.d_topk_w = d_topk_w;
+  cb.gather_dy = gather_dy;
   const moe::XRows x{x_perm, gather ? sorted_pair : nullptr, shape->k, shape->T};
   hipError_t e =
       lean ? moe::launch_experts_bwd_recompute(d, dy_perm, x, offsets, *weights, *saved,

@@ -420,8 +420,9 @@ __device__ __forceinline__ uint32_t gather_vo(const Plan<ROWS, BK, KC, NW>& P, i
   return static_cast<uint32_t>((static_cast<int64_t>(row) * P.ld + cn * 8) * 2);
 }
 
-// Issue one tile: DMA when possible, else an element-wise fill.
-template <int ROWS, int BK, bool KC, int NW>
+// Issue one tile: DMA when possible, else an element-wise fill. GATH false:
+// the operand is never gathered along k (no code for it).
+template <int ROWS, int BK, bool KC, int NW, bool GATH = true>
 __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC, NW>& P, int k0, char* lds, int wave,
                                      int lane, const uint32_t* gtab = nullptr, int tw0 = 0) {
   typedef Geo<ROWS, BK, KC, NW> G;
@@ -434,7 +435,7 @@ __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC, NW>& P, int k0, ch
       const int j = wave + NW * i;
       if (G::TI % NW == 0 || j < G::TI) {
         uint32_t vo = P.vo[i];
-        if (!KC && P.view.grow) vo = gather_vo(P, k0, j, lane, gtab, tw0);
+        if (GATH && !KC && P.view.grow) vo = gather_vo(P, k0, j, lane, gtab, tw0);
         if (tail) {
           const int r = G::RPI * j + lane / G::CPR;
           const int c = (lane % G::CPR) ^ kswz<BK>(r);
@@ -463,17 +464,21 @@ __device__ __forceinline__ void fill(const Plan<ROWS, BK, KC, NW>& P, int k0, ch
 }
 
 // One DMA instruction (index i of this wave's share) of a tile; DMA plans only.
-// gvo: the lane offset when the caller has formed it already (gathered rows)
-template <int ROWS, int BK, bool KC, int NW>
+// GIVEN: gvo is the lane offset, formed by the caller (the plan's own offset,
+// or a gathered row's); GATH false: the operand is never gathered along k.
+template <int ROWS, int BK, bool KC, int NW, bool GATH = true, bool GIVEN = false>
 __device__ __forceinline__ void fill_one(const Plan<ROWS, BK, KC, NW>& P, int k0, char* lds,
-                                         int wave, int lane, int i, int64_t gvo = -1) {
+                                         int wave, int lane, int i, uint32_t gvo = 0) {
   typedef Geo<ROWS, BK, KC, NW> G;
   const int j = wave + NW * i;
   if (G::TI % NW != 0 && j >= G::TI) return;
   uint32_t soff;
   const u32x4 rs = tile_rsrc(P, k0, soff);
   uint32_t vo = P.vo[i];
-  if (!KC && P.view.grow) vo = gvo >= 0 ? static_cast<uint32_t>(gvo) : gather_vo(P, k0, j, lane);
+  if (GIVEN)
+    vo = gvo;
+  else if (GATH && !KC && P.view.grow)
+    vo = gather_vo(P, k0, j, lane);
   if (KC && k0 + BK > P.klim) {  // k tail of a k-contiguous operand: mask by lane
     const int r = G::RPI * j + lane / G::CPR;
     const int c = (lane % G::CPR) ^ kswz<BK>(r);
@@ -630,7 +635,7 @@ __device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <bool F16, int BM, int BN, int WM, int WN, int BK, int NST, int MINB, int MODE, int EPI,
-          bool PAIRED, bool A_KC, bool B_KC, int VST>
+          bool PAIRED, bool A_KC, bool B_KC, int VST, int GATH = 0>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmArgs p) {
   constexpr int WAVES_N = BN / WN, MF = WM / 32, NF = WN / 32;
   constexpr int NW = (BM / WM) * (BN / WN);
@@ -644,9 +649,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
                 "vmcnt range");
   // GROUP_KV: + the block's [BM][32] tile of the side-product B
   constexpr int VB_BYTES = MODE == GROUP_KV ? BM * 32 * 2 : 0;
-  // GROUP_K with a gathered, output-contiguous B (the LoRA A gradient over
-  // x's rows): byte offsets of up to GT_ROWS of the block's rows, formed once
-  constexpr int GT_ROWS = MODE == GROUP_K && !B_KC && BM <= 32 && VST == 0 ? 4096 : 0;
+  // GATH (weight gradients, DMA tiles): the reduction rows of operand A
+  // (GATH 1: dY's rows for the B gradient of down) or B (GATH 2: x's rows for
+  // the LoRA A gradient of gate_up and dW_gu) are read through a row list, so
+  // that operand's lane offsets depend on each k tile's rows: they are formed
+  // a k tile ahead, in the two skinny shapes from a table in LDS of the byte
+  // offsets of up to GT_ROWS of the block's rows (it fits beside two blocks
+  // per CU). A separate instantiation keeps the ungathered loop as it is.
+  constexpr bool GK = MODE == GROUP_K || MODE == GROUP_KV;
+  static_assert(GATH == 0 || (GK && VST == 0 && !A_KC && !B_KC), "gathered rows: DMA weight gradients");
+  constexpr bool GATHER_A = GATH == 1, GATHER_B = GATH == 2;
+  constexpr int GT_ROWS = (GATHER_B && BM <= 32) ? 4096 : (GATHER_A && BN <= 32) ? 2048 : 0;
   __shared__ __attribute__((aligned(1024))) char smem[NST * ST + VB_BYTES + GT_ROWS * 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -736,11 +749,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
       va.klim = krows;
       va.mn_lim = p.M - m0;
       abytes = static_cast<int64_t>(krows) * A.ld * 2 - static_cast<int64_t>(m0) * 2;
+      if (GATHER_A) {
+        va.base = static_cast<const bf16_t*>(A.ptr) + m0;
+        va.grow = A.rows + row0;
+        va.gk = A.rows_div;
+        abytes = A.rows_bytes - static_cast<int64_t>(m0) * 2;
+      }
       vb.base = static_cast<const bf16_t*>(B.ptr) + row0 * B.ld + n0;
       vb.klim = krows;
       vb.mn_lim = p.N - n0;
       bbytes = static_cast<int64_t>(krows) * B.ld * 2 - static_cast<int64_t>(n0) * 2;
-      if (B.rows) {
+      if (GATHER_B) {
         vb.base = static_cast<const bf16_t*>(B.ptr) + n0;
         vb.grow = B.rows + row0;
         vb.gk = B.rows_div;
@@ -763,19 +782,20 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
   const int nk = nk0 + nk1;
   const bool dma0 = pa0.vec && pb0.vec, dma1 = pa1.vec && pb1.vec;
 
-  // GROUP_K with gathered B rows: their byte offsets in LDS, when formed, for
-  // the rows from gw0 on
-  const uint32_t* gtab = nullptr;
+  // Gathered reduction rows (GROUP_K, GROUP_KV): the byte offsets of the rows
+  // from gw0 on in LDS, when formed, for the operand whose rows they are
+  const uint32_t* gtab_a = nullptr;
+  const uint32_t* gtab_b = nullptr;
   int gw0 = 0;
   auto issue = [&](int j) {  // a whole stage at once (prologue, element-wise fills)
     char* sa = smem + (j % NST) * ST;
     char* sb = sa + A_BYTES;
     if (j < nk0) {
-      fill<BM, BK, A_KC, NW>(pa0, j * BK, sa, wave, lane);
-      fill<BN, BK, B_KC, NW>(pb0, j * BK, sb, wave, lane, gtab, gw0);
+      fill<BM, BK, A_KC, NW, GATHER_A>(pa0, j * BK, sa, wave, lane, gtab_a, gw0);
+      fill<BN, BK, B_KC, NW, GATHER_B>(pb0, j * BK, sb, wave, lane, gtab_b, gw0);
     } else {
-      fill<BM, BK, A_KC, NW>(pa1, (j - nk0) * BK, sa, wave, lane);
-      fill<BN, BK, B_KC, NW>(pb1, (j - nk0) * BK, sb, wave, lane);
+      fill<BM, BK, A_KC, NW, false>(pa1, (j - nk0) * BK, sa, wave, lane);
+      fill<BN, BK, B_KC, NW, false>(pb1, (j - nk0) * BK, sb, wave, lane);
     }
   };
   // A stage filled only by DMA leaves at least MINW loads per operand outstanding.
@@ -1109,33 +1129,45 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
     if (live) kloop(std::true_type());
     else kloop(std::false_type());
   } else {
-    // Gathered B rows (GROUP_K): the lane offsets of a refill depend on its
-    // rows' numbers, so they are formed one iteration ahead (their scalar
-    // loads then complete under a k tile of MFMAs instead of delaying the
-    // refill's DMA issue).
-    const bool gath = MODE == GROUP_K && !B_KC && pb0.view.grow != nullptr;
-    uint32_t gvo[GB::NIW];
-    // The rows' byte offsets, GT_ROWS at a time from row gw0 on: formed before
-    // the first DMA, and again (rare: experts of more than GT_ROWS rows) when
-    // a refill passes the window, which then waits for the DMA in flight.
+    // Gathered reduction rows (GROUP_K, GROUP_KV): the lane offsets of a
+    // refill depend on its rows' numbers, so they are formed one iteration
+    // ahead (their loads then complete under a k tile of MFMAs instead of
+    // delaying the refill's DMA issue).
+    constexpr bool gath_a = GATHER_A, gath_b = GATHER_B, gath = GATH != 0;
+    uint32_t gvo_a[GA::NIW], gvo_b[GB::NIW];
+    // The rows' byte offsets, GT_ROWS at a time from row gw0 on: formed
+    // before the first DMA, and again (experts of more than GT_ROWS rows)
+    // when a refill passes the window, which then waits for the DMA in flight.
     uint32_t* gt = reinterpret_cast<uint32_t*>(smem + NST * ST + VB_BYTES);
+    const int32_t* gt_rows = gath_a ? pa0.view.grow : pb0.view.grow;
+    const uint32_t gt_div = static_cast<uint32_t>(gath_a ? pa0.view.gk : pb0.view.gk);
+    const uint32_t gt_ld2 = static_cast<uint32_t>(gath_a ? pa0.ld : pb0.ld) * 2u;
     auto gather_window = [&](int w0) __attribute__((always_inline)) {
       __syncthreads();
       for (int i = tid; i < GT_ROWS && w0 + i < krows; i += NW * 64)
-        gt[i] = static_cast<uint32_t>(pb0.view.grow[w0 + i]) /
-                static_cast<uint32_t>(pb0.view.gk) * static_cast<uint32_t>(pb0.ld) * 2u;
+        gt[i] = static_cast<uint32_t>(gt_rows[w0 + i]) / gt_div * gt_ld2;
       __syncthreads();
       gw0 = w0;
     };
     if (GT_ROWS > 0 && gath) {
       gather_window(0);
-      gtab = gt;
+      if (gath_a)
+        gtab_a = gt;
+      else
+        gtab_b = gt;
     }
     auto gather_plan = [&](int j) __attribute__((always_inline)) {
-      if (gtab && (j + 1) * BK > gw0 + GT_ROWS) gather_window(j * BK);
+      if (GT_ROWS > 0 && gath && (j + 1) * BK > gw0 + GT_ROWS) gather_window(j * BK);
+      if (gath_a) {
 #pragma unroll
-      for (int i = 0; i < GB::NIW; ++i)
-        gvo[i] = gather_vo(pb0, j * BK, wave + NW * i, lane, gtab, gw0);
+        for (int i = 0; i < GA::NIW; ++i)
+          gvo_a[i] = gather_vo(pa0, j * BK, wave + NW * i, lane, gtab_a, gw0);
+      }
+      if (gath_b) {
+#pragma unroll
+        for (int i = 0; i < GB::NIW; ++i)
+          gvo_b[i] = gather_vo(pb0, j * BK, wave + NW * i, lane, gtab_b, gw0);
+      }
     };
   #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
@@ -1174,9 +1206,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
       const char* sb = sa + A_BYTES;
       constexpr int KS = BK / 16;
       constexpr int NT = GA::NIW + GB::NIW;
-      uint32_t gcur[GB::NIW];
+      uint32_t gcur_a[GA::NIW], gcur_b[GB::NIW];
 #pragma unroll
-      for (int i = 0; i < GB::NIW; ++i) gcur[i] = gvo[i];
+      for (int i = 0; i < GA::NIW; ++i) gcur_a[i] = gvo_a[i];
+#pragma unroll
+      for (int i = 0; i < GB::NIW; ++i) gcur_b[i] = gvo_b[i];
       if (gath && jn + 1 < nk) gather_plan(jn + 1);
       // Fragments are double-buffered in registers: the LDS reads of k-step
       // ks+1 are in flight while the MFMAs of k-step ks run.
@@ -1199,12 +1233,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
         if (refill_dma) {
   #pragma unroll
           for (int t = ks * NT / KS; t < (ks + 1) * NT / KS; ++t) {
-            if (t < GA::NIW)
-              fill_one<BM, BK, A_KC, NW>(PA, k0n, san, wave, lane, t);
-            else if (gath)
-              fill_one<BN, BK, B_KC, NW>(PB, k0n, sbn, wave, lane, t - GA::NIW, gcur[t - GA::NIW]);
-            else
-              fill_one<BN, BK, B_KC, NW>(PB, k0n, sbn, wave, lane, t - GA::NIW);
+            if (t < GA::NIW) {
+              if constexpr (gath_a)
+                fill_one<BM, BK, A_KC, NW, false, true>(PA, k0n, san, wave, lane, t, gcur_a[t]);
+              else
+                fill_one<BM, BK, A_KC, NW, false>(PA, k0n, san, wave, lane, t);
+            } else {
+              const int tb = t - GA::NIW;
+              if constexpr (gath_b)
+                fill_one<BN, BK, B_KC, NW, false, true>(PB, k0n, sbn, wave, lane, tb, gcur_b[tb]);
+              else
+                fill_one<BN, BK, B_KC, NW, false>(PB, k0n, sbn, wave, lane, tb);
+            }
           }
         }
   #pragma unroll
@@ -1478,6 +1518,11 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs p) {
       K = krows;
       va.base = static_cast<const float*>(A.ptr) + row0 * A.ld + m0;
       va.mn_lim = p.M - m0;
+      if (A.rows) {
+        va.base = static_cast<const float*>(A.ptr) + m0;
+        va.grow = A.rows + row0;
+        va.gk = A.rows_div;
+      }
       vb.base = static_cast<const float*>(B.ptr) + row0 * B.ld + n0;
       vb.mn_lim = p.N - n0;
       if (B.rows) {
@@ -1861,14 +1906,37 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
   out[i] = from_f32<Elem>(acc);
 }
 
+// One weight-gradient tile shape (BK 32, three stages, two blocks per CU): the
+// instantiation that reads A's rows (GA) or B's rows (GB) through their row
+// list when that operand has one. Shapes without that instantiation refuse a
+// row list, as does a launch with both.
+template <int BM, int BN, int WM, int WN, int MODE, int EPI, bool GA, bool GB>
+hipError_t launch_wg(const GemmArgs& a, int grid, hipStream_t s) {
+  const bool ra = a.a[0].rows != nullptr, rb = a.b[0].rows != nullptr;
+  if (ra && rb) return hipErrorInvalidValue;
+  if (ra) {
+    if constexpr (GA)
+      return launch(GEMM16(a.dtype, BM, BN, WM, WN, 32, 3, 2, MODE, EPI, false, false, false, 0, 1),
+                    grid, a, s);
+    return hipErrorInvalidValue;
+  }
+  if (rb) {
+    if constexpr (GB)
+      return launch(GEMM16(a.dtype, BM, BN, WM, WN, 32, 3, 2, MODE, EPI, false, false, false, 0, 2),
+                    grid, a, s);
+    return hipErrorInvalidValue;
+  }
+  return launch(GEMM16(a.dtype, BM, BN, WM, WN, 32, 3, 2, MODE, EPI, false, false, false, 0),
+                grid, a, s);
+}
+
 template <int EPI>
 hipError_t weight_grad_launch(const ExpertDims& d, GemmArgs& a, int E, int P, int Q,
                               hipStream_t s) {
   if (a.vp) {  // [big, r <= 32] with side-product partials (checked by the caller)
     a.ntn = 1;
     a.ntm = ceil_div(P, 256);
-    return launch(GEMM16(a.dtype, 256, 32, 64, 32, 32, 3, 2, GROUP_KV, EPI, false, false, false, 0),
-                  E * a.ntm, a, s);
+    return launch_wg<256, 32, 64, 32, GROUP_KV, EPI, true, false>(a, E * a.ntm, s);
   }
   if (d.dtype != MOE_F32) {
     // Split partials (EPI_STORE_F32) only come from gradients with a side of
@@ -1877,20 +1945,16 @@ hipError_t weight_grad_launch(const ExpertDims& d, GemmArgs& a, int E, int P, in
     if (Q <= 64 && P > 64) {  // [big, r]
       a.ntn = 1;
       a.ntm = ceil_div(P, 256);
-      if (Q <= 32)
-        return launch(GEMM16(a.dtype, 256, 32, 64, 32, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
-                      E * a.ntm, a, s);
+      if (Q <= 32) return launch_wg<256, 32, 64, 32, GROUP_K, EPI, true, false>(a, E * a.ntm, s);
       if constexpr (WIDE)
-        return launch(GEMM16(a.dtype, 256, 64, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
-                      E * a.ntm, a, s);
+        return launch_wg<256, 64, 64, 64, GROUP_K, EPI, true, false>(a, E * a.ntm, s);
       return hipErrorInvalidValue;
     }
     if (P >= 256 && Q >= 256) {  // [big, big]: full fine-tuning weight gradients
       if constexpr (WIDE) {
         a.ntm = ceil_div(P, 128);
         a.ntn = ceil_div(Q, 256);
-        return launch(GEMM16(a.dtype, 128, 256, 64, 128, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
-                      E * a.ntm * a.ntn, a, s);
+        return launch_wg<128, 256, 64, 128, GROUP_K, EPI, false, true>(a, E * a.ntm * a.ntn, s);
       }
       return hipErrorInvalidValue;
     }
@@ -1898,13 +1962,11 @@ hipError_t weight_grad_launch(const ExpertDims& d, GemmArgs& a, int E, int P, in
     a.ntn = ceil_div(Q, 256);
     if (P <= 32) {
       a.ntm = 1;
-      return launch(GEMM16(a.dtype, 32, 256, 32, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
-                    E * a.ntn, a, s);
+      return launch_wg<32, 256, 32, 64, GROUP_K, EPI, false, true>(a, E * a.ntn, s);
     }
     if constexpr (WIDE) {
       a.ntm = ceil_div(P, 64);
-      return launch(GEMM16(a.dtype, 64, 256, 64, 64, 32, 3, 2, GROUP_K, EPI, false, false, false, 0),
-                    E * a.ntm * a.ntn, a, s);
+      return launch_wg<64, 256, 64, 64, GROUP_K, EPI, true, true>(a, E * a.ntm * a.ntn, s);
     }
     return hipErrorInvalidValue;
   }
@@ -2009,7 +2071,9 @@ hipError_t scale_rows(int dtype, const void* src, const float* w, int64_t rows, 
 // side (optional, side_fusable only): also form V = scale D Bm.
 hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* Lm, int P,
                        const void* Rm, int Q, void* out, hipStream_t s, void* split_ws,
-                       const SideOut* side = nullptr, const XRows* rx = nullptr) {
+                       const SideOut* side = nullptr, const XRows* rx = nullptr,
+                       const XRows* lx = nullptr) {
+  if (lx && rx) return hipErrorInvalidValue;  // at most one operand's rows are gathered
   GemmArgs a{};
   a.vsplit = 1;
   if (side) {
@@ -2026,7 +2090,7 @@ hipError_t weight_grad(const ExpertDims& d, const int32_t* offsets, const void* 
   a.dtype = d.dtype;
   a.out_estride = static_cast<int64_t>(P) * Q;
   a.ld_out = Q;
-  a.a[0] = opnd(Lm, 0, P, 0, P % 8 == 0);
+  a.a[0] = lx ? opnd_x(*lx, P, 0, esz_of(d)) : opnd(Lm, 0, P, 0, P % 8 == 0);
   a.b[0] = rx ? opnd_x(*rx, Q, 0, esz_of(d)) : opnd(Rm, 0, Q, 0, Q % 8 == 0);
   const int S = split_ws ? wgrad_splits(d, P, Q) : 1;
   auto side_sum = [&]() -> hipError_t {
@@ -2253,9 +2317,17 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const XRows& x
   // down backward runs on dY and its epilogue scales the product by w (dw
   // comes from the unweighted product); dA_d = (w s dY B_d)^T act; the full
   // fine-tuning dW_d = (w dY)^T act after the rows are scaled in place.
+  // With cb->gather_dy (never with base) those rows are not copied: the
+  // GEMMs read row sorted_pair[i] / k of dY for permuted row i.
+  const bool dyg = cb && cb->gather_dy;
+  if (dyg && base) return hipErrorInvalidValue;
+  const XRows dyr{cb ? cb->dy : nullptr, cb ? cb->sorted_pair : nullptr, cb ? cb->k : 1,
+                  cb ? cb->T : 0};
+  const Opnd g_rows = dyg ? opnd_x(dyr, H, 1, esz_of(d)) : opnd(g, 0, H, 1, true);
+  const XRows* g_lx = dyg ? &dyr : nullptr;
   const void* ud_eff = sv.u_d;   // right operand of dB_d
   const void* gb_da = gb;        // left operand of dA_d
-  if (cb) {
+  if (cb && !dyg) {
     TimedScope ts(tm, MOE_K_DY_GATHER, s);
     const int64_t row_bytes = static_cast<int64_t>(H) * (d.dtype == MOE_F32 ? 4 : 2);
     MOE_TRY(launch_gather(cb->dy, cb->sorted_pair, offsets, d.E, cb->k, d.N, row_bytes,
@@ -2278,16 +2350,16 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const XRows& x
       so.roww = B.w_perm;
       so.out_w = B.gbw;
     }
-    MOE_TRY(weight_grad(d, offsets, g, H, ud_eff, r, gr.db_d, s, split, &so));
+    MOE_TRY(weight_grad(d, offsets, g, H, ud_eff, r, gr.db_d, s, split, &so, nullptr, g_lx));
   } else {  // gb = s G B_d      (B_d[e] is [H, r]: K = H rows, r contiguous)
     TimedScope ts(tm, MOE_K_LORA_SIDE, s);
-    MOE_TRY(side_product(d, offsets, L, opnd(g, 0, H, 1, true), H, w.b_d,
+    MOE_TRY(side_product(d, offsets, L, g_rows, H, w.b_d,
                          static_cast<int64_t>(H) * r, 0, gb, s));
     if (cb) MOE_TRY(scale_rows(d.dtype, gb, B.w_perm, d.N, r, B.gbw, s));
   }
   {  // dAct = G W_d + gb A_d ; dH = SwiGLU'(h) dAct
     GemmArgs a = base_args(d, offsets, L.big);
-    a.a[0] = opnd(g, 0, H, 1, true);
+    a.a[0] = g_rows;
     a.b[0] = opnd(w.w_d, static_cast<int64_t>(H) * I, I, 0, true);   // [K=H][N=I]
     a.a[1] = opnd(gb, 0, r, 1, r % 8 == 0);
     a.b[1] = opnd(w.a_d, static_cast<int64_t>(r) * I, I, 0, true);   // [K=r][N=I]
@@ -2320,7 +2392,8 @@ hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const XRows& x
   }
   {  // dB_d = G^T u_d  [H, r] (unless fused above) ;  dA_d = gb^T act  [r, I]
     TimedScope ts(tm, MOE_K_LORA_WGRAD, s);
-    if (!fuse_d) MOE_TRY(weight_grad(d, offsets, g, H, ud_eff, r, gr.db_d, s, split));
+    if (!fuse_d)
+      MOE_TRY(weight_grad(d, offsets, g, H, ud_eff, r, gr.db_d, s, split, nullptr, nullptr, g_lx));
     MOE_TRY(weight_grad(d, offsets, gb_da, r, sv.act, I, gr.da_d, s, split));
   }
   if (base) {  // full fine-tuning: dW_d = G^T act  [H, I]

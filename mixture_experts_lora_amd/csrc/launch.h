@@ -99,11 +99,15 @@ struct CombineBwd {
   const int32_t* inv_pos;
   int T, k;
   float* d_topk_w;       // [T, k] out
+  // The GEMMs read dY's rows through sorted_pair and g is not written (not
+  // with base: the base-weight gradient needs w dY in expert order).
+  bool gather_dy = false;
 };
 
 // `base` may be null (LoRA only); otherwise the base-weight gradients are written too.
 // `cb` null: g holds G = w dY rows (read only). Otherwise g is an [N, H]
-// buffer the call fills with dY's rows, and cb's d_topk_w is written.
+// buffer the call fills with dY's rows (unused with cb->gather_dy), and cb's
+// d_topk_w is written.
 hipError_t launch_experts_bwd(const ExpertDims& d, const void* g, const XRows& x,
                               const int32_t* offsets, const moe_weights& w,
                               const moe_saved& sv, void* dx_perm, const moe_lora_grads& gr,

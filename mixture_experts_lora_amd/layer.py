@@ -6,7 +6,8 @@ so nothing is allocated inside a step) and issues, on torch's current stream:
   forward   moe_route -> moe_permute (indices only) -> moe_grouped_lora_fwd_gather
             (the GEMMs read x's rows through sorted_pair) -> moe_unpermute_combine
   backward  moe_grouped_lora_combine_bwd_gather (the combine backward folded
-            into the experts' backward: d_topk_w from the down backward, no G)
+            into the experts' backward: d_topk_w from the down backward, no G;
+            the GEMMs read dY's rows through sorted_pair as well)
             -> moe_route_bwd -> moe_unpermute_combine (weights 1: dX_perm
             summed back to tokens)
   With gather_x=False, moe_permute also gathers x_perm and the calls without
@@ -103,6 +104,9 @@ class MoELoRALayer:
     gather_x=True (the default, with fold_combine_bwd, for x below 2 GiB): the
     expert GEMMs read x's rows in token order through sorted_pair, so x_perm
     is never formed (no gather pass, nothing of it held); backward() needs x.
+    gather_dy=True (the default; with gather_x, not with full_ft, for H > 32):
+    the backward's GEMMs read dY's rows the same way instead of a copy of them
+    in expert order.
 
     scratch: a LayerScratch to share with other layers or chunks (one is made
     when None). out: optional views {"y", "dx", "d_logits"} to write the
@@ -113,7 +117,7 @@ class MoELoRALayer:
                  recompute: bool = False, scratch: LayerScratch | None = None,
                  out: dict | None = None, grads: dict | None = None,
                  base_grads: dict | None = None, fold_combine_bwd: bool = True,
-                 gather_x: bool = True):
+                 gather_x: bool = True, gather_dy: bool = True):
         self.shape, self.router, self.full_ft, self.recompute = shape, router, full_ft, recompute
         self.fold = fold_combine_bwd
         self.gather = gather_x and fold_combine_bwd and _gatherable(shape)
@@ -144,7 +148,10 @@ class MoELoRALayer:
         self.y = out["y"] if "y" in out else z(T, H)
         self.dx = out["dx"] if "dx" in out else z(T, H)
         self.d_logits = out["d_logits"] if "d_logits" in out else z(T, E, dtype=f32)
-        self.dy_perm, self.dx_perm = scratch.row_view(0, shape), scratch.row_view(1, shape)
+        # dY's rows in expert order (not formed when the GEMMs read dY in place)
+        self.gather_dy = self.gather and gather_dy and not full_ft and shape.H > 32
+        self.dy_perm = None if self.gather_dy else scratch.row_view(0, shape)
+        self.dx_perm = scratch.row_view(1, shape)
         self.d_topk_w = scratch.d_topk_w[:T * k].view(T, k)
         self.grads = grads if grads is not None else {
             "da_gu": z(E, r, H), "db_gu": z(E, 2 * I, r), "da_d": z(E, r, I), "db_d": z(E, H, r)}
@@ -234,7 +241,8 @@ class MoELoRAChunkedLayer:
     is what lowers the peak."""
 
     def __init__(self, shape: Shape, router: str, chunks: int, device="cuda",
-                 full_ft: bool = False, recompute: bool = False, gather_x: bool = True):
+                 full_ft: bool = False, recompute: bool = False, gather_x: bool = True,
+                 gather_dy: bool = True):
         if chunks < 1 or chunks > shape.T:
             raise ValueError(f"chunks must be in [1, T], got {chunks}")
         self.shape, self.router, self.chunks = shape, router, chunks
@@ -259,7 +267,8 @@ class MoELoRAChunkedLayer:
             g = None if i < 2 else spare
             part = MoELoRALayer(sh, router, device, full_ft, recompute, self.scratch, out,
                                 grads=None if g is None else g[0],
-                                base_grads=None if g is None else g[1], gather_x=gather)
+                                base_grads=None if g is None else g[1], gather_x=gather,
+                                gather_dy=gather_dy)
             if i == 1:
                 spare = (part.grads, part.base_grads)
             self.parts.append(part)

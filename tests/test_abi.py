@@ -163,6 +163,34 @@ def test_token_rows_must_be_16_byte_aligned(lib):
         assert b"16-byte" in lib.moe_last_error()
 
 
+def test_gather_backward_dy_perm_rules(lib):
+    """moe_grouped_lora_combine_bwd_gather with dy_perm = NULL reads dY's rows
+    in token order; that is refused before any launch for full fine-tuning
+    (dW_d is formed from w dY in expert order) and for H <= 32, and a given
+    dy_perm must be 16-byte aligned."""
+    P = ctypes.c_void_p
+    fake, odd = P(0x10000), P(0x20002)
+    sh = shape()
+    from mixture_experts_lora_amd._lib import MoeBaseGrads, MoeLoraGrads, MoeSaved, MoeWeights
+    w = MoeWeights(*(0x10000,) * 6)
+    sv = MoeSaved(*(0x30000 + i * 0x1000 for i in range(5)))
+    g = MoeLoraGrads(*(0x50000 + i * 0x1000 for i in range(4)))
+    b = MoeBaseGrads(0x90000, 0xa0000)
+
+    def call(dy_perm, base, sh=sh):
+        return lib.moe_grouped_lora_combine_bwd_gather(
+            ctypes.byref(sh), fake, fake, fake, fake, P(0x70000), fake, ctypes.byref(w),
+            ctypes.byref(sv), 0, dy_perm, P(0x80000), ctypes.byref(g), base, fake, fake,
+            1 << 30, None)
+
+    assert call(None, ctypes.byref(b)) == 1
+    assert b"dy_perm is required with base" in lib.moe_last_error()
+    assert call(None, None, shape(H=32)) == 1
+    assert b"dy_perm is required for H <= 32" in lib.moe_last_error()
+    assert call(odd, None) == 1
+    assert b"16-byte" in lib.moe_last_error()
+
+
 def test_noalloc_permute_rejects_tables_beyond_its_array(lib):
     """moe_permute_noalloc's table (E * ceil(T k / 64) int32) must fit its
     4 MiB device array; a larger one is refused before any GPU call."""

@@ -24,16 +24,18 @@ def _mel():
     return mel
 
 
-def _check_layer(name, seed, fold, gather=True):
+def _check_layer(name, seed, fold, gather=True, gather_dy=True):
     mel = _mel()
     cfg = PARITY_CONFIGS[name]
-    say(f"[parity] {name} seed={seed} fold={fold} gather={gather} T={cfg.T} H={cfg.H} "
-        f"I={cfg.I} E={cfg.E} k={cfg.k} r={cfg.r} {cfg.dtype} {cfg.router}")
+    say(f"[parity] {name} seed={seed} fold={fold} gather={gather} gather_dy={gather_dy} "
+        f"T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} r={cfg.r} {cfg.dtype} {cfg.router}")
     inp = gpu_inputs(cfg, seed)
     layer = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, fold_combine_bwd=fold,
-                             gather_x=gather)
-    # the GEMMs read x's rows through sorted_pair exactly when folded and gathering
+                             gather_x=gather, gather_dy=gather_dy)
+    # the GEMMs read x's rows through sorted_pair exactly when folded and
+    # gathering, and dY's rows too when asked (H > 32)
     assert (layer.x_perm is None) == (fold and gather)
+    assert (layer.dy_perm is None) == (fold and gather and gather_dy and cfg.H > 32)
     w = {n: inp[n] for n in WEIGHTS}
     layer.forward(inp["x"], inp["logits"], w)
     torch.cuda.synchronize()
@@ -85,9 +87,17 @@ def _check_layer(name, seed, fold, gather=True):
 @pytest.mark.parametrize("name", list(PARITY_CONFIGS))
 @pytest.mark.parametrize("seed", [0, 3407])
 def test_layer_matches_oracle(name, seed):
-    """The layer as it runs by default: the combine backward folded into the
-    experts' backward (moe_grouped_lora_combine_bwd)."""
+    """The layer with the combine backward folded into the experts' backward
+    and the GEMMs reading x's and dY's rows through sorted_pair
+    (moe_grouped_lora_fwd_gather, moe_grouped_lora_combine_bwd_gather)."""
     _check_layer(name, seed, fold=True)
+
+
+@pytest.mark.parametrize("name", list(PARITY_CONFIGS))
+def test_layer_with_dy_copy_matches_oracle(name):
+    """x's rows read through sorted_pair, dY's rows copied into expert order
+    first (the gathered backward given dy_perm)."""
+    _check_layer(name, 0, fold=True, gather_dy=False)
 
 
 @pytest.mark.parametrize("name", ["tiny", "mini-bf16", "mini-skew", "mini-r1", "mini-f16",
@@ -134,20 +144,22 @@ def test_full_fine_tuning_base_grads(name):
 @pytest.mark.parametrize("name", ["tiny", "mini-bf16", "mini-skew", "mini-r1", "mini-f32",
                                   "mini-f16-skew"])
 @pytest.mark.parametrize("full_ft", [False, True])
-@pytest.mark.parametrize("gather", [True, False])
+@pytest.mark.parametrize("gather", ["x+dy", "x", "none"])
 def test_recompute_mode_is_bit_identical(name, full_ft, gather):
     """Activation-lean mode (h and act recomputed in the backward by the same
     kernel): every output and gradient equals the saving mode's bit for bit,
-    with x's rows read through sorted_pair or gathered into x_perm (the lean
-    backward then gathers it again), and the two agree with each other."""
+    with x's (and dY's) rows read through sorted_pair or gathered into x_perm
+    (the lean backward then gathers it again)."""
     mel = _mel()
     cfg = PARITY_CONFIGS[name]
     say(f"[recompute] {name} full_ft={full_ft} gather={gather}")
     inp = gpu_inputs(cfg, 7)
     w = {n: inp[n] for n in WEIGHTS}
-    a = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=full_ft, gather_x=gather)
+    gx, gdy = gather != "none", gather == "x+dy"
+    a = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=full_ft, gather_x=gx,
+                         gather_dy=gdy)
     b = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=full_ft, recompute=True,
-                         gather_x=gather)
+                         gather_x=gx, gather_dy=gdy)
     a.step(inp["x"], inp["logits"], inp["dy"], w)
     b.step(inp["x"], inp["logits"], inp["dy"], w)
     torch.cuda.synchronize()
