@@ -653,13 +653,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm16(GemmA
   // (GATH 1: dY's rows for the B gradient of down) or B (GATH 2: x's rows for
   // the LoRA A gradient of gate_up and dW_gu) are read through a row list, so
   // that operand's lane offsets depend on each k tile's rows: they are formed
-  // a k tile ahead, in the two skinny shapes from a table in LDS of the byte
-  // offsets of up to GT_ROWS of the block's rows (it fits beside two blocks
-  // per CU). A separate instantiation keeps the ungathered loop as it is.
+  // a k tile ahead from a table in LDS of the byte offsets of up to GT_ROWS
+  // of the block's rows (sized so that two blocks still fit a CU). A
+  // separate instantiation keeps the ungathered loop as it is.
   constexpr bool GK = MODE == GROUP_K || MODE == GROUP_KV;
   static_assert(GATH == 0 || (GK && VST == 0 && !A_KC && !B_KC), "gathered rows: DMA weight gradients");
   constexpr bool GATHER_A = GATH == 1, GATHER_B = GATH == 2;
-  constexpr int GT_ROWS = (GATHER_B && BM <= 32) ? 4096 : (GATHER_A && BN <= 32) ? 2048 : 0;
+  constexpr int GT_ROWS = GATH == 0                ? 0
+                          : (GATHER_B && BM <= 32) ? 4096
+                          : (GATHER_A && BN <= 32) ? 2048
+                                                   : 1024;
   __shared__ __attribute__((aligned(1024))) char smem[NST * ST + VB_BYTES + GT_ROWS * 4];
 
   const int tid = threadIdx.x, lane = tid & 63;

@@ -117,14 +117,18 @@ def test_layer_with_separate_combine_backward_matches_oracle(name):
 
 @pytest.mark.parametrize("name", ["tiny", "mini-bf16", "mini-skew", "mini-f32", "mini-k1",
                                   "mini-renorm", "mini-f16", "mini-split", "mini-f32-split"])
-def test_full_fine_tuning_base_grads(name):
+@pytest.mark.parametrize("gather_x", [None, True])
+def test_full_fine_tuning_base_grads(name, gather_x):
     """Full fine-tuning: dW_gu and dW_d against the oracle; every other output
-    bit-identical to the LoRA-only backward."""
+    bit-identical to the LoRA-only backward (which reads x's and dY's rows
+    through sorted_pair). gather_x None: x_perm (the default with full_ft);
+    True: dW_gu reads x's rows through sorted_pair too."""
     mel = _mel()
     cfg = PARITY_CONFIGS[name]
-    say(f"[full-ft] {name}")
+    say(f"[full-ft] {name} gather_x={gather_x}")
     inp = gpu_inputs(cfg, 5)
-    full = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=True)
+    full = mel.MoELoRALayer(mel.Shape.of(cfg), cfg.router, full_ft=True, gather_x=gather_x)
+    assert (full.x_perm is None) == bool(gather_x)
     full.step(inp["x"], inp["logits"], inp["dy"], {n: inp[n] for n in WEIGHTS})
     torch.cuda.synchronize()
     h = {n: to_numpy(v) for n, v in inp.items()}
