@@ -130,6 +130,10 @@ PARITY_CONFIGS = {
                                   dtype="bf16", router="softmax_topk_renorm"),
     "mini-f16-split-r12": LayerConfig("mini-f16-split-r12", T=1800, H=256, I=160, E=3, k=2,
                                       r=12, dtype="f16", router="topk_softmax"),
+    # 65..128 experts (two logits per lane in the routing kernels), E not a
+    # multiple of the wave
+    "mini-e96": LayerConfig("mini-e96", T=300, H=136, I=72, E=96, k=6, r=8,
+                            dtype="bf16", router="softmax_topk_renorm"),
     # heavily skewed routing at E = 256 (23 live experts, five of more than
     # 4096 rows): the LoRA A gradient over x's gathered rows runs over all of
     # a hot expert's rows in one block, past the 4096 rows whose offsets one
