@@ -1995,12 +1995,20 @@ struct SideOut {
 };
 
 // The fused path covers 16-bit layers, Q = r <= 32 with rows of 16 bytes.
+// The partials cost ceil(P / 256) x Q float32 per row each way; past 2 KB a
+// row (512 values: DeepSeek-V3's dB_d, 28 tiles at r = 32) reading D a second
+// time in a plain side-product GEMM was faster on MI355X (0.45 against
+// 0.53 ms), at 2 KB the two were even (DeepSeek-V3's dB_gu), below it fusing
+// wins (gpt-oss-20b's dB_gu, 1.5 KB: 0.11 against 0.17 ms).
 inline bool side_fusable(const ExpertDims& d, int P, int Q) {
-  return d.dtype != MOE_F32 && Q <= 32 && Q % 8 == 0 && P % 8 == 0 && P > 64;
+  return d.dtype != MOE_F32 && Q <= 32 && Q % 8 == 0 && P % 8 == 0 && P > 64 &&
+         ceil_div(P, 256) * Q <= 512;
 }
 
 inline size_t side_part_bytes(const ExpertDims& d) {
-  const int P = std::max(d.H, 2 * d.I);
+  int P = 0;
+  for (const int p : {d.H, 2 * d.I})
+    if (side_fusable(d, p, d.r)) P = std::max(P, p);
   return static_cast<size_t>(ceil_div(P, 256)) * d.N * d.r * 4;
 }
 
