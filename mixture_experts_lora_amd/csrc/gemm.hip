@@ -61,9 +61,10 @@ struct Opnd {
   int vec;          // 16-byte chunks allowed (alignment and extents are multiples of 8)
   // Gathered rows (the layer input read in token order): row i of the
   // permuted order is row rows[i] / rows_div of ptr, which holds rows_bytes
-  // bytes. Null rows: the operand's rows are in permuted order. Only the A
-  // operand of GROUP_M (rows along mn) and the B operand of GROUP_K (rows
-  // along k) are ever gathered.
+  // bytes. Null rows: the operand's rows are in permuted order. Gathered
+  // are the A operand of GROUP_M (rows along mn: x or dY) and, in the weight
+  // gradients, the operand whose rows run along k (dY as A of dB_d, x as B of
+  // dA_gu and dW_gu).
   const int32_t* rows;
   int rows_div;
   int64_t rows_bytes;

@@ -66,9 +66,10 @@ hipError_t launch_dw_sum(const float* dwp, int slots, const int32_t* inv_pos, in
                          float* d_topk_w, hipStream_t s);
 
 // ---- grouped expert GEMMs
-// The layer input as the expert GEMMs read it: x_perm [N, H] in permuted
-// order (rows null), or x [T, H] in token order, row i of the permuted order
-// being token rows[i] / k (rows = sorted_pair; the GEMMs gather it).
+// A token-row activation as the expert GEMMs read it (x, and dY in the
+// backward): [N, H] in permuted order (rows null, e.g. x_perm), or [T, H] in
+// token order, row i of the permuted order being token rows[i] / k
+// (rows = sorted_pair; the GEMMs gather it).
 struct XRows {
   const void* ptr;
   const int32_t* rows;
